@@ -1,0 +1,207 @@
+/*
+ * dsa.h -- C ABI of libdsa: indexed sparse attention (DSA) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * DSA, as the pages describe it ("Optimizing Next-Gen LLM Inference: Sparse
+ * Attention and Mixed Parallelism in Practice" §1 and §3.1/§3.3; "Long-Context
+ * LLM Inference Optimization: From Sparse Attention to System-Level
+ * Co-Design", architecture section), runs three steps per query token:
+ *   1. a lightweight indexer scores every visible cached position;
+ *   2. a per-query Top-K keeps the K most relevant positions;
+ *   3. a sparse attention kernel reads only those rows of the multi-head latent
+ *      attention (MLA) cache and attends over them.
+ * The entry points below expose each step and the fused pass.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers to dense, row-major arrays in the
+ *    shapes given per argument.  The caller owns every buffer; the library
+ *    allocates nothing, keeps no pointer after a call returns, and never
+ *    synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    null stream) and completes asynchronously.
+ *  - Validation first: every scalar and pointer argument is checked before any
+ *    HIP call.  A non-DSA_OK return enqueues nothing; dsa_last_error() then
+ *    describes the problem (thread-local string).
+ *  - Device-side contents are not validated (that would need a sync).  Every
+ *    kernel clamps each seq_lens[b] to [0, max_seq_len] and skips index-list
+ *    entries outside [0, len_b), so bad values never read out of bounds; they
+ *    only give meaningless results.
+ *  - Sequence b holds len_b = seq_lens[b] filled cache rows; its q_len query
+ *    tokens are the last q_len of them.  Query token t sees the positions
+ *    0 .. vis-1 with vis = len_b - q_len + 1 + t (causal).
+ *  - Reentrant; concurrent calls on different streams must not share a
+ *    workspace or an output buffer.
+ *
+ * Numeric contract
+ * ----------------
+ *  - Index scores are accumulated in fp32 with an fp32 head reduction.  When
+ *    every partial sum is an integer below 2^24 (integer-valued index queries,
+ *    keys and head weights, power-of-two key scales) the scores are exact and
+ *    therefore bit-identical to any exact evaluation.
+ *  - Top-K ranks the fp32 scores; equal scores go to the lower position; -0
+ *    equals +0.  NaN scores are not supported.
+ *  - Attention logits and values are accumulated in fp32 (bf16 matrix-core
+ *    products for bf16/fp8 caches), softmax uses the running-max (online)
+ *    form, outputs are rounded to nearest even when out_dtype is bf16.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t / hipEvent_t are pointers to these opaque HIP structs. */
+struct ihipStream_t;
+struct ihipEvent_t;
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,         /* bad pointer, size, dtype or scalar */
+  DSA_ERR_UNSUPPORTED = 2,         /* valid but not implemented combination */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the *_workspace_size() value */
+  DSA_ERR_HIP = 4                  /* a HIP launch reported an error */
+} dsa_status;
+
+typedef enum dsa_dtype {
+  DSA_F32 = 0,      /* IEEE binary32 */
+  DSA_BF16 = 1,     /* bfloat16 (upper half of binary32) */
+  DSA_FP8_E4M3 = 2  /* OCP FP8 E4M3: bias 7, no infinities, max 448, 0x7F/0xFF NaN */
+} dsa_dtype;
+
+/*
+ * Problem description (host struct, read during the call only).
+ *
+ * Indexer ("Optimizing Next-Gen LLM Inference" §3.1; "Inference Acceleration
+ * for New Large Model Architectures" §3.1): per query token, idx_heads index
+ * heads of idx_dim each score every visible position s as
+ *     S[s] = sum_h head_w[h] * max(0, q_idx[h,:] . k_idx[s,:] * k_scale[s])
+ * (the ReLU-weighted head aggregation is this library's reading of "score,
+ * then head-weight"; k_scale is 1 unless the keys are FP8).
+ *
+ * Sparse MLA attention ("Optimization and Deployment Practices for
+ * Next-Generation Sparse Attention LLMs" §1-§2): one latent row of qk_dim
+ * values per cached token serves as the key of every head; its first v_dim
+ * values are the value.  For head h:
+ *     z_j = softmax_scale * q[h,:] . c[idx_j,:],  out[h,:] = sum_j softmax(z)_j c[idx_j, :v_dim].
+ */
+typedef struct dsa_problem {
+  int32_t batch;        /* B >= 1 sequences */
+  int32_t q_len;        /* T >= 1 query tokens per sequence (decode 1, drafts 2, prefill chunk);
+                           batch * q_len <= 65535 */
+  int64_t max_seq_len;  /* Lmax: rows per sequence in k_idx / kv / scores, q_len <= Lmax < 2^31 */
+  int32_t idx_heads;    /* Hi >= 1 */
+  int32_t idx_dim;      /* Di >= 1 */
+  int32_t heads;        /* H >= 1 attention heads */
+  int32_t qk_dim;       /* Dqk >= 1 latent row width (latent + rope) */
+  int32_t v_dim;        /* 1 <= Dv <= Dqk: leading columns of a row used as the value */
+  int32_t top_k;        /* K >= 1 */
+  float softmax_scale;  /* finite, > 0 (usually 1/sqrt(qk_dim)) */
+  int32_t q_idx_dtype;  /* DSA_F32 | DSA_BF16 */
+  int32_t idx_key_dtype;/* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3 (then k_scale required) */
+  int32_t q_dtype;      /* DSA_F32 | DSA_BF16 */
+  int32_t kv_dtype;     /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3 (then kv_scale required) */
+  int32_t out_dtype;    /* DSA_F32 | DSA_BF16 */
+} dsa_problem;
+
+#define DSA_ABI_VERSION 1
+#define DSA_FORWARD_STAGES 3 /* indexer scores, Top-K, sparse attention */
+
+int dsa_abi_version(void);
+const char* dsa_status_string(dsa_status s);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Indexer scores (step 1).
+ *   q_idx    [B,T,Hi,Di]  q_idx_dtype.  With FP8 keys the index query is
+ *                         quantised to E4M3 (nearest, ties to even, saturating
+ *                         at +-448) before the products, as the pages quantise
+ *                         index Q and K alike ("Inference Acceleration ..." §4.1).
+ *   head_w   [B,T,Hi]     fp32 head weights.
+ *   k_idx    [B,Lmax,Di]  idx_key_dtype index keys.
+ *   k_scale  [B,Lmax]     fp32 positive per-row scale when keys are FP8, else NULL.
+ *   seq_lens [B]          int32 filled rows per sequence.
+ *   scores   [B,T,Lmax]   fp32 output; entries s >= vis are left unspecified
+ *                         (they may be overwritten).
+ * Pointers must be non-NULL (k_scale as stated); q_idx, k_idx and scores must
+ * be 16-byte aligned.
+ */
+dsa_status dsa_index_score(const dsa_problem* p, const void* q_idx, const float* head_w,
+                           const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                           float* scores, struct ihipStream_t* stream);
+
+/* Workspace bytes dsa_topk needs for problem p (0 if p is invalid). */
+size_t dsa_topk_workspace_size(const dsa_problem* p);
+
+/*
+ * Per-query Top-K (step 2).
+ *   scores     [B,T,Lmax] fp32 (only s < vis is read).
+ *   topk_idx   [B,T,K] int32 output: the selected positions in ascending order;
+ *              the last K - count entries are -1.
+ *   topk_count [B,T] int32 output count = min(K, max(vis, 0)), or NULL.
+ *   ws         device scratch of at least dsa_topk_workspace_size(p) bytes
+ *              (any contents; 16-byte aligned).
+ */
+dsa_status dsa_topk(const dsa_problem* p, const float* scores, const int32_t* seq_lens,
+                    int32_t* topk_idx, int32_t* topk_count, void* ws, size_t ws_bytes,
+                    struct ihipStream_t* stream);
+
+/* Workspace bytes dsa_sparse_mla_decode needs for problem p (0 if invalid). */
+size_t dsa_sparse_mla_workspace_size(const dsa_problem* p);
+
+/*
+ * Sparse MLA attention over selected rows (step 3).
+ *   q        [B,T,H,Dqk]  q_dtype queries (already absorbed into the latent space).
+ *   kv       [B,Lmax,Dqk] kv_dtype latent cache rows.
+ *   kv_scale [B,Lmax]     fp32 positive per-row scale when kv is FP8, else NULL.
+ *   topk_idx [B,T,K]      int32 rows to attend over; entries outside [0, len_b)
+ *                         are ignored, so -1 padding is allowed.
+ *   out      [B,T,H,Dv]   out_dtype output.  No valid entry: out = 0.
+ *   lse      [B,T,H]      fp32 natural-log softmax normaliser of the scaled
+ *                         logits (-inf when no entry is valid), or NULL.
+ *   ws       scratch of dsa_sparse_mla_workspace_size(p) bytes (any contents).
+ * q, kv and out must be 16-byte aligned.
+ */
+dsa_status dsa_sparse_mla_decode(const dsa_problem* p, const void* q, const void* kv,
+                                 const float* kv_scale, const int32_t* topk_idx,
+                                 const int32_t* seq_lens, void* out, float* lse, void* ws,
+                                 size_t ws_bytes, struct ihipStream_t* stream);
+
+/* Workspace bytes dsa_forward needs for problem p (0 if invalid). */
+size_t dsa_forward_workspace_size(const dsa_problem* p);
+
+/*
+ * The whole path: indexer scores -> Top-K -> sparse MLA attention, with the
+ * score histogram that drives the Top-K threshold fused into the score pass.
+ * Arguments as in the three calls above, plus:
+ *   scores       [B,T,Lmax] fp32 output of step 1, or NULL to keep it in ws.
+ *   topk_idx     [B,T,K] output of step 2, or NULL to keep it in ws.
+ *   topk_count   [B,T] or NULL.
+ *   stage_events NULL, or DSA_FORWARD_STAGES + 1 hipEvent_t handles: event 0
+ *                is recorded on `stream` before the first kernel and event i+1
+ *                after stage i (for per-stage timing).
+ */
+dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
+                       const void* k_idx, const float* k_scale, const void* q, const void* kv,
+                       const float* kv_scale, const int32_t* seq_lens, float* scores,
+                       int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
+                       size_t ws_bytes, struct ihipStream_t* stream,
+                       struct ihipEvent_t* const* stage_events);
+
+/*
+ * Diagnostics.  dsa_kernel_choice() names the kernels dsa_forward would launch
+ * for p ("mfma" or "generic" per step) into buf (NUL-terminated, truncated to
+ * len).  While the environment variable DSA_FORCE_GENERIC is set to a value
+ * other than "0", every call uses the portable SIMT kernels for every step.
+ */
+int dsa_kernel_choice(const dsa_problem* p, char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

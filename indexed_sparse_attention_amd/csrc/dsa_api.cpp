@@ -1,0 +1,464 @@
+// Host side of libdsa: argument validation, workspace layout, kernel choice
+// and launches.  Every entry point validates all of its arguments before the
+// first HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+dsa_status ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+// Read on every call so a process can switch paths between calls.
+bool force_generic() {
+  const char* e = getenv("DSA_FORCE_GENERIC");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  if (!e || !*e) return dflt;
+  return atoi(e);
+}
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+const int64_t kHistBins = 4096;
+
+dsa_status validate_problem(const dsa_problem* p) {
+  if (!p) return fail(DSA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1) return fail(DSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", p->batch);
+  if (p->q_len < 1) return fail(DSA_ERR_INVALID_ARG, "q_len must be >= 1 (got %d)", p->q_len);
+  if (p->max_seq_len < 1 || p->max_seq_len > INT32_MAX)
+    return fail(DSA_ERR_INVALID_ARG, "max_seq_len must be in [1, 2^31-1] (got %lld)",
+                (long long)p->max_seq_len);
+  if (p->q_len > p->max_seq_len)
+    return fail(DSA_ERR_INVALID_ARG, "q_len (%d) exceeds max_seq_len (%lld)", p->q_len,
+                (long long)p->max_seq_len);
+  if (p->idx_heads < 1 || p->idx_dim < 1)
+    return fail(DSA_ERR_INVALID_ARG, "idx_heads and idx_dim must be >= 1");
+  if (p->heads < 1 || p->qk_dim < 1) return fail(DSA_ERR_INVALID_ARG, "heads and qk_dim must be >= 1");
+  if (p->v_dim < 1 || p->v_dim > p->qk_dim)
+    return fail(DSA_ERR_INVALID_ARG, "v_dim must be in [1, qk_dim] (got %d)", p->v_dim);
+  if (p->top_k < 1) return fail(DSA_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", p->top_k);
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f))
+    return fail(DSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  auto in = [](int32_t d, int lo, int hi) { return d >= lo && d <= hi; };
+  if (!in(p->q_idx_dtype, DSA_F32, DSA_BF16)) return fail(DSA_ERR_INVALID_ARG, "q_idx_dtype must be F32 or BF16");
+  if (!in(p->idx_key_dtype, DSA_F32, DSA_FP8_E4M3)) return fail(DSA_ERR_INVALID_ARG, "idx_key_dtype invalid");
+  if (!in(p->q_dtype, DSA_F32, DSA_BF16)) return fail(DSA_ERR_INVALID_ARG, "q_dtype must be F32 or BF16");
+  if (!in(p->kv_dtype, DSA_F32, DSA_FP8_E4M3)) return fail(DSA_ERR_INVALID_ARG, "kv_dtype invalid");
+  if (!in(p->out_dtype, DSA_F32, DSA_BF16)) return fail(DSA_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
+  // sizes must fit the int64 offsets the kernels use
+  const double bt = (double)p->batch * p->q_len;
+  if (bt * p->max_seq_len > 4.0e18 || (double)p->batch * p->max_seq_len * p->qk_dim > 4.0e18 ||
+      bt * p->top_k > 2.0e9 || bt * p->heads > 2.0e9)
+    return fail(DSA_ERR_INVALID_ARG, "problem too large");
+  // (query, chunk) and (head, query) launch grids put batch * q_len on grid.y
+  if (bt > 65535.0) return fail(DSA_ERR_INVALID_ARG, "batch * q_len must be <= 65535");
+  if (p->heads > 65535) return fail(DSA_ERR_INVALID_ARG, "heads must be <= 65535");
+  return DSA_OK;
+}
+
+// ------------------------------------------------------------------ Top-K layout
+struct TopkLayout {
+  int chunk, n_chunks;
+  int64_t off_hist, off_arrive, zero_words;  // zeroed region = [off_hist, off_hist + zero_words*4)
+  int64_t off_cnt, off_cand, bytes;
+};
+
+TopkLayout topk_layout(const dsa_problem* p) {
+  TopkLayout L;
+  const int64_t BT = (int64_t)p->batch * p->q_len, Lmax = p->max_seq_len;
+  int64_t chunk = std::max<int64_t>(4096, (Lmax * BT + 2047) / 2048);
+  chunk = align_up(chunk, 1024);
+  if (chunk > align_up(Lmax, 1024)) chunk = align_up(Lmax, 1024);
+  L.chunk = (int)chunk;
+  L.n_chunks = (int)((Lmax + chunk - 1) / chunk);
+  L.off_hist = 0;
+  L.off_arrive = BT * kHistBins * 4;
+  L.zero_words = BT * kHistBins + BT;
+  L.off_cnt = align_up(L.off_arrive + BT * 4, kAlign);
+  L.off_cand = align_up(L.off_cnt + BT * L.n_chunks * 4, kAlign);
+  L.bytes = align_up(L.off_cand + BT * Lmax * 4, kAlign);
+  return L;
+}
+
+// ------------------------------------------------------------------ MLA layout
+struct MlaLayout {
+  int splits, rows_per_split;
+  int64_t off_o, off_ml, bytes;
+};
+
+bool mla_uses_mfma(const dsa_problem* p) {
+  return !force_generic() && p->qk_dim == 576 && p->v_dim == 512 && p->heads % 64 == 0 &&
+         p->q_dtype == DSA_BF16 && (p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_FP8_E4M3);
+}
+
+MlaLayout mla_layout(const dsa_problem* p) {
+  MlaLayout L;
+  const int64_t BT = (int64_t)p->batch * p->q_len;
+  const int tile = 32;
+  L.splits = 1;
+  L.rows_per_split = (int)align_up(p->top_k, tile);
+  if (mla_uses_mfma(p)) {
+    const int64_t wgs_per_split = BT * (p->heads / 64);
+    int64_t target = env_int("DSA_MLA_TARGET_WGS", 256);
+    int64_t s = (target + wgs_per_split - 1) / wgs_per_split;
+    const int64_t max_s = std::min<int64_t>(64, (p->top_k + tile - 1) / tile);
+    if (env_int("DSA_MLA_SPLITS", 0) > 0) s = env_int("DSA_MLA_SPLITS", 0);
+    s = std::max<int64_t>(1, std::min(s, max_s));
+    L.rows_per_split = (int)align_up((p->top_k + s - 1) / s, tile);
+    L.splits = (p->top_k + L.rows_per_split - 1) / L.rows_per_split;
+  }
+  L.off_o = 0;
+  L.off_ml = 0;
+  L.bytes = 0;
+  if (L.splits > 1) {
+    L.off_ml = align_up((int64_t)L.splits * BT * p->heads * p->v_dim * 4, kAlign);
+    L.bytes = align_up(L.off_ml + (int64_t)L.splits * BT * p->heads * 2 * 4, kAlign);
+  }
+  return L;
+}
+
+// ------------------------------------------------------------------ forward layout
+struct FwdLayout {
+  TopkLayout tk;
+  MlaLayout mla;
+  int64_t off_topk, off_scores, off_idx, off_mla, bytes;
+};
+
+FwdLayout fwd_layout(const dsa_problem* p) {
+  FwdLayout F;
+  const int64_t BT = (int64_t)p->batch * p->q_len;
+  F.tk = topk_layout(p);
+  F.mla = mla_layout(p);
+  F.off_topk = 0;
+  F.off_scores = align_up(F.tk.bytes, kAlign);
+  F.off_idx = align_up(F.off_scores + BT * p->max_seq_len * 4, kAlign);
+  F.off_mla = align_up(F.off_idx + BT * p->top_k * 4, kAlign);
+  F.bytes = align_up(F.off_mla + F.mla.bytes, kAlign);
+  return F;
+}
+
+int num_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+dsa_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DSA_OK;
+}
+
+#define REQUIRE(cond, ...) \
+  do {                     \
+    if (!(cond)) return fail(DSA_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+dsa_status check_index_inputs(const dsa_problem* p, const void* q_idx, const float* head_w,
+                              const void* k_idx, const float* k_scale, const int32_t* seq_lens) {
+  REQUIRE(q_idx && aligned(q_idx, 16), "q_idx must be non-NULL and 16-byte aligned");
+  REQUIRE(head_w && aligned(head_w, 4), "head_w must be non-NULL and 4-byte aligned");
+  REQUIRE(k_idx && aligned(k_idx, 16), "k_idx must be non-NULL and 16-byte aligned");
+  REQUIRE(seq_lens && aligned(seq_lens, 4), "seq_lens must be non-NULL and 4-byte aligned");
+  if (p->idx_key_dtype == DSA_FP8_E4M3)
+    REQUIRE(k_scale && aligned(k_scale, 4), "k_scale is required (4-byte aligned) for FP8 index keys");
+  else
+    REQUIRE(!k_scale, "k_scale must be NULL unless idx_key_dtype is FP8_E4M3");
+  return DSA_OK;
+}
+
+dsa_status check_mla_inputs(const dsa_problem* p, const void* q, const void* kv, const float* kv_scale,
+                            const int32_t* seq_lens, const void* out, const float* lse) {
+  REQUIRE(q && aligned(q, 16), "q must be non-NULL and 16-byte aligned");
+  REQUIRE(kv && aligned(kv, 16), "kv must be non-NULL and 16-byte aligned");
+  REQUIRE(seq_lens && aligned(seq_lens, 4), "seq_lens must be non-NULL and 4-byte aligned");
+  REQUIRE(out && aligned(out, 16), "out must be non-NULL and 16-byte aligned");
+  REQUIRE(!lse || aligned(lse, 4), "lse must be 4-byte aligned");
+  if (p->kv_dtype == DSA_FP8_E4M3)
+    REQUIRE(kv_scale && aligned(kv_scale, 4), "kv_scale is required (4-byte aligned) for an FP8 cache");
+  else
+    REQUIRE(!kv_scale, "kv_scale must be NULL unless kv_dtype is FP8_E4M3");
+  if (!mla_uses_mfma(p)) {
+    REQUIRE(p->qk_dim <= 2048, "qk_dim > 2048 is not supported by the portable attention kernel");
+    if (p->v_dim > 1024) return fail(DSA_ERR_UNSUPPORTED, "v_dim > 1024 is not supported by the portable attention kernel");
+  }
+  return DSA_OK;
+}
+
+dsa::ScoreParams score_params(const dsa_problem* p, const void* q_idx, const float* head_w,
+                              const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                              float* scores, uint32_t* hist) {
+  dsa::ScoreParams s;
+  s.q_idx = q_idx;
+  s.head_w = head_w;
+  s.k_idx = k_idx;
+  s.k_scale = k_scale;
+  s.seq_lens = seq_lens;
+  s.scores = scores;
+  s.hist = hist;
+  s.B = p->batch;
+  s.T = p->q_len;
+  s.Hi = p->idx_heads;
+  s.Di = p->idx_dim;
+  s.Lmax = p->max_seq_len;
+  s.q_dtype = p->q_idx_dtype;
+  s.k_dtype = p->idx_key_dtype;
+  return s;
+}
+
+dsa::TopkParams topk_params(const dsa_problem* p, const TopkLayout& L, uint8_t* ws, const float* scores,
+                            const int32_t* seq_lens, int32_t* idx, int32_t* cnt) {
+  dsa::TopkParams t;
+  t.scores = scores;
+  t.seq_lens = seq_lens;
+  t.hist = (const uint32_t*)(ws + L.off_hist);
+  t.cand = (uint32_t*)(ws + L.off_cand);
+  t.chunk_cnt = (uint32_t*)(ws + L.off_cnt);
+  t.arrive = (uint32_t*)(ws + L.off_arrive);
+  t.topk_idx = idx;
+  t.topk_count = cnt;
+  t.B = p->batch;
+  t.T = p->q_len;
+  t.K = p->top_k;
+  t.Lmax = p->max_seq_len;
+  t.chunk = L.chunk;
+  t.n_chunks = L.n_chunks;
+  return t;
+}
+
+dsa::MlaParams mla_params(const dsa_problem* p, const MlaLayout& L, uint8_t* ws, const void* q,
+                          const void* kv, const float* kv_scale, const int32_t* idx,
+                          const int32_t* seq_lens, void* out, float* lse) {
+  dsa::MlaParams m;
+  m.q = q;
+  m.kv = kv;
+  m.kv_scale = kv_scale;
+  m.topk_idx = idx;
+  m.seq_lens = seq_lens;
+  m.out = out;
+  m.lse = lse;
+  m.part_o = L.splits > 1 ? (float*)(ws + L.off_o) : nullptr;
+  m.part_ml = L.splits > 1 ? (float*)(ws + L.off_ml) : nullptr;
+  m.B = p->batch;
+  m.T = p->q_len;
+  m.H = p->heads;
+  m.Dqk = p->qk_dim;
+  m.Dv = p->v_dim;
+  m.K = p->top_k;
+  m.Lmax = p->max_seq_len;
+  m.scale = p->softmax_scale;
+  m.q_dtype = p->q_dtype;
+  m.kv_dtype = p->kv_dtype;
+  m.out_dtype = p->out_dtype;
+  m.splits = L.splits;
+  m.rows_per_split = L.rows_per_split;
+  return m;
+}
+
+bool score_uses_mfma(const dsa_problem* p) {
+  if (force_generic()) return false;
+  dsa::ScoreParams s{};
+  s.Hi = p->idx_heads;
+  s.Di = p->idx_dim;
+  s.T = p->q_len;
+  s.q_dtype = p->q_idx_dtype;
+  s.k_dtype = p->idx_key_dtype;
+  return dsa::score_mfma_supported(s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "DSA_ERR_WORKSPACE_TOO_SMALL";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_UNKNOWN_STATUS";
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status dsa_index_score(const dsa_problem* p, const void* q_idx, const float* head_w,
+                           const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                           float* scores, struct ihipStream_t* stream) {
+  dsa_status st = validate_problem(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_index_inputs(p, q_idx, head_w, k_idx, k_scale, seq_lens)) != DSA_OK) return st;
+  REQUIRE(scores && aligned(scores, 16), "scores must be non-NULL and 16-byte aligned");
+  auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, scores, nullptr);
+  if ((st = hip_check(dsa::launch_score(sp, !force_generic(), num_cus(), stream), "index score launch")) != DSA_OK)
+    return st;
+  return ok();
+}
+
+size_t dsa_topk_workspace_size(const dsa_problem* p) {
+  if (validate_problem(p) != DSA_OK) return 0;
+  return (size_t)topk_layout(p).bytes;
+}
+
+dsa_status dsa_topk(const dsa_problem* p, const float* scores, const int32_t* seq_lens,
+                    int32_t* topk_idx, int32_t* topk_count, void* ws, size_t ws_bytes,
+                    struct ihipStream_t* stream) {
+  dsa_status st = validate_problem(p);
+  if (st != DSA_OK) return st;
+  REQUIRE(scores && aligned(scores, 4), "scores must be non-NULL and 4-byte aligned");
+  REQUIRE(seq_lens && aligned(seq_lens, 4), "seq_lens must be non-NULL and 4-byte aligned");
+  REQUIRE(topk_idx && aligned(topk_idx, 4), "topk_idx must be non-NULL and 4-byte aligned");
+  REQUIRE(!topk_count || aligned(topk_count, 4), "topk_count must be 4-byte aligned");
+  const TopkLayout L = topk_layout(p);
+  if ((int64_t)ws_bytes < L.bytes)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_topk needs %lld workspace bytes, got %zu",
+                (long long)L.bytes, ws_bytes);
+  REQUIRE(ws && aligned(ws, 16), "ws must be non-NULL and 16-byte aligned");
+  uint8_t* w = (uint8_t*)ws;
+  hipStream_t s = stream;
+  if ((st = hip_check(dsa::launch_zero_u32((uint32_t*)(w + L.off_hist), L.zero_words, s), "zero")) != DSA_OK) return st;
+  if ((st = hip_check(dsa::launch_hist(scores, seq_lens, (uint32_t*)(w + L.off_hist), p->batch, p->q_len,
+                                       p->max_seq_len, s), "histogram")) != DSA_OK) return st;
+  auto tp = topk_params(p, L, w, scores, seq_lens, topk_idx, topk_count);
+  if ((st = hip_check(dsa::launch_select(tp, s), "select")) != DSA_OK) return st;
+  return ok();
+}
+
+size_t dsa_sparse_mla_workspace_size(const dsa_problem* p) {
+  if (validate_problem(p) != DSA_OK) return 0;
+  return (size_t)mla_layout(p).bytes;
+}
+
+dsa_status dsa_sparse_mla_decode(const dsa_problem* p, const void* q, const void* kv,
+                                 const float* kv_scale, const int32_t* topk_idx,
+                                 const int32_t* seq_lens, void* out, float* lse, void* ws,
+                                 size_t ws_bytes, struct ihipStream_t* stream) {
+  dsa_status st = validate_problem(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_mla_inputs(p, q, kv, kv_scale, seq_lens, out, lse)) != DSA_OK) return st;
+  REQUIRE(topk_idx && aligned(topk_idx, 4), "topk_idx must be non-NULL and 4-byte aligned");
+  const MlaLayout L = mla_layout(p);
+  if ((int64_t)ws_bytes < L.bytes)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_sparse_mla_decode needs %lld workspace bytes, got %zu",
+                (long long)L.bytes, ws_bytes);
+  REQUIRE(L.bytes == 0 || (ws && aligned(ws, 16)), "ws must be non-NULL and 16-byte aligned");
+  auto mp = mla_params(p, L, (uint8_t*)ws, q, kv, kv_scale, topk_idx, seq_lens, out, lse);
+  if ((st = hip_check(dsa::launch_mla(mp, mla_uses_mfma(p), stream), "sparse attention")) != DSA_OK) return st;
+  return ok();
+}
+
+size_t dsa_forward_workspace_size(const dsa_problem* p) {
+  if (validate_problem(p) != DSA_OK) return 0;
+  return (size_t)fwd_layout(p).bytes;
+}
+
+dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
+                       const void* k_idx, const float* k_scale, const void* q, const void* kv,
+                       const float* kv_scale, const int32_t* seq_lens, float* scores,
+                       int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
+                       size_t ws_bytes, struct ihipStream_t* stream,
+                       struct ihipEvent_t* const* stage_events) {
+  dsa_status st = validate_problem(p);
+  if (st != DSA_OK) return st;
+  if ((st = check_index_inputs(p, q_idx, head_w, k_idx, k_scale, seq_lens)) != DSA_OK) return st;
+  if ((st = check_mla_inputs(p, q, kv, kv_scale, seq_lens, out, lse)) != DSA_OK) return st;
+  REQUIRE(!scores || aligned(scores, 16), "scores must be 16-byte aligned");
+  REQUIRE(!topk_idx || aligned(topk_idx, 4), "topk_idx must be 4-byte aligned");
+  REQUIRE(!topk_count || aligned(topk_count, 4), "topk_count must be 4-byte aligned");
+  if (stage_events)
+    for (int i = 0; i <= DSA_FORWARD_STAGES; ++i)
+      REQUIRE(stage_events[i], "stage_events[%d] is NULL", i);
+  const FwdLayout F = fwd_layout(p);
+  if ((int64_t)ws_bytes < F.bytes)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_forward needs %lld workspace bytes, got %zu",
+                (long long)F.bytes, ws_bytes);
+  REQUIRE(ws && aligned(ws, 256), "ws must be non-NULL and 256-byte aligned");
+
+  uint8_t* w = (uint8_t*)ws;
+  hipStream_t s = stream;
+  float* sc = scores ? scores : (float*)(w + F.off_scores);
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + F.off_idx);
+  uint32_t* hist = (uint32_t*)(w + F.off_topk + F.tk.off_hist);
+  auto rec = [&](int i) -> dsa_status {
+    if (!stage_events) return DSA_OK;
+    return hip_check(hipEventRecord((hipEvent_t)stage_events[i], s), "event record");
+  };
+
+  if ((st = rec(0)) != DSA_OK) return st;
+  // stage 1: scores (+ fused histogram when the matrix-core kernel runs)
+  if ((st = hip_check(dsa::launch_zero_u32(hist, F.tk.zero_words, s), "zero")) != DSA_OK) return st;
+  const bool mfma_score = score_uses_mfma(p);
+  auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, sc, hist);
+  if (!mfma_score) sp.hist = nullptr;
+  if ((st = hip_check(dsa::launch_score(sp, mfma_score, num_cus(), s), "index score")) != DSA_OK) return st;
+  if (!mfma_score &&
+      (st = hip_check(dsa::launch_hist(sc, seq_lens, hist, p->batch, p->q_len, p->max_seq_len, s),
+                      "histogram")) != DSA_OK)
+    return st;
+  if ((st = rec(1)) != DSA_OK) return st;
+  // stage 2: Top-K
+  auto tp = topk_params(p, F.tk, w + F.off_topk, sc, seq_lens, idx, topk_count);
+  if ((st = hip_check(dsa::launch_select(tp, s), "select")) != DSA_OK) return st;
+  if ((st = rec(2)) != DSA_OK) return st;
+  // stage 3: sparse MLA attention
+  auto mp = mla_params(p, F.mla, w + F.off_mla, q, kv, kv_scale, idx, seq_lens, out, lse);
+  if ((st = hip_check(dsa::launch_mla(mp, mla_uses_mfma(p), s), "sparse attention")) != DSA_OK) return st;
+  if ((st = rec(3)) != DSA_OK) return st;
+  return ok();
+}
+
+int dsa_kernel_choice(const dsa_problem* p, char* buf, size_t len) {
+  if (!buf || len == 0) return -1;
+  if (validate_problem(p) != DSA_OK) {
+    snprintf(buf, len, "invalid");
+    return -1;
+  }
+  const MlaLayout L = mla_layout(p);
+  snprintf(buf, len, "score=%s topk=radix-select mla=%s splits=%d rows_per_split=%d select_chunk=%d",
+           score_uses_mfma(p) ? "mfma" : "generic", mla_uses_mfma(p) ? "mfma" : "generic", L.splits,
+           L.rows_per_split, topk_layout(p).chunk);
+  return 0;
+}
+
+}  // extern "C"

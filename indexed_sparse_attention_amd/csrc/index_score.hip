@@ -1,0 +1,369 @@
+// Indexer scores: S[b,t,s] = sum_h w[b,t,h] * max(0, (q_idx[b,t,h,:] . k_idx[b,s,:]) * k_scale[b,s])
+// for every visible position s < vis(b,t) = len_b - T + 1 + t.
+//
+// The pages ("Optimizing Next-Gen LLM Inference" §3.1, "Inference Acceleration
+// for New Large Model Architectures" §3.1) fuse relevance scoring and the
+// head-weighted aggregation into one pass over the key cache; here that pass
+// is a matrix-core contraction over (index heads x key rows) with the ReLU,
+// the weights and the head sum applied to the accumulators in registers.  The
+// same pass builds the per-query histogram of the top 12 bits of each score's
+// order-preserving key, which the Top-K threshold search consumes.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------
+// Portable SIMT kernel: one thread per (query, position).  Any dims/dtypes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float load_elem(const void* p, int dtype, int64_t i) {
+  if (dtype == kF32) return ((const float*)p)[i];
+  if (dtype == kBF16) return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+  return e4m3_to_f32(((const uint8_t*)p)[i]);
+}
+
+__global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
+  const int bt = blockIdx.y;
+  const int b = bt / p.T, t = bt % p.T;
+  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const int64_t vis = (int64_t)len - p.T + 1 + t;
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= vis) return;
+  const bool fp8 = (p.k_dtype == kE4M3);
+  const int64_t krow = ((int64_t)b * p.Lmax + s) * p.Di;
+  const float scale = p.k_scale ? p.k_scale[(int64_t)b * p.Lmax + s] : 1.0f;
+  float S = 0.0f;
+  for (int h = 0; h < p.Hi; ++h) {
+    const int64_t qrow = ((int64_t)bt * p.Hi + h) * p.Di;
+    float d = 0.0f;
+    for (int i = 0; i < p.Di; ++i) {
+      float qv = load_elem(p.q_idx, p.q_dtype, qrow + i);
+      if (fp8) qv = e4m3_quantize(qv);
+      d = fmaf(qv, load_elem(p.k_idx, p.k_dtype, krow + i), d);
+    }
+    d *= scale;
+    S = fmaf(p.head_w[(int64_t)bt * p.Hi + h], fmaxf(d, 0.0f), S);
+  }
+  p.scores[(int64_t)bt * p.Lmax + s] = S;
+  if (p.hist) atomicAdd(&p.hist[(int64_t)bt * kHistBins + (score_key(S) >> kHistShift)], 1u);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core kernel for 64 index heads x 128 dims.
+//
+// Work: for each sequence b and group g of TQ consecutive query tokens, the
+// positions [0, vis_end) with vis_end = vis of the group's last token, cut
+// into units of 64 positions.  All units of all (b, g) segments are laid end
+// to end and split evenly over the grid, so ragged lengths stay balanced.
+// Within a workgroup the four waves take the segment's units round-robin.
+//
+// Per wave and sub-tile of 16 positions, the MFMA computes D[16 heads x 16
+// positions] for each of the 4 head tiles: operand A is the index query (kept
+// in registers for the whole segment), operand B the key rows loaded straight
+// from HBM, 16 bytes per lane.  In the 16x16 accumulator layout lane l holds
+// position l%16 and heads 4*(l/16) + e, e < 4, so ReLU, weight and a partial
+// head sum happen in-lane; after 4 sub-tiles a 3-shuffle reduce-scatter across
+// the 4 lane groups leaves lane l with the full score of position 64u + l.
+//
+// Operand k-ordering: MFMA A and B share one (lane group, element) -> k
+// assignment, so any fixed permutation of the 128 dims gives the same dot
+// product; lane group j of k-step ks carries dims 32 ks + 8 j .. +8 (bf16) or
+// dims 32 j .. +32 (e4m3, single k-step of 128).
+// ---------------------------------------------------------------------------
+constexpr int kHi = 64, kDi = 128;
+constexpr int kScoreThreads = 256;
+constexpr int kScoreWaves = kScoreThreads / kWave;
+
+template <bool FP8>
+struct KeyTile;
+template <>
+struct KeyTile<false> {  // bf16: 4 k-steps of 32 dims, 16 bytes each
+  bf16x8 v[4];
+};
+template <>
+struct KeyTile<true> {  // e4m3: one k-step of 128 dims, 32 bytes
+  i32x8 v;
+};
+
+template <bool FP8>
+__device__ __forceinline__ void load_key_tile(KeyTile<FP8>& kt, const void* base_row, int lg) {
+  if constexpr (!FP8) {
+    const bf16x8* r = (const bf16x8*)base_row;  // 128 bf16 = 16 x bf16x8
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kt.v[ks] = __builtin_nontemporal_load(r + ks * 4 + lg);
+  } else {
+    const i32x4* r = (const i32x4*)base_row;  // 128 bytes = 8 x 16 B
+    i32x4 a = __builtin_nontemporal_load(r + 2 * lg);
+    i32x4 c = __builtin_nontemporal_load(r + 2 * lg + 1);
+    kt.v = i32x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  }
+}
+
+template <int TQ, bool FP8>
+struct QRegs;
+template <int TQ>
+struct QRegs<TQ, false> {
+  bf16x8 a[TQ][4][4];  // [token][head tile][k-step]
+};
+template <int TQ>
+struct QRegs<TQ, true> {
+  i32x8 a[TQ][4];  // [token][head tile], 32 e4m3 codes
+};
+
+template <int TQ, int NSLOT, bool FP8>
+__global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParams p) {
+  // LDS: [TQ] index queries in operand order (bf16: 64 x 128 x 2 B; e4m3: 64 x 128 B),
+  // then [TQ][kHistBins] histogram counters when p.hist.
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
+  uint8_t* lds_q = (uint8_t*)lds;
+  uint32_t* lds_hist = lds + TQ * kQBytes / 4;
+  __shared__ int64_t s_total;
+  __shared__ int64_t s_wsum[kScoreWaves];
+  __shared__ int64_t s_excl[kScoreThreads];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int l = lane_id();
+  const int lg = l >> 4;   // lane group 0..3
+  const int lc = l & 15;   // column within a 16-wide tile
+  const int G = (p.T + TQ - 1) / TQ;
+  const int n_seg = p.B * G;
+
+  auto seg_units = [&](int seg) -> int64_t {
+    const int b = seg / G, g = seg % G;
+    const int t_last = min(g * TQ + TQ - 1, p.T - 1);
+    const int64_t vis_end = (int64_t)clamp_len(p.seq_lens[b], p.Lmax) - p.T + 1 + t_last;
+    return vis_end > 0 ? (vis_end + 63) / 64 : 0;
+  };
+
+  // Pass 1: total units.
+  int64_t acc = 0;
+  for (int s = tid; s < n_seg; s += kScoreThreads) acc += seg_units(s);
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  if (l == 0) s_wsum[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t tot = 0;
+    for (int w = 0; w < kScoreWaves; ++w) tot += s_wsum[w];
+    s_total = tot;
+  }
+  __syncthreads();
+  const int64_t U = s_total;
+  const int64_t u0 = U * blockIdx.x / gridDim.x;
+  const int64_t u1 = U * (blockIdx.x + 1) / gridDim.x;
+  if (u0 >= u1) return;
+
+  if (p.hist)
+    for (int i = tid; i < TQ * kHistBins; i += kScoreThreads) lds_hist[i] = 0;
+
+  // Pass 2: walk the segments in chunks of kScoreThreads, with an exclusive
+  // scan of their unit counts, and process those overlapping [u0, u1).
+  int64_t chunk_base = 0;
+  for (int c0 = 0; c0 < n_seg && chunk_base < u1; c0 += kScoreThreads) {
+    const int n_here = min(kScoreThreads, n_seg - c0);
+    const int64_t mine = tid < n_here ? seg_units(c0 + tid) : 0;
+    int64_t v = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int64_t y = __shfl_up(v, o, kWave);
+      if (l >= o) v += y;
+    }
+    if (l == kWave - 1) s_wsum[wave] = v;
+    __syncthreads();
+    int64_t off = 0, chunk_total = 0;
+#pragma unroll
+    for (int w = 0; w < kScoreWaves; ++w) {
+      if (w < wave) off += s_wsum[w];
+      chunk_total += s_wsum[w];
+    }
+    s_excl[tid] = off + v - mine;
+    __syncthreads();
+
+    for (int i = 0; i < n_here; ++i) {
+      const int64_t seg_start = chunk_base + s_excl[i];
+      const int seg = c0 + i;
+      if (seg_start >= u1) break;
+      const int64_t seg_n = (i + 1 < n_here ? s_excl[i + 1] : chunk_total) - s_excl[i];
+      const int64_t seg_end = seg_start + seg_n;
+      if (seg_end <= u0 || seg_n == 0) continue;
+      const int64_t lu0 = max(u0, seg_start) - seg_start;
+      const int64_t lu1 = min(u1, seg_end) - seg_start;
+
+      // ---------------- one segment: sequence b, tokens t0 .. t0+TQ-1 ----------------
+      const int b = seg / G;
+      const int t0 = (seg % G) * TQ;
+      const int len = clamp_len(p.seq_lens[b], p.Lmax);
+      const int vis_last = len - p.T + 1 + min(t0 + TQ - 1, p.T - 1);  // >= 1 here
+
+      // index queries -> LDS (e4m3: quantised), then into registers
+      for (int tq = 0; tq < TQ; ++tq) {
+        const int t = min(t0 + tq, p.T - 1);
+        const int64_t qoff = ((int64_t)b * p.T + t) * kHi * kDi;
+        if constexpr (!FP8) {
+          const i32x4* src = (const i32x4*)((const uint16_t*)p.q_idx + qoff);
+          for (int i = tid; i < kHi * kDi / 8; i += kScoreThreads)
+            ((i32x4*)(lds_q + tq * kQBytes))[i] = src[i];
+        } else {
+          for (int i = tid; i < kHi * kDi / 4; i += kScoreThreads) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int64_t e = qoff + 4 * i + k;
+              const float x = (p.q_dtype == kF32) ? ((const float*)p.q_idx)[e]
+                                                  : bf16_bits_to_f32(((const uint16_t*)p.q_idx)[e]);
+              word |= e4m3_code_exact(e4m3_quantize(x)) << (8 * k);
+            }
+            ((uint32_t*)(lds_q + tq * kQBytes))[i] = word;
+          }
+        }
+      }
+      __syncthreads();
+      QRegs<TQ, FP8> q;
+      float w[TQ][4][4];
+#pragma unroll
+      for (int tq = 0; tq < TQ; ++tq) {
+        const int t = min(t0 + tq, p.T - 1);
+        const float* wrow = p.head_w + ((int64_t)b * p.T + t) * kHi;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[tq][ht][e] = wrow[ht * 16 + 4 * lg + e];
+          const uint8_t* qrow = lds_q + tq * kQBytes + (ht * 16 + lc) * (kQBytes / kHi);
+          if constexpr (!FP8) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) q.a[tq][ht][ks] = ((const bf16x8*)qrow)[ks * 4 + lg];
+          } else {
+            const i32x4* r = (const i32x4*)qrow;
+            const i32x4 x0 = r[2 * lg], x1 = r[2 * lg + 1];
+            q.a[tq][ht] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          }
+        }
+      }
+
+      // this wave's units: lu0 + wave + 4k
+      const int64_t my_first = lu0 + wave;
+      const int n_units = my_first < lu1 ? (int)((lu1 - my_first + kScoreWaves - 1) / kScoreWaves) : 0;
+      const int n_st = n_units * 4;
+      constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
+      const uint8_t* kseq = (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes;
+      const int last_row = len - 1;
+      // first position this lane loads: unit my_first, sub-tile 0, column lc
+      const int64_t pos_base = my_first * 64 + lc;
+
+      auto st_ptr = [&](int x) -> const void* {  // key row this lane loads for sub-tile x
+        int64_t pos = pos_base + (int64_t)kScoreWaves * 64 * (x >> 2) + 16 * (x & 3);
+        if (pos > last_row) pos = last_row;
+        return kseq + pos * kRowBytes;
+      };
+
+      KeyTile<FP8> slot[NSLOT];
+#pragma unroll
+      for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], st_ptr(j), lg);
+
+      float part[TQ][4];
+      for (int x0 = 0; x0 < n_st; x0 += NSLOT) {
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+          const int x = x0 + j;
+          if (x < n_st) {
+            const int st = j & 3;
+#pragma unroll
+            for (int tq = 0; tq < TQ; ++tq) {
+              float s = 0.0f;
+#pragma unroll
+              for (int ht = 0; ht < 4; ++ht) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (!FP8) {
+#pragma unroll
+                  for (int ks = 0; ks < 4; ++ks)
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[tq][ht][ks], slot[j].v[ks], a, 0, 0, 0);
+                } else {
+                  a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[tq][ht], slot[j].v, a, 0, 0, 0,
+                                                                       127, 0, 127);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s = fmaf(w[tq][ht][e], fmaxf(a[e], 0.0f), s);
+              }
+              part[tq][st] = s;
+            }
+          }
+          // refill this slot with the sub-tile NSLOT ahead (rows past the end are clamped)
+          load_key_tile<FP8>(slot[j], st_ptr(x + NSLOT), lg);
+
+          if ((j & 3) == 3 && x < n_st) {
+            // reduce-scatter over the 4 lane groups: lane l gets position 64u + l
+            const int64_t pos = (my_first + (int64_t)kScoreWaves * (x >> 2)) * 64 + l;
+            const bool upper = l >= 32, odd = (lg & 1) != 0;
+            float kscale = 1.0f;
+            if constexpr (FP8) kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
+#pragma unroll
+            for (int tq = 0; tq < TQ; ++tq) {
+              const float r0 = (upper ? part[tq][2] : part[tq][0]) +
+                               __shfl_xor(upper ? part[tq][0] : part[tq][2], 32, kWave);
+              const float r1 = (upper ? part[tq][3] : part[tq][1]) +
+                               __shfl_xor(upper ? part[tq][1] : part[tq][3], 32, kWave);
+              float sc = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16, kWave);
+              if constexpr (FP8) sc *= kscale;
+              const int t = t0 + tq;
+              if (t < p.T && pos < vis_last) {
+                p.scores[((int64_t)b * p.T + t) * p.Lmax + pos] = sc;
+                if (p.hist && pos < (int64_t)len - p.T + 1 + t)
+                  atomicAdd(&lds_hist[tq * kHistBins + (score_key(sc) >> kHistShift)], 1u);
+              }
+            }
+          }
+        }
+      }
+
+      __syncthreads();  // all waves done with lds_q (and their histogram updates)
+      if (p.hist) {
+        for (int tq = 0; tq < TQ; ++tq) {
+          if (t0 + tq >= p.T) break;
+          uint32_t* gh = p.hist + ((int64_t)b * p.T + t0 + tq) * kHistBins;
+          for (int i = tid; i < kHistBins; i += kScoreThreads) {
+            const uint32_t c = lds_hist[tq * kHistBins + i];
+            if (c) {
+              atomicAdd(&gh[i], c);
+              lds_hist[tq * kHistBins + i] = 0;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    chunk_base += chunk_total;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+bool score_mfma_supported(const ScoreParams& p) {
+  if (p.Hi != kHi || p.Di != kDi) return false;
+  if (p.k_dtype == kBF16) return p.q_dtype == kBF16;
+  return p.k_dtype == kE4M3;
+}
+
+template <int TQ, int NSLOT, bool FP8>
+static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream) {
+  constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
+  const size_t lds = TQ * kQBytes + (p.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
+  hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8>), dim3(grid), dim3(kScoreThreads), lds, stream, p);
+}
+
+hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream) {
+  if (allow_mfma && score_mfma_supported(p)) {
+    const int grid = 2 * num_cus;
+    if (p.k_dtype == kBF16) launch_mfma<1, 4, false>(p, grid, stream);
+    else if (p.T == 1) launch_mfma<1, 8, true>(p, grid, stream);
+    else launch_mfma<2, 4, true>(p, grid, stream);
+  } else {
+    dim3 grid((unsigned)((p.Lmax + 255) / 256), (unsigned)(p.B * p.T));
+    hipLaunchKernelGGL(score_generic_kernel, grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,70 @@
+// Kernel parameter blocks and host-side launchers of the DSA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct ScoreParams {
+  const void* q_idx;        // [B,T,Hi,Di] q_dtype
+  const float* head_w;      // [B,T,Hi]
+  const void* k_idx;        // [B,Lmax,Di] k_dtype
+  const float* k_scale;     // [B,Lmax] or null
+  const int32_t* seq_lens;  // [B]
+  float* scores;            // [B,T,Lmax]
+  uint32_t* hist;           // [B*T, 4096] (zeroed) or null
+  int B, T, Hi, Di;
+  int64_t Lmax;
+  int q_dtype, k_dtype;
+};
+
+struct TopkParams {
+  const float* scores;      // [B,T,Lmax]
+  const int32_t* seq_lens;  // [B]
+  const uint32_t* hist;     // [B*T, 4096] score-key histograms (complete)
+  uint32_t* cand;           // [B*T, Lmax] per-chunk ordered candidate positions
+  uint32_t* chunk_cnt;      // [B*T, n_chunks]
+  uint32_t* arrive;         // [B*T] (zeroed)
+  int32_t* topk_idx;        // [B,T,K]
+  int32_t* topk_count;      // [B,T] or null
+  int B, T, K;
+  int64_t Lmax;
+  int chunk;                // positions per select workgroup
+  int n_chunks;             // ceil(Lmax / chunk)
+};
+
+struct MlaParams {
+  const void* q;            // [B,T,H,Dqk]
+  const void* kv;           // [B,Lmax,Dqk]
+  const float* kv_scale;    // [B,Lmax] or null
+  const int32_t* topk_idx;  // [B,T,K]
+  const int32_t* seq_lens;  // [B]
+  void* out;                // [B,T,H,Dv]
+  float* lse;               // [B,T,H] or null
+  float* part_o;            // [splits, B*T, H, Dv] (splits > 1)
+  float* part_ml;           // [splits, B*T, H, 2]  (splits > 1)
+  int B, T, H, Dqk, Dv, K;
+  int64_t Lmax;
+  float scale;
+  int q_dtype, kv_dtype, out_dtype;
+  int splits;               // row splits per query
+  int rows_per_split;       // multiple of the row tile
+};
+
+// index_score.hip
+bool score_mfma_supported(const ScoreParams& p);
+hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream);
+
+// topk.hip
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
+hipError_t launch_hist(const float* scores, const int32_t* seq_lens, uint32_t* hist, int B, int T,
+                       int64_t Lmax, hipStream_t stream);
+hipError_t launch_select(const TopkParams& p, hipStream_t stream);
+
+// sparse_mla.hip
+bool mla_mfma_supported(const MlaParams& p);
+int mla_row_tile();
+hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream);
+
+}  // namespace dsa

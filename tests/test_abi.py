@@ -1,0 +1,158 @@
+"""The C ABI: the library loads without a GPU, exports every symbol that
+include/dsa.h declares, and rejects bad arguments before any HIP call
+(so every case here runs on a machine with no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import indexed_sparse_attention_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="libdsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_forward"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.check_output(["nm", "-D", "--defined-only", dsa.LIB_PATH]).decode()
+    exported = set(re.findall(r"\bT (dsa_[a-z_0-9]+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = dsa.load_library()
+    for n in declared_functions():
+        getattr(lib, n)
+
+
+def test_status_strings_and_version():
+    lib = dsa.load_library()
+    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_status_string(0) == b"DSA_OK"
+    assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def good_problem(**kw):
+    d = dict(batch=2, q_len=1, max_seq_len=4096, idx_heads=64, idx_dim=128, heads=128, qk_dim=576,
+             v_dim=512, top_k=2048)
+    d.update(kw)
+    return dsa.make_problem(**d)
+
+
+BAD_PROBLEMS = [
+    dict(batch=0), dict(q_len=0), dict(max_seq_len=0), dict(q_len=5000), dict(max_seq_len=2 ** 31),
+    dict(idx_heads=0), dict(idx_dim=0), dict(heads=0), dict(qk_dim=0), dict(v_dim=0),
+    dict(v_dim=577), dict(top_k=0), dict(softmax_scale=0.0), dict(softmax_scale=-1.0),
+    dict(softmax_scale=float("inf")), dict(softmax_scale=float("nan")), dict(q_idx_dtype=2),
+    dict(idx_key_dtype=3), dict(q_dtype=2), dict(kv_dtype=-1), dict(out_dtype=2),
+]
+
+FAKE = 0x10000  # a 16-byte aligned non-NULL address: never dereferenced, calls fail validation first
+
+
+@pytest.mark.parametrize("kw", BAD_PROBLEMS)
+def test_invalid_problem_rejected_everywhere(kw):
+    lib = dsa.load_library()
+    p = good_problem(**kw)
+    P = ctypes.byref(p)
+    assert lib.dsa_forward_workspace_size(P) == 0
+    assert lib.dsa_topk_workspace_size(P) == 0
+    assert lib.dsa_sparse_mla_workspace_size(P) == 0
+    f = FAKE
+    assert lib.dsa_index_score(P, f, f, f, None, f, f, None) == 1
+    assert lib.dsa_topk(P, f, f, f, f, f, 1 << 40, None) == 1
+    assert lib.dsa_sparse_mla_decode(P, f, f, None, f, f, f, f, f, 1 << 40, None) == 1
+    assert lib.dsa_forward(P, f, f, f, None, f, f, None, f, None, None, None, f, f, f, 1 << 40, None, None) == 1
+    assert lib.dsa_last_error() != b""
+
+
+def test_null_problem():
+    lib = dsa.load_library()
+    assert lib.dsa_forward_workspace_size(None) == 0
+    assert lib.dsa_index_score(None, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert b"NULL" in lib.dsa_last_error()
+
+
+def test_pointer_checks():
+    lib = dsa.load_library()
+    p = good_problem()
+    P = ctypes.byref(p)
+    f = FAKE
+    # NULL or misaligned tensors
+    assert lib.dsa_index_score(P, None, f, f, None, f, f, None) == 1
+    assert lib.dsa_index_score(P, f + 8, f, f, None, f, f, None) == 1
+    assert lib.dsa_index_score(P, f, f, f + 4, None, f, f, None) == 1
+    assert lib.dsa_index_score(P, f, f, f, None, f, None, None) == 1
+    # scales: required for FP8, forbidden otherwise
+    assert lib.dsa_index_score(P, f, f, f, f, f, f, None) == 1
+    assert b"k_scale" in lib.dsa_last_error()
+    p8 = good_problem(idx_key_dtype=2)
+    assert lib.dsa_index_score(ctypes.byref(p8), f, f, f, None, f, f, None) == 1
+    assert b"k_scale" in lib.dsa_last_error()
+    pk8 = good_problem(kv_dtype=2)
+    assert lib.dsa_sparse_mla_decode(ctypes.byref(pk8), f, f, None, f, f, f, f, f, 1 << 40, None) == 1
+    assert b"kv_scale" in lib.dsa_last_error()
+
+
+def test_workspace_too_small_is_reported_before_launch():
+    lib = dsa.load_library()
+    p = good_problem()
+    P = ctypes.byref(p)
+    need = lib.dsa_forward_workspace_size(P)
+    assert need > 0
+    f = FAKE
+    st = lib.dsa_forward(P, f, f, f, None, f, f, None, f, None, None, None, f, f, f, need - 1, None, None)
+    assert st == 3 and b"workspace" in lib.dsa_last_error()
+    need_t = lib.dsa_topk_workspace_size(P)
+    assert lib.dsa_topk(P, f, f, f, None, f, need_t - 1, None) == 3
+
+
+def test_workspace_sizes_monotone_in_problem_size():
+    lib = dsa.load_library()
+    sizes = [lib.dsa_forward_workspace_size(ctypes.byref(good_problem(max_seq_len=L)))
+             for L in (1024, 4096, 65536, 131072)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    sizes_b = [lib.dsa_forward_workspace_size(ctypes.byref(good_problem(batch=b))) for b in (1, 2, 8, 32)]
+    assert sizes_b == sorted(sizes_b)
+    # Top-K needs at least the score-key histograms and one candidate slot per position
+    p = good_problem()
+    assert lib.dsa_topk_workspace_size(ctypes.byref(p)) >= 2 * 1 * (4096 * 4 + 4096 * 4)
+
+
+def test_stage_events_must_be_non_null():
+    lib = dsa.load_library()
+    p = good_problem()
+    need = lib.dsa_forward_workspace_size(ctypes.byref(p))
+    ev = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    f = FAKE
+    assert lib.dsa_forward(ctypes.byref(p), f, f, f, None, f, f, None, f, None, None, None, f, f,
+                           0x100000, need, None, ev) == 1
+
+
+def test_kernel_choice_reports_paths():
+    p = good_problem()
+    s = dsa.kernel_choice(p)
+    assert "score=mfma" in s and "mla=mfma" in s
+    tiny = dsa.make_problem(batch=1, q_len=1, max_seq_len=256, idx_heads=4, idx_dim=32, heads=4,
+                            qk_dim=80, v_dim=64, top_k=32, q_idx_dtype=0, idx_key_dtype=0, q_dtype=0,
+                            kv_dtype=0, out_dtype=0)
+    s = dsa.kernel_choice(tiny)
+    assert "score=generic" in s and "mla=generic" in s
+    os.environ["DSA_FORCE_GENERIC"] = "1"
+    try:
+        assert "score=generic" in dsa.kernel_choice(p) and "mla=generic" in dsa.kernel_choice(p)
+    finally:
+        del os.environ["DSA_FORCE_GENERIC"]
