@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""DSA decode benchmark on one MI355X: queries/s and achieved HBM GB/s.
+
+Default workload: long-context decode, batch 8, one query token per sequence,
+lengths uniform in [98304, 131072] (max 128K), index keys 64 heads x 128 bf16,
+Top-K 2048, MLA 128 heads over 576-wide bf16 latent rows (512 value columns).
+Synthetic seeded inputs (integer-valued indexer inputs, N(0,1) queries and
+cache), resident in HBM before timing.  A step is one dsa_forward: indexer
+scores over every cached position, Top-K, sparse MLA attention.
+
+Input copies rotate between steps (--rotate, default 3 copies of the index
+keys and latent cache: 4.2 GB) so the 256 MB Infinity Cache cannot serve the
+key stream from one step to the next.  Steps are replayed as HIP graphs (one
+per input copy) unless --no-graph.
+
+Prints one JSON line.  `roofline` covers the dominant kernel (the indexer
+score kernel, timed live with HIP events on the launch stream); `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode queries/s and achieved HBM GB/s (% of peak) at L=128K, K=2048"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode128k")
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--stage-steps", type=int, default=50, help="eager steps timed per stage")
+    ap.add_argument("--cpu-sample", type=int, default=2, help="queries the oracle times (0: skip)")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per score launch")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w):
+    """Bytes the path must move per step: index keys once per sequence, the
+    selected latent rows, queries, weights, outputs and index lists."""
+    import numpy as np
+    kb = {0: 4, 1: 2, 2: 1}[w.idx_key_dtype]
+    cb = {0: 4, 1: 2, 2: 1}[w.kv_dtype]
+    ob = {0: 4, 1: 2}[w.out_dtype]
+    ks = 4 if w.k_scale is not None else 0
+    vs = 4 if w.kv_scale is not None else 0
+    qb = {0: 4, 1: 2}[w.q_dtype]
+    lens = np.minimum(w.seq_lens.astype(np.int64), w.max_seq_len)
+    keys = int(lens.sum()) * (w.idx_dim * kb + ks)
+    sel = 0
+    for b in range(w.batch):
+        for t in range(w.q_len):
+            sel += min(w.top_k, max(w.vis(b, t), 0))
+    gathered = sel * (w.qk_dim * cb + vs)
+    BT = w.batch * w.q_len
+    small = BT * (w.idx_heads * w.idx_dim * 2 + w.idx_heads * 4 + w.heads * w.qk_dim * qb +
+                  w.heads * w.v_dim * ob + 2 * w.top_k * 4)
+    score_kernel = keys + BT * (w.idx_heads * w.idx_dim * 2 + w.idx_heads * 4)
+    return {"total": keys + gathered + small, "keys": keys, "gathered": gathered, "small": small,
+            "score_kernel": score_kernel}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU (context-parallel) "
+                                   "sharding is a design note, not implemented", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import indexed_sparse_attention_amd as dsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = synth.make(args.workload)
+    print(f"# generated {args.workload} in {time.time() - t0:.1f}s: B={w.batch} T={w.q_len} "
+          f"Lmax={w.max_seq_len} lens={w.seq_lens.tolist()}", file=sys.stderr, flush=True)
+
+    def t(a, code):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if code == synth.BF16:
+            x = x.view(torch.bfloat16)
+        return x.to(dev)
+
+    q_idx, head_w = t(w.q_idx, w.q_idx_dtype), t(w.head_w, synth.F32)
+    q, seq_lens = t(w.q, w.q_dtype), t(w.seq_lens, synth.F32)
+    k_scale, kv_scale = t(w.k_scale, synth.F32), t(w.kv_scale, synth.F32)
+    k0, kv0 = t(w.k_idx, w.idx_key_dtype), t(w.kv, w.kv_dtype)
+    R = max(1, args.rotate)
+    k_copies = [k0] + [k0.clone() for _ in range(R - 1)]
+    kv_copies = [kv0] + [kv0.clone() for _ in range(R - 1)]
+    out_dtype = torch.float32 if w.out_dtype == synth.F32 else torch.bfloat16
+    prob = dsa.forward_problem(q_idx, k0, q, kv0, seq_lens, w.top_k, w.v_dim, w.softmax_scale, out_dtype)
+    ws = torch.empty(dsa.forward_workspace_size(prob), dtype=torch.uint8, device=dev)
+    B, T, H = w.batch, w.q_len, w.heads
+    outs = {"out": torch.empty((B, T, H, w.v_dim), dtype=out_dtype, device=dev),
+            "lse": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+            "topk_idx": torch.empty((B, T, w.top_k), dtype=torch.int32, device=dev),
+            "topk_count": torch.empty((B, T), dtype=torch.int32, device=dev)}
+
+    def step(r, stage_events=None):
+        dsa.dsa_forward(q_idx, head_w, k_copies[r], q, kv_copies[r], seq_lens, w.top_k, w.v_dim,
+                        w.softmax_scale, k_scale=k_scale, kv_scale=kv_scale, out_dtype=out_dtype,
+                        out=outs, workspace=ws, stage_events=stage_events)
+
+    # eager reference results (also warms up every kernel)
+    step(0)
+    torch.cuda.synchronize()
+    ref_idx = outs["topk_idx"].clone()
+    ref_out = outs["out"].clone()
+
+    graphs = None
+    if not args.no_graph:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(0)
+        torch.cuda.current_stream().wait_stream(s)
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        # every copy must reproduce the eager result
+        for r in range(R):
+            outs["out"].zero_()
+            graphs[r].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(outs["topk_idx"], ref_idx) and torch.equal(outs["out"], ref_out), \
+                f"graph replay {r} differs from the eager step"
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            step(i % R)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        run(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    assert torch.equal(outs["topk_idx"], ref_idx), "timed steps changed the Top-K result"
+
+    # per-stage durations (eager, events recorded on the launch stream)
+    n_st = max(1, args.stage_steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(dsa.FORWARD_STAGES + 1)] for _ in range(n_st)]
+    for row in evs:
+        for e in row:
+            e.record()  # creates the underlying event
+    torch.cuda.synchronize()
+    for i in range(n_st):
+        step(i % R, stage_events=evs[i])
+    torch.cuda.synchronize()
+    stage_ms = [sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(n_st)) / n_st
+                for k in range(dsa.FORWARD_STAGES)]
+
+    ab = algorithmic_bytes(w)
+    queries = B * T
+    qps = queries / (ms * 1e-3)
+    e2e_gbps = ab["total"] / (ms * 1e-3) / 1e9
+    score_ms = stage_ms[0]
+    score_gbps = ab["score_kernel"] / (score_ms * 1e-3) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("score_kernel_bytes")
+
+    cpu = None
+    if args.cpu_sample > 0:
+        import oracle
+        n = min(args.cpu_sample, queries)
+        want = np.zeros((B, T), bool)
+        want.reshape(-1)[:n] = True
+        c0 = time.time()
+        sc = oracle.index_scores(w, want)
+        idx, _ = oracle.topk(w, sc, want)
+        oracle.sparse_mla(w, idx, want)
+        dt = time.time() - c0
+        gpu_idx = ref_idx.cpu().numpy()
+        match = bool(all(np.array_equal(gpu_idx.reshape(-1, w.top_k)[j], idx.reshape(-1, w.top_k)[j])
+                         for j in range(n)))
+        cpu = {"value": n / dt, "unit": "queries/s",
+               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+               "sample": f"{n} of {queries} queries of this workload: fp64 scores over every visible "
+                         f"position, full-sort Top-K, 128-head two-pass-softmax attention; {dt:.1f} s",
+               "topk_matches_gpu": match}
+
+    line = {
+        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.idx_key_dtype == synth.BF16 else "fp8-e4m3/bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_len": T, "max_seq_len": w.max_seq_len,
+                   "mean_len": float(np.mean(w.seq_lens)), "top_k": w.top_k,
+                   "indexer": f"{w.idx_heads}x{w.idx_dim}", "mla_heads": H, "qk_dim": w.qk_dim,
+                   "v_dim": w.v_dim, "graph": graphs is not None, "rotate": R,
+                   "kernels": dsa.kernel_choice(prob)},
+        "hbm_gbps_e2e": e2e_gbps, "hbm_frac_e2e": e2e_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": ab["total"],
+        "stages_us": {"scores": stage_ms[0] * 1e3, "topk": stage_ms[1] * 1e3, "attention": stage_ms[2] * 1e3},
+        "roofline": {"kernel": "score_mfma_kernel", "bound": "hbm", "achieved": score_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "bytes_per_launch": ab["score_kernel"],
+                     "launch_us": score_ms * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

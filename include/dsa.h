@@ -182,8 +182,10 @@ size_t dsa_forward_workspace_size(const dsa_problem* p);
  *   topk_idx     [B,T,K] output of step 2, or NULL to keep it in ws.
  *   topk_count   [B,T] or NULL.
  *   stage_events NULL, or DSA_FORWARD_STAGES + 1 hipEvent_t handles: event 0
- *                is recorded on `stream` before the first kernel and event i+1
- *                after stage i (for per-stage timing).
+ *                is recorded on `stream` after the workspace counters are
+ *                cleared, just before the score kernel, and event i after
+ *                stage i (1 = scores, 2 = Top-K, 3 = attention), for per-stage
+ *                timing.
  */
 dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
                        const void* k_idx, const float* k_scale, const void* q, const void* kv,

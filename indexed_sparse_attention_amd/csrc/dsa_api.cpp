@@ -98,6 +98,7 @@ TopkLayout topk_layout(const dsa_problem* p) {
   TopkLayout L;
   const int64_t BT = (int64_t)p->batch * p->q_len, Lmax = p->max_seq_len;
   int64_t chunk = std::max<int64_t>(4096, (Lmax * BT + 2047) / 2048);
+  chunk = std::max<int64_t>(chunk, (Lmax + 1023) / 1024);  // at most 1024 chunks per query
   chunk = align_up(chunk, 1024);
   if (chunk > align_up(Lmax, 1024)) chunk = align_up(Lmax, 1024);
   L.chunk = (int)chunk;
@@ -107,7 +108,7 @@ TopkLayout topk_layout(const dsa_problem* p) {
   L.zero_words = BT * kHistBins + BT;
   L.off_cnt = align_up(L.off_arrive + BT * 4, kAlign);
   L.off_cand = align_up(L.off_cnt + BT * L.n_chunks * 4, kAlign);
-  L.bytes = align_up(L.off_cand + BT * Lmax * 4, kAlign);
+  L.bytes = align_up(L.off_cand + BT * Lmax * 8, kAlign);
   return L;
 }
 
@@ -250,7 +251,7 @@ dsa::TopkParams topk_params(const dsa_problem* p, const TopkLayout& L, uint8_t* 
   t.scores = scores;
   t.seq_lens = seq_lens;
   t.hist = (const uint32_t*)(ws + L.off_hist);
-  t.cand = (uint32_t*)(ws + L.off_cand);
+  t.cand = (uint2*)(ws + L.off_cand);
   t.chunk_cnt = (uint32_t*)(ws + L.off_cnt);
   t.arrive = (uint32_t*)(ws + L.off_arrive);
   t.topk_idx = idx;
@@ -425,9 +426,10 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
     return hip_check(hipEventRecord((hipEvent_t)stage_events[i], s), "event record");
   };
 
+  // histogram counters and arrival flags start at zero
+  if ((st = hip_check(dsa::launch_zero_u32(hist, F.tk.zero_words, s), "zero")) != DSA_OK) return st;
   if ((st = rec(0)) != DSA_OK) return st;
   // stage 1: scores (+ fused histogram when the matrix-core kernel runs)
-  if ((st = hip_check(dsa::launch_zero_u32(hist, F.tk.zero_words, s), "zero")) != DSA_OK) return st;
   const bool mfma_score = score_uses_mfma(p);
   auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, sc, hist);
   if (!mfma_score) sp.hist = nullptr;

@@ -8,6 +8,8 @@
 // the weights and the head sum applied to the accumulators in registers.  The
 // same pass builds the per-query histogram of the top 12 bits of each score's
 // order-preserving key, which the Top-K threshold search consumes.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -53,9 +55,11 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
 //
 // Work: for each sequence b and group g of TQ consecutive query tokens, the
 // positions [0, vis_end) with vis_end = vis of the group's last token, cut
-// into units of 64 positions.  All units of all (b, g) segments are laid end
-// to end and split evenly over the grid, so ragged lengths stay balanced.
-// Within a workgroup the four waves take the segment's units round-robin.
+// into units of 64 positions (a "segment").  Each segment gets a contiguous
+// run of workgroups in proportion to its units (at least one), and the waves
+// of that run take its units round-robin, so all of them sweep the segment's
+// key rows together through a window of a few MB: neighbouring waves read
+// neighbouring 16 KB blocks, which keeps HBM pages and channels evenly busy.
 //
 // Per wave and sub-tile of 16 positions, the MFMA computes D[16 heads x 16
 // positions] for each of the 4 head tiles: operand A is the index query (kept
@@ -110,8 +114,8 @@ struct QRegs<TQ, true> {
   i32x8 a[TQ][4];  // [token][head tile], 32 e4m3 codes
 };
 
-template <int TQ, int NSLOT, bool FP8>
-__global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParams p) {
+template <int TQ, int NSLOT, bool FP8, int MINB>
+__global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScoreParams p) {
   // LDS: [TQ] index queries in operand order (bf16: 64 x 128 x 2 B; e4m3: 64 x 128 B),
   // then [TQ][kHistBins] histogram counters when p.hist.
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
@@ -127,11 +131,11 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParam
   const int l = lane_id();
   const int lg = l >> 4;   // lane group 0..3
   const int lc = l & 15;   // column within a 16-wide tile
-  const int G = (p.T + TQ - 1) / TQ;
-  const int n_seg = p.B * G;
+  const int n_groups = (p.T + TQ - 1) / TQ;
+  const int n_seg = p.B * n_groups;
 
   auto seg_units = [&](int seg) -> int64_t {
-    const int b = seg / G, g = seg % G;
+    const int b = seg / n_groups, g = seg % n_groups;
     const int t_last = min(g * TQ + TQ - 1, p.T - 1);
     const int64_t vis_end = (int64_t)clamp_len(p.seq_lens[b], p.Lmax) - p.T + 1 + t_last;
     return vis_end > 0 ? (vis_end + 63) / 64 : 0;
@@ -150,17 +154,22 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParam
   }
   __syncthreads();
   const int64_t U = s_total;
-  const int64_t u0 = U * blockIdx.x / gridDim.x;
-  const int64_t u1 = U * (blockIdx.x + 1) / gridDim.x;
-  if (u0 >= u1) return;
+  if (U == 0) return;
+  const int64_t G = gridDim.x;
+  const int64_t wg = blockIdx.x;
+  // workgroups of a segment starting at unit `start` with `n` units
+  auto wg_first = [&](int64_t start) -> int64_t { return start * G / U; };
+  auto wg_end = [&](int64_t start, int64_t n) -> int64_t {
+    return max(wg_first(start) + 1, (start + n) * G / U);
+  };
 
   if (p.hist)
     for (int i = tid; i < TQ * kHistBins; i += kScoreThreads) lds_hist[i] = 0;
 
   // Pass 2: walk the segments in chunks of kScoreThreads, with an exclusive
-  // scan of their unit counts, and process those overlapping [u0, u1).
+  // scan of their unit counts, and process the segments this workgroup serves.
   int64_t chunk_base = 0;
-  for (int c0 = 0; c0 < n_seg && chunk_base < u1; c0 += kScoreThreads) {
+  for (int c0 = 0; c0 < n_seg && wg_first(chunk_base) <= wg; c0 += kScoreThreads) {
     const int n_here = min(kScoreThreads, n_seg - c0);
     const int64_t mine = tid < n_here ? seg_units(c0 + tid) : 0;
     int64_t v = mine;
@@ -183,16 +192,18 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParam
     for (int i = 0; i < n_here; ++i) {
       const int64_t seg_start = chunk_base + s_excl[i];
       const int seg = c0 + i;
-      if (seg_start >= u1) break;
+      if (wg_first(seg_start) > wg) break;
       const int64_t seg_n = (i + 1 < n_here ? s_excl[i + 1] : chunk_total) - s_excl[i];
-      const int64_t seg_end = seg_start + seg_n;
-      if (seg_end <= u0 || seg_n == 0) continue;
-      const int64_t lu0 = max(u0, seg_start) - seg_start;
-      const int64_t lu1 = min(u1, seg_end) - seg_start;
+      if (seg_n == 0) continue;
+      const int64_t g0 = wg_first(seg_start), g1 = wg_end(seg_start, seg_n);
+      if (wg >= g1) continue;
+      // this wave's units: iw, iw + n_w, iw + 2 n_w, ... of the segment
+      const int64_t n_w = (g1 - g0) * kScoreWaves;
+      const int64_t iw = (wg - g0) * kScoreWaves + wave;
 
       // ---------------- one segment: sequence b, tokens t0 .. t0+TQ-1 ----------------
-      const int b = seg / G;
-      const int t0 = (seg % G) * TQ;
+      const int b = seg / n_groups;
+      const int t0 = (seg % n_groups) * TQ;
       const int len = clamp_len(p.seq_lens[b], p.Lmax);
       const int vis_last = len - p.T + 1 + min(t0 + TQ - 1, p.T - 1);  // >= 1 here
 
@@ -205,16 +216,28 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParam
           for (int i = tid; i < kHi * kDi / 8; i += kScoreThreads)
             ((i32x4*)(lds_q + tq * kQBytes))[i] = src[i];
         } else {
-          for (int i = tid; i < kHi * kDi / 4; i += kScoreThreads) {
+          // 4 consecutive values per word; all loads issued before converting
+          constexpr int kWords = kHi * kDi / 4 / kScoreThreads;  // 8 per thread
+          f32x4 x[kWords];
+          if (p.q_dtype == kF32) {
+            const f32x4* src = (const f32x4*)((const float*)p.q_idx + qoff);
+#pragma unroll
+            for (int k = 0; k < kWords; ++k) x[k] = src[tid + k * kScoreThreads];
+          } else {
+            const i32x2* src = (const i32x2*)((const uint16_t*)p.q_idx + qoff);
+#pragma unroll
+            for (int k = 0; k < kWords; ++k) {
+              const i32x2 v = src[tid + k * kScoreThreads];
+              x[k] = f32x4{bf16_bits_to_f32((uint32_t)v[0] & 0xFFFFu), bf16_bits_to_f32((uint32_t)v[0] >> 16),
+                           bf16_bits_to_f32((uint32_t)v[1] & 0xFFFFu), bf16_bits_to_f32((uint32_t)v[1] >> 16)};
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < kWords; ++k) {
             uint32_t word = 0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int64_t e = qoff + 4 * i + k;
-              const float x = (p.q_dtype == kF32) ? ((const float*)p.q_idx)[e]
-                                                  : bf16_bits_to_f32(((const uint16_t*)p.q_idx)[e]);
-              word |= e4m3_code_exact(e4m3_quantize(x)) << (8 * k);
-            }
-            ((uint32_t*)(lds_q + tq * kQBytes))[i] = word;
+            for (int e = 0; e < 4; ++e) word |= e4m3_code_exact(e4m3_quantize(x[k][e])) << (8 * e);
+            ((uint32_t*)(lds_q + tq * kQBytes))[tid + k * kScoreThreads] = word;
           }
         }
       }
@@ -241,10 +264,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParam
         }
       }
 
-      // this wave's units: lu0 + wave + 4k
-      const int64_t my_first = lu0 + wave;
-      const int n_units = my_first < lu1 ? (int)((lu1 - my_first + kScoreWaves - 1) / kScoreWaves) : 0;
-      const int n_st = n_units * 4;
+      const int64_t my_first = iw;
+      const int n_units = iw < seg_n ? (int)((seg_n - iw + n_w - 1) / n_w) : 0;
       constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
       const uint8_t* kseq = (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes;
       const int last_row = len - 1;
@@ -252,51 +273,64 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParam
       const int64_t pos_base = my_first * 64 + lc;
 
       auto st_ptr = [&](int x) -> const void* {  // key row this lane loads for sub-tile x
-        int64_t pos = pos_base + (int64_t)kScoreWaves * 64 * (x >> 2) + 16 * (x & 3);
+        int64_t pos = pos_base + n_w * 64 * (x >> 2) + 16 * (x & 3);
         if (pos > last_row) pos = last_row;
         return kseq + pos * kRowBytes;
       };
 
+      // Key tiles stream through a ring of NSLOT sub-tile register slots.  The
+      // scores of RB units are kept in registers and stored together after
+      // each batch: on this target loads and stores share one completion
+      // counter, so any store inside the streaming loop would make every
+      // iteration wait for all loads in flight.
+      constexpr int RB = 8;
+      static_assert((4 * RB) % NSLOT == 0 && NSLOT % 4 == 0, "ring must tile the batch");
       KeyTile<FP8> slot[NSLOT];
 #pragma unroll
       for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], st_ptr(j), lg);
 
-      float part[TQ][4];
-      for (int x0 = 0; x0 < n_st; x0 += NSLOT) {
+      const bool upper = l >= 32, odd = (lg & 1) != 0;
+      for (int u0 = 0; u0 < n_units; u0 += RB) {
+        float sbuf[TQ][RB];
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j) {
-          const int x = x0 + j;
-          if (x < n_st) {
-            const int st = j & 3;
+        for (int ub = 0; ub < RB; ++ub) {
+          const bool live = u0 + ub < n_units;
+          // this unit's position for lane l, and (e4m3 keys) its row scale, loaded
+          // before the ring refills so waiting for it does not drain them
+          const int64_t pos = (my_first + n_w * (u0 + ub)) * 64 + l;
+          float kscale = 1.0f;
+          if constexpr (FP8) kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
+          float part[TQ][4];
 #pragma unroll
-            for (int tq = 0; tq < TQ; ++tq) {
-              float s = 0.0f;
+          for (int st = 0; st < 4; ++st) {
+            const int x = (u0 + ub) * 4 + st;
+            const int j = (ub * 4 + st) % NSLOT;
+            if (live) {
 #pragma unroll
-              for (int ht = 0; ht < 4; ++ht) {
-                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (!FP8) {
+              for (int tq = 0; tq < TQ; ++tq) {
+                float sacc = 0.0f;
 #pragma unroll
-                  for (int ks = 0; ks < 4; ++ks)
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[tq][ht][ks], slot[j].v[ks], a, 0, 0, 0);
-                } else {
-                  a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[tq][ht], slot[j].v, a, 0, 0, 0,
-                                                                       127, 0, 127);
+                for (int ht = 0; ht < 4; ++ht) {
+                  f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+                  if constexpr (!FP8) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[tq][ht][ks], slot[j].v[ks], a, 0, 0, 0);
+                  } else {
+                    a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[tq][ht], slot[j].v, a, 0, 0, 0,
+                                                                         127, 0, 127);
+                  }
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) sacc = fmaf(w[tq][ht][e], fmaxf(a[e], 0.0f), sacc);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s = fmaf(w[tq][ht][e], fmaxf(a[e], 0.0f), s);
+                part[tq][st] = sacc;
               }
-              part[tq][st] = s;
             }
+            // refill this slot with the sub-tile NSLOT ahead (rows past the end are clamped)
+            load_key_tile<FP8>(slot[j], st_ptr(x + NSLOT), lg);
           }
-          // refill this slot with the sub-tile NSLOT ahead (rows past the end are clamped)
-          load_key_tile<FP8>(slot[j], st_ptr(x + NSLOT), lg);
-
-          if ((j & 3) == 3 && x < n_st) {
+          if (live) {
             // reduce-scatter over the 4 lane groups: lane l gets position 64u + l
-            const int64_t pos = (my_first + (int64_t)kScoreWaves * (x >> 2)) * 64 + l;
-            const bool upper = l >= 32, odd = (lg & 1) != 0;
-            float kscale = 1.0f;
-            if constexpr (FP8) kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
 #pragma unroll
             for (int tq = 0; tq < TQ; ++tq) {
               const float r0 = (upper ? part[tq][2] : part[tq][0]) +
@@ -305,13 +339,20 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_mfma_kernel(ScoreParam
                                __shfl_xor(upper ? part[tq][1] : part[tq][3], 32, kWave);
               float sc = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16, kWave);
               if constexpr (FP8) sc *= kscale;
-              const int t = t0 + tq;
-              if (t < p.T && pos < vis_last) {
-                p.scores[((int64_t)b * p.T + t) * p.Lmax + pos] = sc;
-                if (p.hist && pos < (int64_t)len - p.T + 1 + t)
-                  atomicAdd(&lds_hist[tq * kHistBins + (score_key(sc) >> kHistShift)], 1u);
-              }
+              sbuf[tq][ub] = sc;
+              if (p.hist && t0 + tq < p.T && pos < (int64_t)len - p.T + 1 + t0 + tq)
+                atomicAdd(&lds_hist[tq * kHistBins + (score_key(sc) >> kHistShift)], 1u);
             }
+          }
+        }
+        // store the batch
+#pragma unroll
+        for (int ub = 0; ub < RB; ++ub) {
+          const int64_t pos = (my_first + n_w * (u0 + ub)) * 64 + l;
+          if (u0 + ub < n_units && pos < vis_last) {
+#pragma unroll
+            for (int tq = 0; tq < TQ; ++tq)
+              if (t0 + tq < p.T) p.scores[((int64_t)b * p.T + t0 + tq) * p.Lmax + pos] = sbuf[tq][ub];
           }
         }
       }
@@ -346,19 +387,36 @@ bool score_mfma_supported(const ScoreParams& p) {
   return p.k_dtype == kE4M3;
 }
 
-template <int TQ, int NSLOT, bool FP8>
+template <int TQ, int NSLOT, bool FP8, int MINB = 2>
 static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream) {
   constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
   const size_t lds = TQ * kQBytes + (p.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
-  hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8>), dim3(grid), dim3(kScoreThreads), lds, stream, p);
+  hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB>), dim3(grid), dim3(kScoreThreads), lds, stream, p);
 }
 
+static int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return (e && *e) ? atoi(e) : dflt;
+}
+
+// Launch shape: DSA_SCORE_WGS_PER_CU workgroups per compute unit (default 1)
+// or DSA_SCORE_WGS workgroups in total,
+// and DSA_SCORE_VARIANT selecting the bf16 key-prefetch depth / occupancy
+// (0: 4 sub-tiles with 2 workgroups/CU occupancy; 1: 8 sub-tiles, 1/CU).
 hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream) {
   if (allow_mfma && score_mfma_supported(p)) {
-    const int grid = 2 * num_cus;
-    if (p.k_dtype == kBF16) launch_mfma<1, 4, false>(p, grid, stream);
-    else if (p.T == 1) launch_mfma<1, 8, true>(p, grid, stream);
-    else launch_mfma<2, 4, true>(p, grid, stream);
+    int grid = max(1, env_int("DSA_SCORE_WGS_PER_CU", 1)) * num_cus;
+    if (env_int("DSA_SCORE_WGS", 0) > 0) grid = env_int("DSA_SCORE_WGS", 0);
+    if (p.k_dtype == kBF16) {
+      switch (env_int("DSA_SCORE_VARIANT", 1)) {
+        case 0: launch_mfma<1, 4, false, 2>(p, grid, stream); break;
+        default: launch_mfma<1, 8, false, 1>(p, grid, stream); break;
+      }
+    } else if (p.T == 1) {
+      launch_mfma<1, 8, true>(p, grid, stream);
+    } else {
+      launch_mfma<2, 4, true>(p, grid, stream);
+    }
   } else {
     dim3 grid((unsigned)((p.Lmax + 255) / 256), (unsigned)(p.B * p.T));
     hipLaunchKernelGGL(score_generic_kernel, grid, dim3(256), 0, stream, p);

@@ -23,7 +23,7 @@ struct TopkParams {
   const float* scores;      // [B,T,Lmax]
   const int32_t* seq_lens;  // [B]
   const uint32_t* hist;     // [B*T, 4096] score-key histograms (complete)
-  uint32_t* cand;           // [B*T, Lmax] per-chunk ordered candidate positions
+  uint2* cand;              // [B*T, Lmax] per-chunk ordered (key, position) candidates
   uint32_t* chunk_cnt;      // [B*T, n_chunks]
   uint32_t* arrive;         // [B*T] (zeroed)
   int32_t* topk_idx;        // [B,T,K]
@@ -31,7 +31,7 @@ struct TopkParams {
   int B, T, K;
   int64_t Lmax;
   int chunk;                // positions per select workgroup
-  int n_chunks;             // ceil(Lmax / chunk)
+  int n_chunks;             // ceil(Lmax / chunk) <= 1024
 };
 
 struct MlaParams {

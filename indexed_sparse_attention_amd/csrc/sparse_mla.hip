@@ -113,30 +113,54 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel: qk_dim 576, v_dim 512, 64 heads per workgroup (4 waves x
-// 16 heads), row tiles of 32 selected rows staged in LDS.
+// Matrix-core kernel: qk_dim 576, v_dim 512, 64 heads per workgroup, row tiles
+// of 32 selected rows staged in LDS once and read by every wave.
+//
+// Eight waves: wave w serves heads 16*(w/2) .. +16 and half h = w%2 of the
+// work: dims [288h, 288h+288) of the QK^T contraction and value columns
+// [256h, 256h+256) of PV.  The two halves of a head group exchange their
+// partial logits through LDS, so each wave keeps only 36 query registers and
+// 64 output accumulators.
 //
 // QK^T is computed transposed, S^T[row, head], with the LDS row tile as MFMA
-// operand A and the wave's 16 query heads (registers) as operand B, so in the
-// 16x16 accumulator lane l holds head l%16 and rows 4*(l/16)+e of each
-// 16-row half.  Those 8 probabilities are exactly the A operand the PV product
-// needs for head l%16 (the 32 k-slots of the PV step are a fixed permutation
-// of the tile's rows; the V operand is read from LDS in the same order), so P
-// never leaves registers.  Online softmax (running max/sum per head) in base 2.
-// Splits of the index list run in separate workgroups and are merged by
-// mla_combine_kernel with their (max, sum) pairs.
+// operand A and 16 query heads (registers) as operand B; in the 16x16
+// accumulator lane l holds head l%16 and rows 4*(l/16)+e of each 16-row half.
+// Those 8 probabilities are exactly the A operand the PV product needs for
+// head l%16 (the PV k-slots are a fixed permutation of the tile's rows; the V
+// operand is read from LDS in the same order), so P never leaves registers.
+// The V operand needs 8 rows at one column per lane; gfx950's LDS transpose
+// read (ds_read_b64_tr_b16) delivers that from the row-major tile: within each
+// 16-lane group, output lane j receives element j%4 of the 4-element segments
+// addressed by lanes j/4 + 4k, k < 4.  MFMA lane i of 16-row block mt reads
+// LDS row perm(mt, i) = 16 mt + 2 (i%4) + (i/4)%2 + 8 (i/8), which keeps both
+// the QK^T operand reads and the transpose reads free of bank conflicts.
+// Online softmax (running max/sum per head) in base 2.  Row splits of the
+// index list run in separate workgroups and are merged by mla_combine_kernel
+// from their (O, max, sum) partials.
 // ---------------------------------------------------------------------------
 constexpr int kDqk = 576, kDv = 512;
-constexpr int kMlaWaves = 4, kMlaThreads = kMlaWaves * kWave;
-constexpr int kHeadsPerWave = 16, kHeadsPerWG = kMlaWaves * kHeadsPerWave;
+constexpr int kMlaWaves = 8, kMlaThreads = kMlaWaves * kWave;
+constexpr int kHeadsPerWave = 16, kHeadsPerWG = 64;
 constexpr int kTile = 32;
 constexpr int kRowStride = kDqk + 8;  // bf16 elements per LDS row (1168 bytes)
-constexpr int kKSteps = kDqk / 32;    // 18
-constexpr int kNTiles = kDv / 16;     // 32
+constexpr int kKStepsHalf = kDqk / 2 / 32;  // 9 k-steps of 32 dims per half
+constexpr int kNTilesHalf = kDv / 2 / 16;   // 16 value tiles of 16 columns per half
+constexpr int kIdxCap = 2048;               // index entries staged in LDS at a time
 
 int mla_row_tile() { return kTile; }
 
-// Global chunks (16 bytes) per tile and per thread for staging.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+// LDS row holding row i (0..15) of 16-row block mt of the MFMA row order.
+__device__ __forceinline__ int tile_row(int mt, int i) {
+  return 16 * mt + 2 * (i & 3) + ((i >> 2) & 1) + 8 * (i >> 3);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+// Global 16-byte chunks per tile and per thread for staging.
 template <bool FP8>
 struct Stage {
   static constexpr int kChunksPerRow = FP8 ? kDqk / 16 : kDqk / 8;  // 36 or 72
@@ -146,23 +170,19 @@ struct Stage {
   float sc[kPerThread];
 };
 
+// s_pos: resolved row positions of the current tile (-1: not a row).
 template <bool FP8>
-__device__ __forceinline__ void stage_load(Stage<FP8>& st, const MlaParams& p, const int32_t* sel,
-                                           int j0, int n_rows, int b, int len) {
+__device__ __forceinline__ void stage_load(Stage<FP8>& st, const MlaParams& p, const int32_t* s_pos,
+                                           int64_t seq_row0) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < Stage<FP8>::kPerThread; ++k) {
     const int id = tid + k * kMlaThreads;
-    const int r = id / Stage<FP8>::kChunksPerRow, c = id % Stage<FP8>::kChunksPerRow;
-    int32_t pos = 0;
-    if (id < Stage<FP8>::kChunks && r < n_rows) {
-      const int32_t v = sel[j0 + r];
-      pos = (v >= 0 && v < len) ? v : 0;
-    }
-    const int64_t row = (int64_t)b * p.Lmax + pos;
     if (id < Stage<FP8>::kChunks) {
-      const i32x4* src = (const i32x4*)((const uint8_t*)p.kv + row * (FP8 ? kDqk : 2 * kDqk)) + c;
-      st.v[k] = *src;
+      const int r = id / Stage<FP8>::kChunksPerRow, c = id % Stage<FP8>::kChunksPerRow;
+      const int32_t pos = max(s_pos[r], 0);
+      const int64_t row = seq_row0 + pos;
+      st.v[k] = *((const i32x4*)((const uint8_t*)p.kv + row * (FP8 ? kDqk : 2 * kDqk)) + c);
       if constexpr (FP8) st.sc[k] = p.kv_scale[row];
     }
   }
@@ -201,142 +221,167 @@ __device__ __forceinline__ void stage_store(const Stage<FP8>& st, uint16_t* lds)
 template <bool FP8>
 __global__ __launch_bounds__(kMlaThreads) void mla_mfma_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_rows[kTile * kRowStride];
+  __shared__ float s_xch[kMlaWaves][8][kWave];  // partial logits exchanged between halves
+  __shared__ int32_t s_idx[kIdxCap];            // resolved positions of the split's rows
 
   const int split = blockIdx.x, bt = blockIdx.y, hg = blockIdx.z;
   const int b = bt / p.T;
   const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
   const int lg = l >> 4, lc = l & 15;
+  const int half = wave & 1;
   const int len = clamp_len(p.seq_lens[b], p.Lmax);
-  const int h0 = hg * kHeadsPerWG + wave * kHeadsPerWave;  // this wave's first head
+  const int h0 = hg * kHeadsPerWG + (wave >> 1) * kHeadsPerWave;  // this wave's first head
+  const int64_t seq_row0 = (int64_t)b * p.Lmax;
   const int32_t* sel = p.topk_idx + (int64_t)bt * p.K;
   const int j_begin = split * p.rows_per_split;
   const int j_end = min(p.K, j_begin + p.rows_per_split);
 
-  // query heads h0 + lc, dims 32 ks + 8 lg .. +8  (operand B of QK^T)
-  bf16x8 qreg[kKSteps];
+  // query heads h0 + lc, dims 288 half + 32 ks + 8 lg .. +8  (operand B of QK^T)
+  bf16x8 qreg[kKStepsHalf];
   {
-    const bf16x8* qrow = (const bf16x8*)((const uint16_t*)p.q + ((int64_t)bt * p.H + h0 + lc) * kDqk);
+    const bf16x8* qrow =
+        (const bf16x8*)((const uint16_t*)p.q + ((int64_t)bt * p.H + h0 + lc) * kDqk + 288 * half);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qrow[ks * 4 + lg];
+    for (int ks = 0; ks < kKStepsHalf; ++ks) qreg[ks] = qrow[ks * 4 + lg];
   }
   const float zscale = p.scale * 1.4426950408889634f;  // logits in base-2 units
 
-  f32x4 o[kNTiles];
+  f32x4 o[kNTilesHalf];
 #pragma unroll
-  for (int n = 0; n < kNTiles; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < kNTilesHalf; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;  // for head h0 + lc
 
   Stage<FP8> stage;
-  if (j_begin < j_end) stage_load<FP8>(stage, p, sel, j_begin, min(kTile, j_end - j_begin), b, len);
-
-  for (int j0 = j_begin; j0 < j_end; j0 += kTile) {
-    const int n_rows = min(kTile, j_end - j0);
-    __syncthreads();
-    stage_store<FP8>(stage, s_rows);
-    __syncthreads();
-    if (j0 + kTile < j_end) stage_load<FP8>(stage, p, sel, j0 + kTile, min(kTile, j_end - j0 - kTile), b, len);
-
-    // ---- S^T[32 rows x 16 heads] ----
-    f32x4 s[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* arow = s_rows + (mt * 16 + lc) * kRowStride + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(arow + ks * 32);
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s[mt], 0, 0, 0);
-      }
+  for (int jc = j_begin; jc < j_end; jc += kIdxCap) {
+    const int jc_end = min(j_end, jc + kIdxCap);
+    __syncthreads();  // previous users of s_idx are done
+    for (int i = tid; i < jc_end - jc; i += kMlaThreads) {
+      const int32_t v = sel[jc + i];
+      s_idx[i] = (v >= 0 && v < len) ? v : -1;
     }
-    // ---- online softmax for head h0 + lc over rows 4 lg + e (+16) ----
-    float z[2][4];
-    float tmax = -INFINITY;
+    // pad the last tile
+    for (int i = jc_end - jc + tid; i < ((jc_end - jc + kTile - 1) / kTile) * kTile; i += kMlaThreads)
+      s_idx[i] = -1;
+    __syncthreads();
+    stage_load<FP8>(stage, p, s_idx, seq_row0);
+
+    for (int j0 = 0; j0 < jc_end - jc; j0 += kTile) {
+      __syncthreads();
+      stage_store<FP8>(stage, s_rows);
+      __syncthreads();
+      if (j0 + kTile < jc_end - jc) stage_load<FP8>(stage, p, s_idx + j0 + kTile, seq_row0);
+
+      // ---- partial S^T[32 rows x 16 heads] over this wave's 288 dims ----
+      f32x4 s[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* arow = s_rows + tile_row(mt, lc) * kRowStride + 288 * half + 8 * lg;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = mt * 16 + 4 * lg + e;
-        bool valid = r < n_rows;
-        if (valid) {
-          const int32_t v = sel[j0 + r];
-          valid = v >= 0 && v < len;
+        for (int ks = 0; ks < kKStepsHalf; ++ks) {
+          const bf16x8 a = *(const bf16x8*)(arow + ks * 32);
+          s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s[mt], 0, 0, 0);
         }
-        z[mt][e] = valid ? s[mt][e] * zscale : -INFINITY;
-        tmax = fmaxf(tmax, z[mt][e]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.0f, psum = 0.0f;
-    float pr[2][4];
-    if (m_new == -INFINITY) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pr[mt][e] = 0.0f;
-    } else {
-      alpha = exp2f(m_run - m_new);  // m_run = -inf gives 0
+        for (int e = 0; e < 4; ++e) s_xch[wave][mt * 4 + e][l] = s[mt][e];
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[mt][e] += s_xch[wave ^ 1][mt * 4 + e][l];
+
+      // ---- online softmax for head h0 + lc over rows 4 lg + e (+16) ----
+      float z[2][4];
+      float tmax = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pr[mt][e] = exp2f(z[mt][e] - m_new);
-          psum += pr[mt][e];
+          const bool valid = s_idx[j0 + tile_row(mt, 4 * lg + e)] >= 0;
+          z[mt][e] = valid ? s[mt][e] * zscale : -INFINITY;
+          tmax = fmaxf(tmax, z[mt][e]);
         }
-    }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // rescale O rows (heads h0 + 4 lg + e) by their head's alpha
-    float al[4];
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float m_new = fmaxf(m_run, tmax);
+      float alpha = 1.0f, psum = 0.0f;
+      float pr[2][4];
+      if (m_new == -INFINITY) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * lg + e, kWave);
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int n = 0; n < kNTiles; ++n)
+          for (int e = 0; e < 4; ++e) pr[mt][e] = 0.0f;
+      } else {
+        alpha = exp2f(m_run - m_new);  // m_run = -inf gives 0
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[n][e] *= al[e];
-
-    // P operand (A of PV): head lc, k-slot 8 lg + j <-> row (j < 4 ? 4 lg + j : 16 + 4 lg + j - 4)
-    bf16x8 pa;
-    {
-      uint16_t pb[8];
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[j >> 2][j & 3]);
-      pa = __builtin_bit_cast(bf16x8, pb);
-    }
-    // ---- O[16 heads x 512] += P V ----
-    const uint16_t* v0 = s_rows + (4 * lg) * kRowStride + lc;
-    const uint16_t* v1 = s_rows + (16 + 4 * lg) * kRowStride + lc;
-#pragma unroll
-    for (int n = 0; n < kNTiles; ++n) {
-      uint16_t vb[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vb[j] = v0[j * kRowStride + n * 16];
-        vb[4 + j] = v1[j * kRowStride + n * 16];
+          for (int e = 0; e < 4; ++e) {
+            pr[mt][e] = exp2f(z[mt][e] - m_new);
+            psum += pr[mt][e];
+          }
       }
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
+      psum += __shfl_xor(psum, 16, kWave);
+      psum += __shfl_xor(psum, 32, kWave);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+
+      // rescale O rows (heads h0 + 4 lg + e) by their head's alpha
+      float al[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * lg + e, kWave);
+#pragma unroll
+      for (int n = 0; n < kNTilesHalf; ++n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[n][e] *= al[e];
+
+      // P operand (A of PV): head lc, k-slot 8 lg + j <-> row (j < 4 ? 4 lg + j : 16 + 4 lg + j - 4)
+      bf16x8 pa;
+      {
+        uint16_t pb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[j >> 2][j & 3]);
+        pa = __builtin_bit_cast(bf16x8, pb);
+      }
+      // ---- O[16 heads x 256 value columns] += P V ----
+      // k-slot 8 lg + k (k < 4) is LDS row tile_row(0, 4 lg + k), slot 8 lg + 4 + k
+      // is tile_row(1, 4 lg + k): lane lc addresses row k = lc/4 of its group and
+      // columns 4 (lc%4) .. +4 of the 16-column tile.
+      const uint16_t* va = s_rows + tile_row(0, 4 * lg + (lc >> 2)) * kRowStride + 256 * half + 4 * (lc & 3);
+      const uint16_t* vb = s_rows + tile_row(1, 4 * lg + (lc >> 2)) * kRowStride + 256 * half + 4 * (lc & 3);
+#pragma unroll
+      for (int n = 0; n < kNTilesHalf; ++n) {
+        const i16x4 lo = lds_read_tr16(va + n * 16);
+        const i16x4 hi = lds_read_tr16(vb + n * 16);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, (i32x4){__builtin_bit_cast(int, (short2){lo[0], lo[1]}),
+                                                               __builtin_bit_cast(int, (short2){lo[2], lo[3]}),
+                                                               __builtin_bit_cast(int, (short2){hi[0], hi[1]}),
+                                                               __builtin_bit_cast(int, (short2){hi[2], hi[3]})});
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vop, o[n], 0, 0, 0);
+      }
     }
   }
 
-  // ---- write-out: O rows are heads h0 + 4 lg + e, columns 16 n + lc ----
+  // ---- write-out: O rows are heads h0 + 4 lg + e, columns 256 half + 16 n + lc ----
   float lh[4], mh[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     lh[e] = __shfl(l_run, 4 * lg + e, kWave);
     mh[e] = __shfl(m_run, 4 * lg + e, kWave);
   }
+  const int col0 = 256 * half + lc;
   if (p.splits == 1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int h = h0 + 4 * lg + e;
       const float inv = lh[e] > 0.0f ? 1.0f / lh[e] : 0.0f;
-      const int64_t ooff = ((int64_t)bt * p.H + h) * kDv;
+      const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + col0;
 #pragma unroll
-      for (int n = 0; n < kNTiles; ++n) store_out(p.out, p.out_dtype, ooff + n * 16 + lc, o[n][e] * inv);
-      if (p.lse && lc == 0)
+      for (int n = 0; n < kNTilesHalf; ++n) store_out(p.out, p.out_dtype, ooff + n * 16, o[n][e] * inv);
+      if (p.lse && lc == 0 && half == 0)
         p.lse[(int64_t)bt * p.H + h] = lh[e] > 0.0f ? (mh[e] + log2f(lh[e])) * 0.6931471805599453f : -INFINITY;
     }
   } else {
@@ -345,10 +390,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_mfma_kernel(MlaParams p) {
     for (int e = 0; e < 4; ++e) {
       const int h = h0 + 4 * lg + e;
       const int64_t slot = ((int64_t)split * BT + bt) * p.H + h;
-      float* po = p.part_o + slot * kDv;
+      float* po = p.part_o + slot * kDv + col0;
 #pragma unroll
-      for (int n = 0; n < kNTiles; ++n) po[n * 16 + lc] = o[n][e];
-      if (lc == 0) {
+      for (int n = 0; n < kNTilesHalf; ++n) po[n * 16] = o[n][e];
+      if (lc == 0 && half == 0) {
         p.part_ml[slot * 2] = mh[e];
         p.part_ml[slot * 2 + 1] = lh[e];
       }
@@ -356,34 +401,54 @@ __global__ __launch_bounds__(kMlaThreads) void mla_mfma_kernel(MlaParams p) {
   }
 }
 
-// Merge the per-split partial (O, max, sum) of one (query, head).
+// Merge the per-split partials (O, max, sum) of one (query, head): 128
+// threads, 4 consecutive value columns each.
 __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
+  __shared__ float s_w[64];
+  __shared__ float s_stat[2];
   const int h = blockIdx.x, bt = blockIdx.y;
+  const int tid = threadIdx.x;
   const int64_t BT = (int64_t)p.B * p.T;
-  const float* ml = p.part_ml + ((int64_t)bt * p.H + h) * 2;
-  const int64_t ml_stride = BT * p.H * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s)
-    if (ml[s * ml_stride + 1] > 0.0f) M = fmaxf(M, ml[s * ml_stride]);
-  float L = 0.0f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float ls = ml[s * ml_stride + 1];
-    if (ls > 0.0f) L += ls * exp2f(ml[s * ml_stride] - M);
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const int64_t ooff = ((int64_t)bt * p.H + h) * p.Dv;
-  const float* po = p.part_o + ((int64_t)bt * p.H + h) * p.Dv;
-  const int64_t po_stride = BT * p.H * p.Dv;
-  for (int d = threadIdx.x; d < p.Dv; d += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float ls = ml[s * ml_stride + 1];
-      if (ls > 0.0f) acc = fmaf(po[s * po_stride + d], exp2f(ml[s * ml_stride] - M), acc);
+  const int64_t slot0 = (int64_t)bt * p.H + h;
+  const int64_t slot_stride = BT * p.H;
+  if (tid < kWave) {
+    float ms = -INFINITY, ls = 0.0f;
+    if (tid < p.splits) {
+      ms = p.part_ml[(slot0 + tid * slot_stride) * 2];
+      ls = p.part_ml[(slot0 + tid * slot_stride) * 2 + 1];
     }
-    store_out(p.out, p.out_dtype, ooff + d, acc * inv);
+    const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
+    const float wgt = (ls > 0.0f) ? exp2f(ms - M) : 0.0f;
+    const float L = wave_sum(ls * wgt);
+    if (tid < 64) s_w[tid] = wgt;
+    if (tid == 0) {
+      s_stat[0] = M;
+      s_stat[1] = L;
+    }
   }
-  if (p.lse && threadIdx.x == 0)
-    p.lse[(int64_t)bt * p.H + h] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  __syncthreads();
+  const float M = s_stat[0], L = s_stat[1];
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const int d = tid * 4;
+  if (d < p.Dv) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* po = p.part_o + slot0 * p.Dv + d;
+    const int64_t stride = slot_stride * p.Dv;
+#pragma unroll 4
+    for (int s = 0; s < p.splits; ++s) {
+      const float wgt = s_w[s];
+      const f32x4 v = *(const f32x4*)(po + s * stride);
+      acc[0] = fmaf(v[0], wgt, acc[0]);
+      acc[1] = fmaf(v[1], wgt, acc[1]);
+      acc[2] = fmaf(v[2], wgt, acc[2]);
+      acc[3] = fmaf(v[3], wgt, acc[3]);
+    }
+    const int64_t ooff = slot0 * p.Dv + d;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) store_out(p.out, p.out_dtype, ooff + k, acc[k] * inv);
+  }
+  if (p.lse && tid == 0)
+    p.lse[slot0] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
 bool mla_mfma_supported(const MlaParams& p) {
@@ -401,7 +466,7 @@ hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)p.H, (unsigned)(p.B * p.T)), dim3(128), 0,
-                       stream, p);
+                       stream, p);  // needs Dv <= 512 and splits <= 64
     return hipGetLastError();
   }
   hipLaunchKernelGGL(mla_generic_kernel, dim3((unsigned)p.H, (unsigned)(p.B * p.T)), dim3(kGenThreads),

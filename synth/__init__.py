@@ -201,6 +201,10 @@ def make(name: str, seed: Optional[int] = None, **overrides) -> Workload:
     oracle finishes in seconds.
     """
     r = dict(WORKLOADS[name])
+    if "max_seq_len" in overrides and "len_range" not in overrides:
+        L = overrides["max_seq_len"]
+        lo, hi = r["len_range"]
+        overrides = dict(overrides, len_range=(min(lo, L), min(hi, L)))
     r.update(overrides)
     if seed is None:
         seed = 0xD5A00000 + r["number"]
