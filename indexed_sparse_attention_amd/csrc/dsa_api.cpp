@@ -90,8 +90,8 @@ dsa_status validate_problem(const dsa_problem* p) {
 // ------------------------------------------------------------------ Top-K layout
 struct TopkLayout {
   int chunk, n_chunks;
-  int64_t off_hist, off_arrive, zero_words;  // zeroed region = [off_hist, off_hist + zero_words*4)
-  int64_t off_cnt, off_cand, bytes;
+  int64_t off_hist, off_sub, off_bcnt, zero_words;  // zeroed region = [off_hist, off_hist + zero_words*4)
+  int64_t off_hdr, off_cnt, off_above, off_cand, off_blist, bytes;
 };
 
 TopkLayout topk_layout(const dsa_problem* p) {
@@ -104,11 +104,15 @@ TopkLayout topk_layout(const dsa_problem* p) {
   L.chunk = (int)chunk;
   L.n_chunks = (int)((Lmax + chunk - 1) / chunk);
   L.off_hist = 0;
-  L.off_arrive = BT * kHistBins * 4;
-  L.zero_words = BT * kHistBins + BT;
-  L.off_cnt = align_up(L.off_arrive + BT * 4, kAlign);
-  L.off_cand = align_up(L.off_cnt + BT * L.n_chunks * 4, kAlign);
-  L.bytes = align_up(L.off_cand + BT * Lmax * 8, kAlign);
+  L.off_sub = BT * kHistBins * 4;
+  L.off_bcnt = L.off_sub + BT * kHistBins * 4;
+  L.zero_words = 2 * BT * kHistBins + BT;
+  L.off_hdr = align_up(L.off_bcnt + BT * 4, kAlign);
+  L.off_cnt = align_up(L.off_hdr + BT * 8, kAlign);
+  L.off_above = align_up(L.off_cnt + BT * L.n_chunks * 4, kAlign);
+  L.off_cand = align_up(L.off_above + BT * L.n_chunks * 4, kAlign);
+  L.off_blist = align_up(L.off_cand + BT * Lmax * 8, kAlign);
+  L.bytes = align_up(L.off_blist + BT * Lmax * 8, kAlign);
   return L;
 }
 
@@ -253,7 +257,11 @@ dsa::TopkParams topk_params(const dsa_problem* p, const TopkLayout& L, uint8_t* 
   t.hist = (const uint32_t*)(ws + L.off_hist);
   t.cand = (uint2*)(ws + L.off_cand);
   t.chunk_cnt = (uint32_t*)(ws + L.off_cnt);
-  t.arrive = (uint32_t*)(ws + L.off_arrive);
+  t.chunk_above = (uint32_t*)(ws + L.off_above);
+  t.bin_list = (uint2*)(ws + L.off_blist);
+  t.bin_count = (uint32_t*)(ws + L.off_bcnt);
+  t.sub_hist = (uint32_t*)(ws + L.off_sub);
+  t.header = (uint2*)(ws + L.off_hdr);
   t.topk_idx = idx;
   t.topk_count = cnt;
   t.B = p->batch;

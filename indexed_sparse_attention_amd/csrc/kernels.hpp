@@ -23,9 +23,13 @@ struct TopkParams {
   const float* scores;      // [B,T,Lmax]
   const int32_t* seq_lens;  // [B]
   const uint32_t* hist;     // [B*T, 4096] score-key histograms (complete)
+  uint32_t* sub_hist;       // [B*T, 4096] next-12-bit histograms of the threshold bin (zeroed)
+  uint2* header;            // [B*T] (threshold bin, entries above it)
   uint2* cand;              // [B*T, Lmax] per-chunk ordered (key, position) candidates
-  uint32_t* chunk_cnt;      // [B*T, n_chunks]
-  uint32_t* arrive;         // [B*T] (zeroed)
+  uint2* bin_list;          // [B*T, Lmax] the query's threshold-bin entries (unordered)
+  uint32_t* bin_count;      // [B*T] entries in bin_list (zeroed)
+  uint32_t* chunk_cnt;      // [B*T, n_chunks] candidates per chunk
+  uint32_t* chunk_above;    // [B*T, n_chunks] candidates above the threshold bin per chunk
   int32_t* topk_idx;        // [B,T,K]
   int32_t* topk_count;      // [B,T] or null
   int B, T, K;

@@ -60,6 +60,18 @@ def test_forward_matches_oracle(case):
     _full_check(w)
 
 
+@pytest.mark.parametrize("mode", ["row", "chunk"])
+def test_topk_modes_match_oracle(mode):
+    # both Top-K strategies (one workgroup per query; chunked with a finishing
+    # workgroup) on ragged decode and on two draft tokens with fp8 keys
+    os.environ["DSA_TOPK_MODE"] = mode
+    try:
+        _full_check(_case("decode128k", batch=3, max_seq_len=30000, len_range=(17000, 30000)))
+        _full_check(_case("fp8_1m", batch=2, max_seq_len=20000, len_range=(12000, 20000), top_k=1500))
+    finally:
+        del os.environ["DSA_TOPK_MODE"]
+
+
 def test_entry_points_separately():
     w = _case("decode128k", batch=2, max_seq_len=9000, len_range=(5000, 9000), top_k=1024)
     d = G.to_device(w)
@@ -101,11 +113,17 @@ def test_edge_fewer_visible_than_k_and_empty():
     assert np.all(np.isneginf(got["lse"][1]))
 
 
-def test_edge_all_scores_tie():
-    # q_idx = 0 makes every score 0: the K lowest positions win
-    w = _case("decode8k", batch=2, max_seq_len=5000, top_k=300)
+@pytest.mark.parametrize("mode", ["row", "chunk"])
+def test_edge_all_scores_tie(mode):
+    # q_idx = 0 makes every score 0: the K lowest positions win; 9000 tied
+    # candidates also overflow the row-mode LDS candidate buffer
+    w = _case("decode8k", batch=2, max_seq_len=9000, top_k=300)
     w.q_idx[:] = 0
-    got, _ = _full_check(w)
+    os.environ["DSA_TOPK_MODE"] = mode
+    try:
+        got, _ = _full_check(w)
+    finally:
+        del os.environ["DSA_TOPK_MODE"]
     assert np.array_equal(got["topk_idx"][:, 0], np.tile(np.arange(300), (2, 1)))
 
 
