@@ -15,7 +15,10 @@ per input copy) unless --no-graph.
 
 Prints one JSON line.  `roofline` covers the dominant kernel (the indexer
 score kernel, timed live with HIP events on the launch stream); `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+times the CPU oracle on a bounded sample of the same workload.  `traffic`
+comes from a counter record under profiles/ (see --copy-probe and
+--traffic-from) and is null when that record was taken from other kernel
+sources.
 """
 import argparse
 import json
@@ -35,14 +38,104 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode128k")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--stage-steps", type=int, default=50, help="eager steps timed per stage")
-    ap.add_argument("--cpu-sample", type=int, default=2, help="queries the oracle times (0: skip)")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per score launch")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle baseline: repeat whole-batch oracle passes for at least this long (0: skip)")
+    ap.add_argument("--cpu-max-passes", type=int, default=100)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB copy kernel first (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-probe run into the traffic record, then exit")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 1 << 30
+SCORE_KERNEL = "score_mfma_kernel"
+SCORE_SOURCES = ("index_score.hip", "common.hpp", "kernels.hpp")
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"{SCORE_KERNEL}_{workload}_traffic.txt")
+
+
+def score_source_hash():
+    """Hash of the sources the score kernel is built from: a traffic record
+    taken from another version of the kernel is stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "indexed_sparse_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_csv(path, counter):
+    """Per-dispatch values of one counter from a rocprofv3 counter_collection CSV:
+    list of (kernel name, value)."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic_record(fetch_csv, write_csv, workload):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the score kernel, each scaled
+    by the factor that makes the copy probe's counter equal its known size."""
+    import numpy as np
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = read_counter_csv(path, name)
+        copy = [v for k, v in rows if "neg" in k.lower()]
+        score = [v for k, v in rows if SCORE_KERNEL in k]
+        if not copy or not score:
+            raise SystemExit(f"{path}: no copy-probe or {SCORE_KERNEL} dispatch with {name}")
+        factor = COPY_PROBE_BYTES / (max(copy) * 1024.0)
+        out[name] = (float(np.mean(score)) * 1024.0, factor, len(score), max(copy) * 1024.0)
+    fetch, fw = out["FETCH_SIZE"][0], out["FETCH_SIZE"][1]
+    write, ww = out["WRITE_SIZE"][0], out["WRITE_SIZE"][1]
+    traffic = fetch * fw + write * ww
+    path = traffic_path(workload)
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of {SCORE_KERNEL} per launch, workload {workload}\n")
+        f.write("# from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over\n")
+        f.write(f"#   python3 bench.py --workload {workload} --no-graph --copy-probe --steps 3 --warmup 1 "
+                "--stage-steps 2 --cpu-seconds 0\n")
+        f.write(f"# each scaled by (copy probe bytes {COPY_PROBE_BYTES}) / (counter bytes of the copy probe)\n")
+        f.write(f"source_hash: {score_source_hash()}\n")
+        f.write(f"dispatches: {out['FETCH_SIZE'][2]}\n")
+        f.write(f"fetch_bytes_raw: {fetch:.0f}\n")
+        f.write(f"fetch_factor: {fw:.4f}\n")
+        f.write(f"copy_probe_fetch_bytes_raw: {out['FETCH_SIZE'][3]:.0f}\n")
+        f.write(f"write_bytes_raw: {write:.0f}\n")
+        f.write(f"write_factor: {ww:.4f}\n")
+        f.write(f"copy_probe_write_bytes_raw: {out['WRITE_SIZE'][3]:.0f}\n")
+        f.write(f"traffic_bytes: {traffic:.0f}\n")
+    print(open(path).read())
+
+
+def read_traffic_record(workload):
+    """Calibrated HBM bytes per score launch, or None when there is no record
+    or it was taken from other kernel sources."""
+    path = traffic_path(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != score_source_hash():
+        return None
+    return float(kv["traffic_bytes"])
 
 
 def algorithmic_bytes(w):
@@ -72,6 +165,9 @@ def algorithmic_bytes(w):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU (context-parallel) "
                                    "sharding is a design note, not implemented", "n_gpus": args.gpus}))
@@ -117,6 +213,13 @@ def main():
         dsa.dsa_forward(q_idx, head_w, k_copies[r], q, kv_copies[r], seq_lens, w.top_k, w.v_dim,
                         w.softmax_scale, k_scale=k_scale, kv_scale=kv_scale, out_dtype=out_dtype,
                         out=outs, workspace=ws, stage_events=stage_events)
+
+    if args.copy_probe:  # one plain streaming copy of known size for counter calibration
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # eager reference results (also warms up every kernel)
     step(0)
@@ -182,29 +285,30 @@ def main():
     e2e_gbps = ab["total"] / (ms * 1e-3) / 1e9
     score_ms = stage_ms[0]
     score_gbps = ab["score_kernel"] / (score_ms * 1e-3) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("score_kernel_bytes")
+    traffic = read_traffic_record(args.workload)
 
     cpu = None
-    if args.cpu_sample > 0:
+    if args.cpu_seconds > 0:
+        # the oracle as it stands, on whole batches of this workload's queries,
+        # repeated until the time bound; its first pass is checked against the GPU
         import oracle
-        n = min(args.cpu_sample, queries)
-        want = np.zeros((B, T), bool)
-        want.reshape(-1)[:n] = True
+        passes, match = 0, None
         c0 = time.time()
-        sc = oracle.index_scores(w, want)
-        idx, _ = oracle.topk(w, sc, want)
-        oracle.sparse_mla(w, idx, want)
-        dt = time.time() - c0
-        gpu_idx = ref_idx.cpu().numpy()
-        match = bool(all(np.array_equal(gpu_idx.reshape(-1, w.top_k)[j], idx.reshape(-1, w.top_k)[j])
-                         for j in range(n)))
-        cpu = {"value": n / dt, "unit": "queries/s",
-               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
-               "sample": f"{n} of {queries} queries of this workload: fp64 scores over every visible "
-                         f"position, full-sort Top-K, 128-head two-pass-softmax attention; {dt:.1f} s",
+        while True:
+            sc = oracle.index_scores(w)
+            idx, _ = oracle.topk(w, sc)
+            oracle.sparse_mla(w, idx)
+            passes += 1
+            if match is None:
+                match = bool(np.array_equal(ref_idx.cpu().numpy(), idx))
+            dt = time.time() - c0
+            if dt >= args.cpu_seconds or passes >= args.cpu_max_passes:
+                break
+        cpu = {"value": passes * queries / dt, "unit": "queries/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{passes} pass(es) over all {queries} queries of this workload (fp64 scores over "
+                         f"every visible position, full-sort Top-K, {H}-head two-pass-softmax attention) "
+                         f"in {dt:.1f} s",
                "topk_matches_gpu": match}
 
     line = {

@@ -72,6 +72,7 @@ def _load():
         for f in (lib.oracle_index_scores, lib.oracle_topk, lib.oracle_sparse_mla,
                   lib.oracle_attention_weights):
             f.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_value.restype = ctypes.c_double
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
@@ -163,3 +164,8 @@ def forward(w, want=None) -> dict:
     idx, cnt = topk(w, s, want)
     out, lse = sparse_mla(w, idx, want)
     return {"scores": s, "idx": idx, "count": cnt, "out": out, "lse": lse}
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().oracle_num_threads())

@@ -38,6 +38,7 @@
  * both index Q and K.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -53,6 +54,9 @@ typedef struct {
 } oracle_dims;
 
 /* ---------------- decoders (the formats' definitions) ---------------- */
+
+/* OpenMP threads the oracle's parallel loops use. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 double oracle_bf16_value(uint16_t bits) {
   uint32_t u = (uint32_t)bits << 16; /* bf16 is the upper half of binary32 */
