@@ -202,7 +202,7 @@ def main():
     kv_copies = [kv0] + [kv0.clone() for _ in range(R - 1)]
     out_dtype = torch.float32 if w.out_dtype == synth.F32 else torch.bfloat16
     prob = dsa.forward_problem(q_idx, k0, q, kv0, seq_lens, w.top_k, w.v_dim, w.softmax_scale, out_dtype)
-    ws = torch.empty(dsa.forward_workspace_size(prob), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(dsa.forward_workspace_size(prob), dtype=torch.uint8, device=dev)  # counters start at zero
     B, T, H = w.batch, w.q_len, w.heads
     outs = {"out": torch.empty((B, T, H, w.v_dim), dtype=out_dtype, device=dev),
             "lse": torch.empty((B, T, H), dtype=torch.float32, device=dev),

@@ -31,6 +31,14 @@
  *    0 .. vis-1 with vis = len_b - q_len + 1 + t (causal).
  *  - Reentrant; concurrent calls on different streams must not share a
  *    workspace or an output buffer.
+ *  - Workspaces of dsa_topk and dsa_forward begin with counters (score
+ *    histograms, per-query arrival counts) that must be zero when a call
+ *    starts: the first dsa_workspace_zero_bytes(p) bytes.  Every call that
+ *    returns DSA_OK leaves them zero again, so a workspace is zeroed once
+ *    (dsa_workspace_init, or allocate it zeroed) and then reused without a
+ *    clearing pass per call.  Zero it again after a call that failed with
+ *    DSA_ERR_HIP, or before using it for a problem whose counter region is
+ *    larger.  The rest of a workspace may hold anything.
  *
  * Numeric contract
  * ----------------
@@ -107,7 +115,7 @@ typedef struct dsa_problem {
   int32_t out_dtype;    /* DSA_F32 | DSA_BF16 */
 } dsa_problem;
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 #define DSA_FORWARD_STAGES 3 /* indexer scores, Top-K, sparse attention */
 
 int dsa_abi_version(void);
@@ -138,13 +146,28 @@ dsa_status dsa_index_score(const dsa_problem* p, const void* q_idx, const float*
 size_t dsa_topk_workspace_size(const dsa_problem* p);
 
 /*
+ * Leading bytes of a dsa_topk or dsa_forward workspace for problem p that
+ * must be zero when a call starts (the counters; see the conventions above).
+ * 0 if p is invalid.
+ */
+size_t dsa_workspace_zero_bytes(const dsa_problem* p);
+
+/*
+ * Zero-fills ws_bytes bytes of ws on `stream` (a kernel, so it can be
+ * captured in a HIP graph).  ws: device pointer, 4-byte aligned; ws_bytes a
+ * multiple of 4.  Use once on a new workspace (or after a DSA_ERR_HIP).
+ */
+dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, struct ihipStream_t* stream);
+
+/*
  * Per-query Top-K (step 2).
  *   scores     [B,T,Lmax] fp32 (only s < vis is read).
  *   topk_idx   [B,T,K] int32 output: the selected positions in ascending order;
  *              the last K - count entries are -1.
  *   topk_count [B,T] int32 output count = min(K, max(vis, 0)), or NULL.
- *   ws         device scratch of at least dsa_topk_workspace_size(p) bytes
- *              (any contents; 16-byte aligned).
+ *   ws         device scratch of at least dsa_topk_workspace_size(p) bytes,
+ *              16-byte aligned, whose first dsa_workspace_zero_bytes(p)
+ *              bytes are zero (left zero on success).
  */
 dsa_status dsa_topk(const dsa_problem* p, const float* scores, const int32_t* seq_lens,
                     int32_t* topk_idx, int32_t* topk_count, void* ws, size_t ws_bytes,
@@ -181,9 +204,12 @@ size_t dsa_forward_workspace_size(const dsa_problem* p);
  *   scores       [B,T,Lmax] fp32 output of step 1, or NULL to keep it in ws.
  *   topk_idx     [B,T,K] output of step 2, or NULL to keep it in ws.
  *   topk_count   [B,T] or NULL.
+ *   ws           dsa_forward_workspace_size(p) bytes, 256-byte aligned,
+ *                whose first dsa_workspace_zero_bytes(p) bytes are zero
+ *                (left zero on success).
  *   stage_events NULL, or DSA_FORWARD_STAGES + 1 hipEvent_t handles: event 0
- *                is recorded on `stream` after the workspace counters are
- *                cleared, just before the score kernel, and event i after
+ *                is recorded on `stream` just before the score kernel, and
+ *                event i after
  *                stage i (1 = scores, 2 = Top-K, 3 = attention), for per-stage
  *                timing.
  */

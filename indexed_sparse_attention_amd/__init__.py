@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_index_score.argtypes = [PP, P, P, P, P, P, P, P]
     lib.dsa_topk_workspace_size.argtypes = [PP]
+    lib.dsa_workspace_zero_bytes.argtypes = [PP]
+    lib.dsa_workspace_init.argtypes = [P, ctypes.c_size_t, P]
     lib.dsa_topk.argtypes = [PP, P, P, P, P, P, ctypes.c_size_t, P]
     lib.dsa_sparse_mla_workspace_size.argtypes = [PP]
     lib.dsa_sparse_mla_decode.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -82,7 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
               lib.dsa_kernel_choice):
         f.restype = ctypes.c_int
     for f in (lib.dsa_topk_workspace_size, lib.dsa_sparse_mla_workspace_size,
-              lib.dsa_forward_workspace_size):
+              lib.dsa_forward_workspace_size, lib.dsa_workspace_zero_bytes):
         f.restype = ctypes.c_size_t
     _lib = lib
     return lib
@@ -140,6 +142,17 @@ def topk_workspace_size(p: Problem) -> int:
     return load_library().dsa_topk_workspace_size(ctypes.byref(p))
 
 
+def workspace_zero_bytes(p: Problem) -> int:
+    """Leading workspace bytes (counters) that must be zero when a call starts;
+    every successful call leaves them zero."""
+    return load_library().dsa_workspace_zero_bytes(ctypes.byref(p))
+
+
+def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    """Zero a workspace on the device (once per new workspace)."""
+    _check(load_library().dsa_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def sparse_mla_workspace_size(p: Problem) -> int:
     return load_library().dsa_sparse_mla_workspace_size(ctypes.byref(p))
 
@@ -155,7 +168,8 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Option
         return workspace
     if workspace is not None:
         return workspace
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    # zeroed: the leading counter region must be zero on the first call
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def _index_problem(q_idx, k_idx, seq_lens, top_k=1) -> dict:

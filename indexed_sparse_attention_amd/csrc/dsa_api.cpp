@@ -88,9 +88,12 @@ dsa_status validate_problem(const dsa_problem* p) {
 }
 
 // ------------------------------------------------------------------ Top-K layout
+// The counters (histograms, threshold-bin counts, arrivals) come first, at
+// offset 0 of every workspace that holds them: they must be zero when a call
+// starts, and every successful call leaves them zero again.
 struct TopkLayout {
   int chunk, n_chunks;
-  int64_t off_hist, off_sub, off_bcnt, zero_words;  // zeroed region = [off_hist, off_hist + zero_words*4)
+  int64_t off_hist, off_sub, off_bcnt, off_done, zero_bytes;
   int64_t off_hdr, off_cnt, off_above, off_cand, off_blist, bytes;
 };
 
@@ -106,8 +109,9 @@ TopkLayout topk_layout(const dsa_problem* p) {
   L.off_hist = 0;
   L.off_sub = BT * kHistBins * 4;
   L.off_bcnt = L.off_sub + BT * kHistBins * 4;
-  L.zero_words = 2 * BT * kHistBins + BT;
-  L.off_hdr = align_up(L.off_bcnt + BT * 4, kAlign);
+  L.off_done = L.off_bcnt + BT * 4;
+  L.zero_bytes = L.off_done + BT * 4;
+  L.off_hdr = align_up(L.zero_bytes, kAlign);
   L.off_cnt = align_up(L.off_hdr + BT * 8, kAlign);
   L.off_above = align_up(L.off_cnt + BT * L.n_chunks * 4, kAlign);
   L.off_cand = align_up(L.off_above + BT * L.n_chunks * 4, kAlign);
@@ -124,6 +128,7 @@ struct MlaLayout {
 
 bool mla_uses_mfma(const dsa_problem* p) {
   return !force_generic() && p->qk_dim == 576 && p->v_dim == 512 && p->heads % 64 == 0 &&
+         (int64_t)p->top_k <= 64 * (int64_t)dsa::mla_max_rows_per_split() &&
          p->q_dtype == DSA_BF16 && (p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_FP8_E4M3);
 }
 
@@ -140,6 +145,9 @@ MlaLayout mla_layout(const dsa_problem* p) {
     const int64_t max_s = std::min<int64_t>(64, (p->top_k + tile - 1) / tile);
     if (env_int("DSA_MLA_SPLITS", 0) > 0) s = env_int("DSA_MLA_SPLITS", 0);
     s = std::max<int64_t>(1, std::min(s, max_s));
+    // each split stages its whole index list in LDS
+    const int64_t cap = dsa::mla_max_rows_per_split();
+    s = std::max<int64_t>(s, (p->top_k + cap - 1) / cap);
     L.rows_per_split = (int)align_up((p->top_k + s - 1) / s, tile);
     L.splits = (p->top_k + L.rows_per_split - 1) / L.rows_per_split;
   }
@@ -147,7 +155,7 @@ MlaLayout mla_layout(const dsa_problem* p) {
   L.off_ml = 0;
   L.bytes = 0;
   if (L.splits > 1) {
-    L.off_ml = align_up((int64_t)L.splits * BT * p->heads * p->v_dim * 4, kAlign);
+    L.off_ml = align_up((int64_t)L.splits * BT * p->heads * p->v_dim * 2, kAlign);
     L.bytes = align_up(L.off_ml + (int64_t)L.splits * BT * p->heads * 2 * 4, kAlign);
   }
   return L;
@@ -254,14 +262,15 @@ dsa::TopkParams topk_params(const dsa_problem* p, const TopkLayout& L, uint8_t* 
   dsa::TopkParams t;
   t.scores = scores;
   t.seq_lens = seq_lens;
-  t.hist = (const uint32_t*)(ws + L.off_hist);
+  t.hist = (uint32_t*)(ws + L.off_hist);
   t.cand = (uint2*)(ws + L.off_cand);
   t.chunk_cnt = (uint32_t*)(ws + L.off_cnt);
-  t.chunk_above = (uint32_t*)(ws + L.off_above);
   t.bin_list = (uint2*)(ws + L.off_blist);
   t.bin_count = (uint32_t*)(ws + L.off_bcnt);
-  t.sub_hist = (uint32_t*)(ws + L.off_sub);
+  t.done = (uint32_t*)(ws + L.off_done);
   t.header = (uint2*)(ws + L.off_hdr);
+  t.chunk_above = (uint32_t*)(ws + L.off_above);
+  t.sub_hist = (uint32_t*)(ws + L.off_sub);
   t.topk_idx = idx;
   t.topk_count = cnt;
   t.B = p->batch;
@@ -284,7 +293,7 @@ dsa::MlaParams mla_params(const dsa_problem* p, const MlaLayout& L, uint8_t* ws,
   m.seq_lens = seq_lens;
   m.out = out;
   m.lse = lse;
-  m.part_o = L.splits > 1 ? (float*)(ws + L.off_o) : nullptr;
+  m.part_o = L.splits > 1 ? (uint16_t*)(ws + L.off_o) : nullptr;
   m.part_ml = L.splits > 1 ? (float*)(ws + L.off_ml) : nullptr;
   m.B = p->batch;
   m.T = p->q_len;
@@ -366,11 +375,25 @@ dsa_status dsa_topk(const dsa_problem* p, const float* scores, const int32_t* se
   REQUIRE(ws && aligned(ws, 16), "ws must be non-NULL and 16-byte aligned");
   uint8_t* w = (uint8_t*)ws;
   hipStream_t s = stream;
-  if ((st = hip_check(dsa::launch_zero_u32((uint32_t*)(w + L.off_hist), L.zero_words, s), "zero")) != DSA_OK) return st;
   if ((st = hip_check(dsa::launch_hist(scores, seq_lens, (uint32_t*)(w + L.off_hist), p->batch, p->q_len,
                                        p->max_seq_len, s), "histogram")) != DSA_OK) return st;
   auto tp = topk_params(p, L, w, scores, seq_lens, topk_idx, topk_count);
   if ((st = hip_check(dsa::launch_select(tp, s), "select")) != DSA_OK) return st;
+  return ok();
+}
+
+size_t dsa_workspace_zero_bytes(const dsa_problem* p) {
+  if (validate_problem(p) != DSA_OK) return 0;
+  return (size_t)topk_layout(p).zero_bytes;  // the counters sit at offset 0 of both workspaces
+}
+
+dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, struct ihipStream_t* stream) {
+  if (ws_bytes == 0) return ok();
+  REQUIRE(ws && aligned(ws, 4), "ws must be non-NULL and 4-byte aligned");
+  REQUIRE(ws_bytes % 4 == 0, "ws_bytes must be a multiple of 4 (got %zu)", ws_bytes);
+  dsa_status st;
+  if ((st = hip_check(dsa::launch_zero_u32((uint32_t*)ws, (int64_t)(ws_bytes / 4), stream), "zero")) != DSA_OK)
+    return st;
   return ok();
 }
 
@@ -434,8 +457,7 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
     return hip_check(hipEventRecord((hipEvent_t)stage_events[i], s), "event record");
   };
 
-  // histogram counters and arrival flags start at zero
-  if ((st = hip_check(dsa::launch_zero_u32(hist, F.tk.zero_words, s), "zero")) != DSA_OK) return st;
+  // the counters at the start of the workspace are zero on entry (and on return)
   if ((st = rec(0)) != DSA_OK) return st;
   // stage 1: scores (+ fused histogram when the matrix-core kernel runs)
   const bool mfma_score = score_uses_mfma(p);

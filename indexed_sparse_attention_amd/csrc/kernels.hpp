@@ -22,12 +22,13 @@ struct ScoreParams {
 struct TopkParams {
   const float* scores;      // [B,T,Lmax]
   const int32_t* seq_lens;  // [B]
-  const uint32_t* hist;     // [B*T, 4096] score-key histograms (complete)
-  uint32_t* sub_hist;       // [B*T, 4096] next-12-bit histograms of the threshold bin (zeroed)
-  uint2* header;            // [B*T] (threshold bin, entries above it)
+  uint32_t* hist;           // [B*T, 4096] score-key histograms (complete; cleared after use)
+  uint32_t* sub_hist;       // [B*T, 4096] next-12-bit histograms of the threshold bin (zero on entry)
   uint2* cand;              // [B*T, Lmax] per-chunk ordered (key, position) candidates
   uint2* bin_list;          // [B*T, Lmax] the query's threshold-bin entries (unordered)
-  uint32_t* bin_count;      // [B*T] entries in bin_list (zeroed)
+  uint32_t* bin_count;      // [B*T] entries in bin_list (zero on entry)
+  uint32_t* done;           // [B*T] emit workgroups of the query finished (zero on entry)
+  uint2* header;            // [B*T] (threshold bin, entries above it)
   uint32_t* chunk_cnt;      // [B*T, n_chunks] candidates per chunk
   uint32_t* chunk_above;    // [B*T, n_chunks] candidates above the threshold bin per chunk
   int32_t* topk_idx;        // [B,T,K]
@@ -46,8 +47,8 @@ struct MlaParams {
   const int32_t* seq_lens;  // [B]
   void* out;                // [B,T,H,Dv]
   float* lse;               // [B,T,H] or null
-  float* part_o;            // [splits, B*T, H, Dv] (splits > 1)
-  float* part_ml;           // [splits, B*T, H, 2]  (splits > 1)
+  uint16_t* part_o;         // [splits, B*T, H, Dv] bf16, each split's output normalised by its own sum (splits > 1)
+  float* part_ml;           // [splits, B*T, H, 2]  running max (base 2) and sum of each split (splits > 1)
   int B, T, H, Dqk, Dv, K;
   int64_t Lmax;
   float scale;
@@ -69,6 +70,7 @@ hipError_t launch_select(const TopkParams& p, hipStream_t stream);
 // sparse_mla.hip
 bool mla_mfma_supported(const MlaParams& p);
 int mla_row_tile();
+int mla_max_rows_per_split();  // index entries one MFMA-kernel workgroup stages in LDS
 hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream);
 
 }  // namespace dsa

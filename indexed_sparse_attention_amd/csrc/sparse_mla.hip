@@ -116,11 +116,20 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
 // Matrix-core kernel: qk_dim 576, v_dim 512, 64 heads per workgroup, row tiles
 // of 32 selected rows staged in LDS once and read by every wave.
 //
-// Eight waves: wave w serves heads 16*(w/2) .. +16 and half h = w%2 of the
-// work: dims [288h, 288h+288) of the QK^T contraction and value columns
-// [256h, 256h+256) of PV.  The two halves of a head group exchange their
-// partial logits through LDS, so each wave keeps only 36 query registers and
-// 64 output accumulators.
+// Four waves, one per SIMD; wave w owns heads 16w .. 16w+15 of the group
+// completely: all 576 dims of the QK^T contraction and all 512 value columns
+// of PV, so no partial logits cross waves and the only barrier per tile is
+// the one that hands over an LDS tile buffer.  With one wave per SIMD the
+// wave may hold up to 512 registers: 72 for its queries and 128 accumulators.
+//
+// Row tiles rotate through three LDS buffers: while tile t is computed, tiles
+// t+1 and t+2 are in flight.  A bf16 cache is copied global -> LDS directly
+// (global_load_lds_dwordx4, no registers); an e4m3 cache goes through
+// registers one tile ahead and is decoded to bf16 (x its row scale) on the
+// way in.  A tile is 32 rows x 72 chunks of 16 bytes, stored in 1 KB segments
+// of 8 rows x 8 chunks with the chunk slot XOR-swizzled by row, so that one
+// DMA instruction fills one segment with eight 128-byte row pieces and both
+// operand reads below are free of bank conflicts.
 //
 // QK^T is computed transposed, S^T[row, head], with the LDS row tile as MFMA
 // operand A and 16 query heads (registers) as operand B; in the 16x16
@@ -129,326 +138,558 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
 // head l%16 (the PV k-slots are a fixed permutation of the tile's rows; the V
 // operand is read from LDS in the same order), so P never leaves registers.
 // The V operand needs 8 rows at one column per lane; gfx950's LDS transpose
-// read (ds_read_b64_tr_b16) delivers that from the row-major tile: within each
-// 16-lane group, output lane j receives element j%4 of the 4-element segments
-// addressed by lanes j/4 + 4k, k < 4.  MFMA lane i of 16-row block mt reads
-// LDS row perm(mt, i) = 16 mt + 2 (i%4) + (i/4)%2 + 8 (i/8), which keeps both
-// the QK^T operand reads and the transpose reads free of bank conflicts.
-// Online softmax (running max/sum per head) in base 2.  Row splits of the
-// index list run in separate workgroups and are merged by mla_combine_kernel
-// from their (O, max, sum) partials.
+// read (ds_read_b64_tr_b16) delivers that: within each 16-lane group, output
+// lane j receives element j%4 of the 4-element segments addressed by lanes
+// j/4 + 4k, k < 4.  MFMA lane i of 16-row block mt uses tile row
+// perm(mt, i) = 16 mt + 2 (i%4) + (i/4)%2 + 8 (i/8).  Online softmax in base 2
+// with a lazily moved reference max.  Row splits of the index list run in
+// separate workgroups and are merged by mla_combine_kernel from their
+// (O, max, sum) partials.
 // ---------------------------------------------------------------------------
 constexpr int kDqk = 576, kDv = 512;
-constexpr int kMlaWaves = 8, kMlaThreads = kMlaWaves * kWave;
-constexpr int kHeadsPerWave = 16, kHeadsPerWG = 64;
+constexpr int kMlaWaves = 4, kMlaThreads = kMlaWaves * kWave;
+constexpr int kHeadsPerWave = 16, kHeadsPerWG = kMlaWaves * kHeadsPerWave;
 constexpr int kTile = 32;
-constexpr int kRowStride = kDqk + 8;  // bf16 elements per LDS row (1168 bytes)
-constexpr int kKStepsHalf = kDqk / 2 / 32;  // 9 k-steps of 32 dims per half
-constexpr int kNTilesHalf = kDv / 2 / 16;   // 16 value tiles of 16 columns per half
-constexpr int kIdxCap = 2048;               // index entries staged in LDS at a time
+constexpr int kChunksPerRow = kDqk / 8;                  // 72 bf16 chunks of 16 bytes
+constexpr int kTileBytes = kTile * kChunksPerRow * 16;   // 36 KB
+constexpr int kKSteps = kDqk / 32;                       // 18 k-steps of 32 dims
+constexpr int kNTiles = kDv / 16;                        // 32 value tiles of 16 columns
+constexpr int kIdxCap = 2048;                            // most index entries of one split
+constexpr int kIdxPad = 4 * kTile;                       // the last tile's padding + 3 tiles read ahead
+constexpr float kSlack = 8.0f;                           // log2 headroom before the running max moves
+static_assert(kMlaWaves * 8 == kTile, "one 8-row group of the tile per wave");
 
 int mla_row_tile() { return kTile; }
+int mla_max_rows_per_split() { return kIdxCap; }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
-// LDS row holding row i (0..15) of 16-row block mt of the MFMA row order.
+// Tile row used by row i (0..15) of 16-row block mt of the MFMA row order.
 __device__ __forceinline__ int tile_row(int mt, int i) {
   return 16 * mt + 2 * (i & 3) + ((i >> 2) & 1) + 8 * (i >> 3);
 }
 
-__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+// Byte offset of 16-byte chunk c (0..71) of tile row r (0..31).
+__device__ __forceinline__ int chunk_off(int r, int c) {
+  return ((r >> 3) * 9 + (c >> 3)) * 1024 + 16 * (8 * (r & 7) + ((c ^ r ^ (r >> 3)) & 7));
 }
 
-// Global 16-byte chunks per tile and per thread for staging.
-template <bool FP8>
-struct Stage {
-  static constexpr int kChunksPerRow = FP8 ? kDqk / 16 : kDqk / 8;  // 36 or 72
-  static constexpr int kChunks = kTile * kChunksPerRow;
+// Transpose reads of the PV operand, 4 value tiles (8 reads) per group, in
+// inline asm: the compiler's own wait insertion treats the transpose-read
+// intrinsic as aliasing every pending global->LDS copy and would drain them
+// all before each read.  Here the tile being read is known to be complete
+// (its copies were waited for before the barrier that opened the tile), so
+// only the LDS counter matters: each block issues the next group's reads and
+// then waits until at most those 8 are outstanding, which completes the
+// previous group.  The previous group's registers are in/out operands of
+// that block, so nothing reads them before the wait, and no register of an
+// in-flight read is reused.
+struct TrGroup {
+  i16x4 r[8];  // [2 k + h]: value tile 4 g + k, row half h
+};
+
+// addr[2 k + h]: LDS byte address of value tile k (mod 4), row half h, of the
+// tile's first 4-tile group; group G sits G KB further (immediate offset).
+template <int G>
+__device__ __forceinline__ void tr_issue_wait(TrGroup& nxt, TrGroup& prev, const uint32_t (&addr)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n"
+      "ds_read_b64_tr_b16 %1, %17 offset:%24\n"
+      "ds_read_b64_tr_b16 %2, %18 offset:%24\n"
+      "ds_read_b64_tr_b16 %3, %19 offset:%24\n"
+      "ds_read_b64_tr_b16 %4, %20 offset:%24\n"
+      "ds_read_b64_tr_b16 %5, %21 offset:%24\n"
+      "ds_read_b64_tr_b16 %6, %22 offset:%24\n"
+      "ds_read_b64_tr_b16 %7, %23 offset:%24\n"
+      "s_waitcnt lgkmcnt(8)"
+      : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3]), "=&v"(nxt.r[4]), "=&v"(nxt.r[5]),
+        "=&v"(nxt.r[6]), "=&v"(nxt.r[7]), "+v"(prev.r[0]), "+v"(prev.r[1]), "+v"(prev.r[2]), "+v"(prev.r[3]),
+        "+v"(prev.r[4]), "+v"(prev.r[5]), "+v"(prev.r[6]), "+v"(prev.r[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7]), "i"(G * 1024)
+      : "memory");
+}
+
+__device__ __forceinline__ void tr_wait_last(TrGroup& prev) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(prev.r[0]), "+v"(prev.r[1]), "+v"(prev.r[2]), "+v"(prev.r[3]), "+v"(prev.r[4]),
+                 "+v"(prev.r[5]), "+v"(prev.r[6]), "+v"(prev.r[7])
+               :
+               : "memory");
+}
+
+// QK^T operand reads in the same style: group g = k-steps 2g, 2g+1 of both
+// 16-row blocks (4 reads of 16 bytes), at base + g KB; three groups in
+// flight, each block issuing group g+2 and completing group g.
+struct QkGroup {
+  bf16x8 r[4];  // [2 mt + k-step parity]
+};
+
+template <int G>
+__device__ __forceinline__ void qk_issue_wait(QkGroup& nxt, QkGroup& done, const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%12\n"
+      "ds_read_b128 %1, %9 offset:%12\n"
+      "ds_read_b128 %2, %10 offset:%12\n"
+      "ds_read_b128 %3, %11 offset:%12\n"
+      "s_waitcnt lgkmcnt(8)"
+      : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3]), "+v"(done.r[0]), "+v"(done.r[1]),
+        "+v"(done.r[2]), "+v"(done.r[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024)
+      : "memory");
+}
+
+template <int G>
+__device__ __forceinline__ void qk_issue(QkGroup& nxt, const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n"
+      "ds_read_b128 %1, %5 offset:%8\n"
+      "ds_read_b128 %2, %6 offset:%8\n"
+      "ds_read_b128 %3, %7 offset:%8"
+      : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void qk_wait(QkGroup& done) {
+  asm volatile("s_waitcnt lgkmcnt(%4)"
+               : "+v"(done.r[0]), "+v"(done.r[1]), "+v"(done.r[2]), "+v"(done.r[3])
+               : "i"(N)
+               : "memory");
+}
+
+// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane groups
+// holding one head's rows) with the gfx950 lane-swap instructions: VALU
+// work, no LDS round trip.  permlane{16,32}_swap(x, x) returns, per lane,
+// x(l) and x(l ^ 16) (or x(l ^ 32)) in some order.
+__device__ __forceinline__ float group4_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float group4_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct MlaShared {
+  uint8_t rows[3][kTileBytes];  // tile buffers (read only through inline asm)
+  int32_t idx[kIdxCap + kIdxPad];
+  uint32_t vmask[(kIdxCap + kIdxPad) / kTile];  // bit r of word t: row r of tile t is a valid entry
+};
+
+// Opens a tile of the copy pipeline: this wave's copies of the tile have
+// landed (the 9 copies of the next tile may stay in flight) and its earlier
+// LDS accesses are done, then the workgroup barrier.  The barrier is issued
+// bare: __syncthreads() would also drain every copy still in flight, since
+// its release fence covers the copies' pending LDS writes.  All waves share
+// one LDS, so once every wave has passed its own waits, the tile is complete
+// for all of them.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// bf16 cache: wave w copies rows 8w .. 8w+7 of a tile with nine 1 KB DMA
+// instructions; pos is the position of this lane's row 8w + l/8 (< 0: row 0).
+__device__ __forceinline__ void tile_dma(uint8_t* dst, const MlaParams& p, int32_t pos, int64_t seq_row0, int wave,
+                                         int l) {
+  const int64_t row = seq_row0 + max(pos, 0);
+  const int cx = ((l & 7) ^ (l >> 3) ^ wave) & 7;  // chunk slot of this lane within each 8-chunk group
+  const uint8_t* src = (const uint8_t*)p.kv + row * (2 * kDqk) + cx * 16;
+  uint8_t* seg = dst + wave * 9 * 1024;
+#pragma unroll
+  for (int i = 0; i < 9; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(src + 128 * i),
+                                     (__attribute__((address_space(3))) void*)(seg + 1024 * i), 16, 0, 0);
+}
+
+// e4m3 cache: 32 rows x 36 chunks of 16 codes; thread k-th chunk id = tid + 256 k
+// (ids past the end repeat the last chunk, so loads and stores are unconditional).
+struct Fp8Stage {
+  static constexpr int kChunks = kTile * (kDqk / 16);
   static constexpr int kPerThread = (kChunks + kMlaThreads - 1) / kMlaThreads;
   i32x4 v[kPerThread];
   float sc[kPerThread];
 };
 
-// s_pos: resolved row positions of the current tile (-1: not a row).
-template <bool FP8>
-__device__ __forceinline__ void stage_load(Stage<FP8>& st, const MlaParams& p, const int32_t* s_pos,
-                                           int64_t seq_row0) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void fp8_load(Fp8Stage& st, const MlaParams& p, const int32_t* s_pos, int64_t seq_row0) {
 #pragma unroll
-  for (int k = 0; k < Stage<FP8>::kPerThread; ++k) {
-    const int id = tid + k * kMlaThreads;
-    if (id < Stage<FP8>::kChunks) {
-      const int r = id / Stage<FP8>::kChunksPerRow, c = id % Stage<FP8>::kChunksPerRow;
-      const int32_t pos = max(s_pos[r], 0);
-      const int64_t row = seq_row0 + pos;
-      st.v[k] = *((const i32x4*)((const uint8_t*)p.kv + row * (FP8 ? kDqk : 2 * kDqk)) + c);
-      if constexpr (FP8) st.sc[k] = p.kv_scale[row];
-    }
+  for (int k = 0; k < Fp8Stage::kPerThread; ++k) {
+    const int id = min((int)threadIdx.x + k * kMlaThreads, Fp8Stage::kChunks - 1);
+    const int r = id / (kDqk / 16), c = id % (kDqk / 16);
+    const int64_t row = seq_row0 + max(s_pos[r], 0);
+    st.v[k] = *((const i32x4*)((const uint8_t*)p.kv + row * kDqk) + c);
+    st.sc[k] = p.kv_scale[row];
   }
 }
 
-template <bool FP8>
-__device__ __forceinline__ void stage_store(const Stage<FP8>& st, uint16_t* lds) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void fp8_store(const Fp8Stage& st, uint8_t* dst) {
 #pragma unroll
-  for (int k = 0; k < Stage<FP8>::kPerThread; ++k) {
-    const int id = tid + k * kMlaThreads;
-    if (id >= Stage<FP8>::kChunks) break;
-    const int r = id / Stage<FP8>::kChunksPerRow, c = id % Stage<FP8>::kChunksPerRow;
-    if constexpr (!FP8) {
-      *(i32x4*)(lds + r * kRowStride + c * 8) = st.v[k];
-    } else {
-      // 16 e4m3 codes -> 16 bf16 (exact: code * 2^e fits bf16)
-      uint32_t w[8];
+  for (int k = 0; k < Fp8Stage::kPerThread; ++k) {
+    const int id = min((int)threadIdx.x + k * kMlaThreads, Fp8Stage::kChunks - 1);
+    const int r = id / (kDqk / 16), c = id % (kDqk / 16);
+    // 16 e4m3 codes -> 16 bf16 (exact: code * 2^e fits bf16) = bf16 chunks 2c, 2c+1
+    uint32_t w[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t word = (uint32_t)st.v[k][q];
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t word = (uint32_t)st.v[k][q];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const float a = e4m3_to_f32((word >> (16 * h2)) & 0xFFu) * st.sc[k];
-          const float bb = e4m3_to_f32((word >> (16 * h2 + 8)) & 0xFFu) * st.sc[k];
-          w[2 * q + h2] = (__float_as_uint(a) >> 16) | (__float_as_uint(bb) & 0xFFFF0000u);
-        }
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float a = e4m3_to_f32((word >> (16 * h2)) & 0xFFu) * st.sc[k];
+        const float bb = e4m3_to_f32((word >> (16 * h2 + 8)) & 0xFFu) * st.sc[k];
+        w[2 * q + h2] = (__float_as_uint(a) >> 16) | (__float_as_uint(bb) & 0xFFFF0000u);
       }
-      i32x4* dst = (i32x4*)(lds + r * kRowStride + c * 16);
-      dst[0] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      dst[1] = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
     }
+    *(i32x4*)(dst + chunk_off(r, 2 * c)) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    *(i32x4*)(dst + chunk_off(r, 2 * c + 1)) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
   }
 }
 
 template <bool FP8>
-__global__ __launch_bounds__(kMlaThreads) void mla_mfma_kernel(MlaParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_rows[kTile * kRowStride];
-  __shared__ float s_xch[kMlaWaves][8][kWave];  // partial logits exchanged between halves
-  __shared__ int32_t s_idx[kIdxCap];            // resolved positions of the split's rows
+__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_mfma_kernel(MlaParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
+  MlaShared& sh = *reinterpret_cast<MlaShared*>(mla_smem);
+  int32_t* s_idx = sh.idx;
+  // An accumulation-register operand makes the compiler select the MFMA
+  // forms that accumulate in AGPRs, so the 128 output accumulators live there
+  // and the arithmetic registers stay free for operands and addresses.
+  asm volatile("" ::"a"(0.0f));
 
   const int split = blockIdx.x, bt = blockIdx.y, hg = blockIdx.z;
   const int b = bt / p.T;
   const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
   const int lg = l >> 4, lc = l & 15;
-  const int half = wave & 1;
   const int len = clamp_len(p.seq_lens[b], p.Lmax);
-  const int h0 = hg * kHeadsPerWG + (wave >> 1) * kHeadsPerWave;  // this wave's first head
+  const int h0 = hg * kHeadsPerWG + wave * kHeadsPerWave;  // this wave's first head
   const int64_t seq_row0 = (int64_t)b * p.Lmax;
   const int32_t* sel = p.topk_idx + (int64_t)bt * p.K;
   const int j_begin = split * p.rows_per_split;
-  const int j_end = min(p.K, j_begin + p.rows_per_split);
+  const int n_rows = max(0, min(min(p.K, j_begin + p.rows_per_split) - j_begin, kIdxCap));
 
-  // query heads h0 + lc, dims 288 half + 32 ks + 8 lg .. +8  (operand B of QK^T)
-  bf16x8 qreg[kKStepsHalf];
+  // resolve the split's index list (the host sizes splits to <= kIdxCap rows)
+  for (int i = tid; i < n_rows; i += kMlaThreads) {
+    const int32_t v = sel[j_begin + i];
+    s_idx[i] = (v >= 0 && v < len) ? v : -1;
+  }
+  // pad the last tile plus the 3 tiles whose positions are read ahead
+  const int n_pad = ((n_rows + kTile - 1) / kTile + 3) * kTile;
+  for (int i = n_rows + tid; i < n_pad; i += kMlaThreads) s_idx[i] = -1;
+  __syncthreads();
+  for (int t = wave; t < n_pad / kTile; t += kMlaWaves) {
+    const uint64_t bal = __ballot(l < kTile && s_idx[t * kTile + (l & (kTile - 1))] >= 0);
+    if (l == 0) sh.vmask[t] = (uint32_t)bal;
+  }
+
+  // query heads h0 + lc, dims 32 ks + 8 lg .. +8  (operand B of QK^T)
+  bf16x8 qreg[kKSteps];
   {
-    const bf16x8* qrow =
-        (const bf16x8*)((const uint16_t*)p.q + ((int64_t)bt * p.H + h0 + lc) * kDqk + 288 * half);
+    const bf16x8* qrow = (const bf16x8*)((const uint16_t*)p.q + ((int64_t)bt * p.H + h0 + lc) * kDqk);
 #pragma unroll
-    for (int ks = 0; ks < kKStepsHalf; ++ks) qreg[ks] = qrow[ks * 4 + lg];
+    for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qrow[ks * 4 + lg];
   }
   const float zscale = p.scale * 1.4426950408889634f;  // logits in base-2 units
 
-  f32x4 o[kNTilesHalf];
+  // LDS byte offsets of this lane's operand reads within a tile
+  int a_off[2][2];  // QK^T operand A: [mt][ks parity], plus 1 KB per pair of k-steps
 #pragma unroll
-  for (int n = 0; n < kNTilesHalf; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) a_off[mt][par] = chunk_off(tile_row(mt, lc), 4 * par + lg);
+  int v_off[2][4];  // PV operand B: [row half][n % 4], plus 1 KB per 4 value tiles
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int n4 = 0; n4 < 4; ++n4)
+      v_off[t][n4] = chunk_off(tile_row(t, 4 * lg + (lc >> 2)), 2 * n4 + ((lc & 3) >> 1)) + 8 * (lc & 1);
+
+  f32x4 o[kNTiles];
+#pragma unroll
+  for (int n = 0; n < kNTiles; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;  // for head h0 + lc
 
-  Stage<FP8> stage;
-  for (int jc = j_begin; jc < j_end; jc += kIdxCap) {
-    const int jc_end = min(j_end, jc + kIdxCap);
-    __syncthreads();  // previous users of s_idx are done
-    for (int i = tid; i < jc_end - jc; i += kMlaThreads) {
-      const int32_t v = sel[jc + i];
-      s_idx[i] = (v >= 0 && v < len) ? v : -1;
+  auto compute = [&](const uint8_t* rows, int j0) {
+    const uint32_t vm = sh.vmask[j0 / kTile];  // read early: its latency hides behind QK^T
+    // ---- S^T[32 rows x 16 heads] over all 576 dims (two chains per half) ----
+    f32x4 s[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // pad the last tile
-    for (int i = jc_end - jc + tid; i < ((jc_end - jc + kTile - 1) / kTile) * kTile; i += kMlaThreads)
-      s_idx[i] = -1;
-    __syncthreads();
-    stage_load<FP8>(stage, p, s_idx, seq_row0);
-
-    for (int j0 = 0; j0 < jc_end - jc; j0 += kTile) {
-      __syncthreads();
-      stage_store<FP8>(stage, s_rows);
-      __syncthreads();
-      if (j0 + kTile < jc_end - jc) stage_load<FP8>(stage, p, s_idx + j0 + kTile, seq_row0);
-
-      // ---- partial S^T[32 rows x 16 heads] over this wave's 288 dims ----
-      f32x4 s[2];
+    uint32_t qaddr[4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* arow = s_rows + tile_row(mt, lc) * kRowStride + 288 * half + 8 * lg;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < kKStepsHalf; ++ks) {
-          const bf16x8 a = *(const bf16x8*)(arow + ks * 32);
-          s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s[mt], 0, 0, 0);
-        }
-      }
+      for (int par = 0; par < 2; ++par) qaddr[2 * mt + par] = (uint32_t)(uintptr_t)rows + a_off[mt][par];
+    QkGroup qg[3];
+    auto qk_group = [&](const QkGroup& cur, int g) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_xch[wave][mt * 4 + e][l] = s[mt][e];
-      __syncthreads();
+        for (int par = 0; par < 2; ++par)
+          s[mt][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.r[2 * mt + par], qreg[2 * g + par], s[mt][par], 0,
+                                                               0, 0);
+    };
+    static_assert(kKSteps == 18, "nine groups of two k-steps");
+    qk_issue<0>(qg[0], qaddr);
+    qk_issue<1>(qg[1], qaddr);
+    qk_issue_wait<2>(qg[2], qg[0], qaddr);
+    qk_group(qg[0], 0);
+    qk_issue_wait<3>(qg[0], qg[1], qaddr);
+    qk_group(qg[1], 1);
+    qk_issue_wait<4>(qg[1], qg[2], qaddr);
+    qk_group(qg[2], 2);
+    qk_issue_wait<5>(qg[2], qg[0], qaddr);
+    qk_group(qg[0], 3);
+    qk_issue_wait<6>(qg[0], qg[1], qaddr);
+    qk_group(qg[1], 4);
+    qk_issue_wait<7>(qg[1], qg[2], qaddr);
+    qk_group(qg[2], 5);
+    qk_issue_wait<8>(qg[2], qg[0], qaddr);
+    qk_group(qg[0], 6);
+    qk_wait<4>(qg[1]);
+    qk_group(qg[1], 7);
+    qk_wait<0>(qg[2]);
+    qk_group(qg[2], 8);
+    // ---- online softmax for head h0 + lc over rows 4 lg + e (+16) ----
+    float z[2][4];
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[mt][e] += s_xch[wave ^ 1][mt * 4 + e][l];
-
-      // ---- online softmax for head h0 + lc over rows 4 lg + e (+16) ----
-      float z[2][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool valid = s_idx[j0 + tile_row(mt, 4 * lg + e)] >= 0;
-          z[mt][e] = valid ? s[mt][e] * zscale : -INFINITY;
-          tmax = fmaxf(tmax, z[mt][e]);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha = 1.0f, psum = 0.0f;
-      float pr[2][4];
-      if (m_new == -INFINITY) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pr[mt][e] = 0.0f;
-      } else {
-        alpha = exp2f(m_run - m_new);  // m_run = -inf gives 0
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pr[mt][e] = exp2f(z[mt][e] - m_new);
-            psum += pr[mt][e];
-          }
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = (vm >> tile_row(mt, 4 * lg + e)) & 1u;
+        z[mt][e] = valid ? (s[mt][0][e] + s[mt][1][e]) * zscale : -INFINITY;
+        tmax = fmaxf(tmax, z[mt][e]);
       }
-      psum += __shfl_xor(psum, 16, kWave);
-      psum += __shfl_xor(psum, 32, kWave);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-
-      // rescale O rows (heads h0 + 4 lg + e) by their head's alpha
-      float al[4];
+    tmax = group4_max(tmax);
+    // Lazy rescaling: the reference max m_run only moves when the tile's
+    // max exceeds it by more than kSlack (probabilities then stay <= 2^kSlack,
+    // exact enough in bf16 and fp32), or when it is still -inf (O and l are
+    // zero then, so nothing needs rescaling).  Moving it costs a pass over the
+    // 128 accumulators; with a stable max that pass is skipped for the wave.
+    const bool move = tmax > m_run + kSlack;
+    const float m_new = move ? tmax : m_run;
+    const float alpha = move ? exp2f(m_run - m_new) : 1.0f;  // m_run = -inf gives 0
+    float psum = 0.0f;
+    float pr[2][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * lg + e, kWave);
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int n = 0; n < kNTilesHalf; ++n)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[n][e] *= al[e];
-
-      // P operand (A of PV): head lc, k-slot 8 lg + j <-> row (j < 4 ? 4 lg + j : 16 + 4 lg + j - 4)
-      bf16x8 pa;
-      {
-        uint16_t pb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[j >> 2][j & 3]);
-        pa = __builtin_bit_cast(bf16x8, pb);
+      for (int e = 0; e < 4; ++e) {
+        pr[mt][e] = z[mt][e] > -INFINITY ? exp2f(z[mt][e] - m_new) : 0.0f;  // m_new >= z when z is finite
+        psum += pr[mt][e];
       }
-      // ---- O[16 heads x 256 value columns] += P V ----
-      // k-slot 8 lg + k (k < 4) is LDS row tile_row(0, 4 lg + k), slot 8 lg + 4 + k
-      // is tile_row(1, 4 lg + k): lane lc addresses row k = lc/4 of its group and
-      // columns 4 (lc%4) .. +4 of the 16-column tile.
-      const uint16_t* va = s_rows + tile_row(0, 4 * lg + (lc >> 2)) * kRowStride + 256 * half + 4 * (lc & 3);
-      const uint16_t* vb = s_rows + tile_row(1, 4 * lg + (lc >> 2)) * kRowStride + 256 * half + 4 * (lc & 3);
+    psum = group4_sum(psum);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // rescale this lane's outputs (all of head h0 + lc) by alpha, only when
+    // some head of the wave moved its max past a nonzero O
+    if (__any(move && alpha != 0.0f)) {
 #pragma unroll
-      for (int n = 0; n < kNTilesHalf; ++n) {
-        const i16x4 lo = lds_read_tr16(va + n * 16);
-        const i16x4 hi = lds_read_tr16(vb + n * 16);
+      for (int n = 0; n < kNTiles; ++n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[n][e] *= alpha;
+    }
+
+    // P^T operand (B of O^T = V^T P^T): head lc, k-slot 8 lg + j <-> row
+    // (j < 4 ? 4 lg + j : 16 + 4 lg + j - 4) of the tile's MFMA row order
+    bf16x8 pa;
+    {
+      uint16_t pb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[j >> 2][j & 3]);
+      pa = __builtin_bit_cast(bf16x8, pb);
+    }
+    // ---- O^T[512 value columns x 16 heads] += V^T P^T ----
+    // The accumulator is O transposed, so lane l holds 4 consecutive columns
+    // 16 n + 4 (l/16) .. +4 of head lc: rescaling and normalising need no
+    // lane exchange and the write-out is one vector store per value tile.
+    // V^T operand (A): k-slot 8 lg + k (k < 4) is tile row tile_row(0, 4 lg + k),
+    // slot 8 lg + 4 + k is tile_row(1, 4 lg + k): lane lc addresses row k = lc/4
+    // of its group and columns 4 (lc%4) .. +4 of the 16-column tile.
+    uint32_t taddr[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      taddr[2 * k] = (uint32_t)(uintptr_t)rows + v_off[0][k];
+      taddr[2 * k + 1] = (uint32_t)(uintptr_t)rows + v_off[1][k];
+    }
+    TrGroup grp[2];
+    auto pv_group = [&](const TrGroup& cur, int g) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const i16x4 lo = cur.r[2 * k], hi = cur.r[2 * k + 1];
         const bf16x8 vop = __builtin_bit_cast(bf16x8, (i32x4){__builtin_bit_cast(int, (short2){lo[0], lo[1]}),
                                                                __builtin_bit_cast(int, (short2){lo[2], lo[3]}),
                                                                __builtin_bit_cast(int, (short2){hi[0], hi[1]}),
                                                                __builtin_bit_cast(int, (short2){hi[2], hi[3]})});
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vop, o[n], 0, 0, 0);
+        o[4 * g + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pa, o[4 * g + k], 0, 0, 0);
       }
+    };
+    tr_issue_wait<0>(grp[0], grp[1], taddr);  // grp[1] is a dummy here
+    tr_issue_wait<1>(grp[1], grp[0], taddr);
+    pv_group(grp[0], 0);
+    tr_issue_wait<2>(grp[0], grp[1], taddr);
+    pv_group(grp[1], 1);
+    tr_issue_wait<3>(grp[1], grp[0], taddr);
+    pv_group(grp[0], 2);
+    tr_issue_wait<4>(grp[0], grp[1], taddr);
+    pv_group(grp[1], 3);
+    tr_issue_wait<5>(grp[1], grp[0], taddr);
+    pv_group(grp[0], 4);
+    tr_issue_wait<6>(grp[0], grp[1], taddr);
+    pv_group(grp[1], 5);
+    tr_issue_wait<7>(grp[1], grp[0], taddr);
+    pv_group(grp[0], 6);
+    tr_wait_last(grp[1]);
+    pv_group(grp[1], 7);
+  };
+
+  __syncthreads();  // s_idx complete
+  // One compact loop over the tiles: the loop body stays in the instruction
+  // cache, where a fully unrolled schedule would be fetched cold for every
+  // tile.  Tile t sits in buffer t % 3.
+  const int n_tiles = (n_rows + kTile - 1) / kTile;
+  if constexpr (!FP8) {
+    // Step t: wait for this wave's copy of tile t (the copies of tile t+1 may
+    // stay in flight), barrier (tile t complete; every wave is done with tile
+    // t-1, whose buffer is reused), start copying tile t+2, compute tile t.
+    // The row this lane copies for tile t is entry 32 t + 8 wave + l/8; it is
+    // read one tile ahead, so the copy is issued without an LDS round trip.
+    // Copies of padding tiles past the end read row 0 and are never computed.
+    const int my_row = 8 * wave + (l >> 3);
+    tile_dma(sh.rows[0], p, s_idx[my_row], seq_row0, wave, l);
+    tile_dma(sh.rows[1], p, s_idx[kTile + my_row], seq_row0, wave, l);
+    int32_t pos = s_idx[2 * kTile + my_row];
+    int cur = 0, nxt = 2;  // buffers of tiles t and t+2
+    for (int t = 0; t < n_tiles; ++t) {
+      tile_barrier();
+      tile_dma(sh.rows[nxt], p, pos, seq_row0, wave, l);
+      pos = s_idx[(t + 3) * kTile + my_row];
+      compute(sh.rows[cur], t * kTile);
+      cur = cur == 2 ? 0 : cur + 1;
+      nxt = nxt == 2 ? 0 : nxt + 1;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // copies of padding tiles land before exit
+  } else {
+    // Tile t+1 waits in registers while tile t is computed; step t stores it
+    // (decoded) into buffer (t+1) % 3 and loads tile t+2.
+    Fp8Stage st;
+    fp8_load(st, p, s_idx, seq_row0);
+    fp8_store(st, sh.rows[0]);
+    fp8_load(st, p, s_idx + kTile, seq_row0);
+    int cur = 0, nxt = 1;  // buffers of tiles t and t+1
+    for (int t = 0; t < n_tiles; ++t) {
+      __syncthreads();
+      fp8_store(st, sh.rows[nxt]);
+      fp8_load(st, p, s_idx + (t + 2) * kTile, seq_row0);
+      compute(sh.rows[cur], t * kTile);
+      cur = cur == 2 ? 0 : cur + 1;
+      nxt = nxt == 2 ? 0 : nxt + 1;
     }
   }
 
-  // ---- write-out: O rows are heads h0 + 4 lg + e, columns 256 half + 16 n + lc ----
-  float lh[4], mh[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    lh[e] = __shfl(l_run, 4 * lg + e, kWave);
-    mh[e] = __shfl(m_run, 4 * lg + e, kWave);
-  }
-  const int col0 = 256 * half + lc;
+  // ---- write-out: lane l holds head h0 + lc, columns 16 n + 4 lg .. +4 ----
+  const int h = h0 + lc;
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   if (p.splits == 1) {
+    const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + 4 * lg;
+    if (p.out_dtype == kF32) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = h0 + 4 * lg + e;
-      const float inv = lh[e] > 0.0f ? 1.0f / lh[e] : 0.0f;
-      const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + col0;
+      for (int n = 0; n < kNTiles; ++n)
+        *(f32x4*)((float*)p.out + ooff + 16 * n) = f32x4{o[n][0] * inv, o[n][1] * inv, o[n][2] * inv, o[n][3] * inv};
+    } else {
 #pragma unroll
-      for (int n = 0; n < kNTilesHalf; ++n) store_out(p.out, p.out_dtype, ooff + n * 16, o[n][e] * inv);
-      if (p.lse && lc == 0 && half == 0)
-        p.lse[(int64_t)bt * p.H + h] = lh[e] > 0.0f ? (mh[e] + log2f(lh[e])) * 0.6931471805599453f : -INFINITY;
+      for (int n = 0; n < kNTiles; ++n)
+        *(i32x2*)((uint16_t*)p.out + ooff + 16 * n) =
+            i32x2{(int)(f32_to_bf16_bits(o[n][0] * inv) | (f32_to_bf16_bits(o[n][1] * inv) << 16)),
+                  (int)(f32_to_bf16_bits(o[n][2] * inv) | (f32_to_bf16_bits(o[n][3] * inv) << 16))};
     }
+    if (p.lse && lg == 0)
+      p.lse[(int64_t)bt * p.H + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
   } else {
-    const int64_t BT = (int64_t)p.B * p.T;
+    const int64_t slot = ((int64_t)split * p.B * p.T + bt) * p.H + h;
+    uint16_t* po = p.part_o + slot * kDv + 4 * lg;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = h0 + 4 * lg + e;
-      const int64_t slot = ((int64_t)split * BT + bt) * p.H + h;
-      float* po = p.part_o + slot * kDv + col0;
-#pragma unroll
-      for (int n = 0; n < kNTilesHalf; ++n) po[n * 16] = o[n][e];
-      if (lc == 0 && half == 0) {
-        p.part_ml[slot * 2] = mh[e];
-        p.part_ml[slot * 2 + 1] = lh[e];
-      }
+    for (int n = 0; n < kNTiles; ++n)
+      *(i32x2*)(po + 16 * n) =
+          i32x2{(int)(f32_to_bf16_bits(o[n][0] * inv) | (f32_to_bf16_bits(o[n][1] * inv) << 16)),
+                (int)(f32_to_bf16_bits(o[n][2] * inv) | (f32_to_bf16_bits(o[n][3] * inv) << 16))};
+    if (lg == 0) {
+      p.part_ml[slot * 2] = m_run;
+      p.part_ml[slot * 2 + 1] = l_run;
     }
   }
 }
 
-// Merge the per-split partials (O, max, sum) of one (query, head): 128
-// threads, 4 consecutive value columns each.
-__global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
-  __shared__ float s_w[64];
-  __shared__ float s_stat[2];
+// Merge the per-split partials of one (query, head): split s holds its
+// output normalised by its own sum l_s and its running max m_s (base 2), so
+//   out = sum_s w_s O_s / sum_s w_s,   w_s = l_s 2^(m_s - M),  M = max_s m_s.
+// 64 threads, 8 consecutive value columns (16 bytes of bf16 partials) each;
+// the partials of up to 16 splits are loaded before any is used, so their
+// latencies overlap.
+constexpr int kCombineBatch = 16;
+
+__global__ __launch_bounds__(64) void mla_combine_kernel(MlaParams p) {
+  __shared__ float s_w[kWave];
   const int h = blockIdx.x, bt = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t BT = (int64_t)p.B * p.T;
   const int64_t slot0 = (int64_t)bt * p.H + h;
   const int64_t slot_stride = BT * p.H;
-  if (tid < kWave) {
-    float ms = -INFINITY, ls = 0.0f;
-    if (tid < p.splits) {
-      ms = p.part_ml[(slot0 + tid * slot_stride) * 2];
-      ls = p.part_ml[(slot0 + tid * slot_stride) * 2 + 1];
-    }
-    const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
-    const float wgt = (ls > 0.0f) ? exp2f(ms - M) : 0.0f;
-    const float L = wave_sum(ls * wgt);
-    if (tid < 64) s_w[tid] = wgt;
-    if (tid == 0) {
-      s_stat[0] = M;
-      s_stat[1] = L;
-    }
+  float ms = -INFINITY, ls = 0.0f;
+  if (tid < p.splits) {
+    ms = p.part_ml[(slot0 + tid * slot_stride) * 2];
+    ls = p.part_ml[(slot0 + tid * slot_stride) * 2 + 1];
   }
-  __syncthreads();
-  const float M = s_stat[0], L = s_stat[1];
+  const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
+  const float wgt = (ls > 0.0f) ? ls * exp2f(ms - M) : 0.0f;
+  const float L = wave_sum(wgt);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const int d = tid * 4;
+  s_w[tid] = wgt * inv;
+  __syncthreads();
+  const int d = tid * 8;
   if (d < p.Dv) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* po = p.part_o + slot0 * p.Dv + d;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    const uint16_t* po = p.part_o + slot0 * p.Dv + d;
     const int64_t stride = slot_stride * p.Dv;
-#pragma unroll 4
-    for (int s = 0; s < p.splits; ++s) {
-      const float wgt = s_w[s];
-      const f32x4 v = *(const f32x4*)(po + s * stride);
-      acc[0] = fmaf(v[0], wgt, acc[0]);
-      acc[1] = fmaf(v[1], wgt, acc[1]);
-      acc[2] = fmaf(v[2], wgt, acc[2]);
-      acc[3] = fmaf(v[3], wgt, acc[3]);
+    for (int s0 = 0; s0 < p.splits; s0 += kCombineBatch) {
+      i32x4 v[kCombineBatch];
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j)  // splits past the end reread split s0 (weight 0)
+        v[j] = *(const i32x4*)(po + (s0 + j < p.splits ? s0 + j : s0) * stride);
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j) {
+        const float w = s0 + j < p.splits ? s_w[s0 + j] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = fmaf(bf16_bits_to_f32((uint32_t)v[j][k] & 0xFFFFu), w, acc[2 * k]);
+          acc[2 * k + 1] = fmaf(bf16_bits_to_f32((uint32_t)v[j][k] >> 16), w, acc[2 * k + 1]);
+        }
+      }
     }
     const int64_t ooff = slot0 * p.Dv + d;
+    if (p.out_dtype == kF32) {
+      *(f32x4*)((float*)p.out + ooff) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)((float*)p.out + ooff + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    } else {
+      i32x4 ob;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) store_out(p.out, p.out_dtype, ooff + k, acc[k] * inv);
+      for (int k = 0; k < 4; ++k)
+        ob[k] = (int)(f32_to_bf16_bits(acc[2 * k]) | (f32_to_bf16_bits(acc[2 * k + 1]) << 16));
+      *(i32x4*)((uint16_t*)p.out + ooff) = ob;
+    }
   }
-  if (p.lse && tid == 0)
-    p.lse[slot0] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  if (p.lse && tid == 0) p.lse[slot0] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
 bool mla_mfma_supported(const MlaParams& p) {
@@ -459,13 +700,22 @@ bool mla_mfma_supported(const MlaParams& p) {
 hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream) {
   if (allow_mfma && mla_mfma_supported(p)) {
     dim3 grid((unsigned)p.splits, (unsigned)(p.B * p.T), (unsigned)(p.H / kHeadsPerWG));
-    if (p.kv_dtype == kBF16)
-      hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kMlaThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL(mla_mfma_kernel<true>, grid, dim3(kMlaThreads), 0, stream, p);
-    hipError_t e = hipGetLastError();
+    const size_t lds = sizeof(MlaShared);
+    hipError_t e;
+    if (p.kv_dtype == kBF16) {
+      e = hipFuncSetAttribute((const void*)mla_mfma_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kMlaThreads), lds, stream, p);
+    } else {
+      e = hipFuncSetAttribute((const void*)mla_mfma_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(mla_mfma_kernel<true>, grid, dim3(kMlaThreads), lds, stream, p);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)p.H, (unsigned)(p.B * p.T)), dim3(128), 0,
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)p.H, (unsigned)(p.B * p.T)), dim3(kWave), 0,
                        stream, p);  // needs Dv <= 512 and splits <= 64
     return hipGetLastError();
   }

@@ -22,6 +22,10 @@
 //      order, the first K - #{key > tau} keys equal to tau.
 // select_row_kernel does all of it in one 1024-thread workgroup per query
 // (used for many short queries, where it saves two launches).
+// The counters (histograms, threshold-bin count) are zero on entry and are
+// cleared again by their last reader: in the emit step the query's last
+// chunk to finish (an arrival ticket taken after its own reads completed),
+// in row mode the query's workgroup.  The workspace is left as it was found.
 #include <stdlib.h>
 #include <string.h>
 
@@ -163,6 +167,21 @@ __device__ __forceinline__ void write_all_visible(int32_t* out, int64_t c_lo, in
   }
 }
 
+// Clears the query's counters (histograms, threshold-bin count, arrivals):
+// run by the last workgroup that reads them.
+__device__ __forceinline__ void clear_query_counters(const TopkParams& p, int bt, int nthreads) {
+  uint32_t* h = p.hist + (int64_t)bt * kHistBins;
+  uint32_t* g = p.sub_hist + (int64_t)bt * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += nthreads) {
+    h[i] = 0;
+    g[i] = 0;
+  }
+  if (threadIdx.x == 0) {
+    p.bin_count[bt] = 0;
+    p.done[bt] = 0;
+  }
+}
+
 // Step 2: candidates of one chunk + second-level histogram of the threshold bin.
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(TopkParams p) {
   __shared__ uint32_t s_wave[kSelWaves];
@@ -178,8 +197,9 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(TopkParams p)
   int32_t* out = p.topk_idx + (int64_t)bt * K;
   const int64_t c_lo = (int64_t)c * p.chunk;
   const int64_t c_hi = min(c_lo + p.chunk, vis);
-  if (vis <= K) {  // every visible position is selected
+  if (vis <= K) {  // every visible position is selected; nobody reads the counters
     write_all_visible(out, c_lo, c_hi, vis, K, c, p.topk_count ? p.topk_count + bt : nullptr);
+    if (c == 0) clear_query_counters(p, bt, kSelThreads);
     return;
   }
   if (c_lo >= c_hi) return;  // beyond this query's visible range
@@ -372,6 +392,18 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) 
     ties_seen += q_tot;
   }
   if (c == 0 && tid == 0 && p.topk_count) p.topk_count[bt] = K;
+
+  // Arrival ticket, taken once every read of the query's counters by this
+  // workgroup has completed (the fence waits for them): the last chunk of
+  // the query clears them.  Nothing is published, so no cache write-back.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t n_act = (uint32_t)((vis + p.chunk - 1) / p.chunk);
+    sh.res[0] = atomicAdd(&p.done[bt], 1u) + 1u == n_act ? 1u : 0u;
+  }
+  __syncthreads();
+  if (sh.res[0]) clear_query_counters(p, bt, kSelThreads);
 }
 
 // --------------------------------------------------------------------------
@@ -462,12 +494,15 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   if (vis <= K) {  // every visible position is selected
     for (int64_t s = tid; s < K; s += kRowThreads) out[s] = s < vis ? (int32_t)s : -1;
     if (tid == 0 && p.topk_count) p.topk_count[bt] = (int32_t)vis;
+    clear_query_counters(p, bt, kRowThreads);
     return;
   }
 
-  // 1. threshold bin from the complete histogram
+  // 1. threshold bin from the complete histogram (then the counters are
+  // cleared: this workgroup is their only reader)
   uint32_t bin, above;
   row_threshold_bin<kHistBins>(p.hist + (int64_t)bt * kHistBins, (uint32_t)K, sh.wave, sh.res, &bin, &above);
+  clear_query_counters(p, bt, kRowThreads);
 
   // 2. one pass over the scores: candidates in position order into LDS
   const float* row = p.scores + (int64_t)bt * p.Lmax;

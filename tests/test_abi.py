@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = dsa.load_library()
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     assert lib.dsa_status_string(0) == b"DSA_OK"
     assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
 
@@ -130,6 +130,21 @@ def test_workspace_sizes_monotone_in_problem_size():
     # Top-K needs at least the score-key histograms and one candidate slot per position
     p = good_problem()
     assert lib.dsa_topk_workspace_size(ctypes.byref(p)) >= 2 * 1 * (4096 * 4 + 4096 * 4)
+
+
+def test_workspace_counter_region_and_init_validation():
+    lib = dsa.load_library()
+    p = good_problem(batch=3, q_len=2)
+    z = lib.dsa_workspace_zero_bytes(ctypes.byref(p))
+    # two 4096-bin histograms plus two counters per query, at the start of the workspace
+    assert z == 3 * 2 * (2 * 4096 * 4 + 2 * 4)
+    assert z < lib.dsa_topk_workspace_size(ctypes.byref(p)) <= lib.dsa_forward_workspace_size(ctypes.byref(p))
+    assert lib.dsa_workspace_zero_bytes(None) == 0
+    # argument checks happen before any HIP call
+    assert lib.dsa_workspace_init(None, 64, None) == 1 and b"ws" in lib.dsa_last_error()
+    assert lib.dsa_workspace_init(FAKE, 6, None) == 1 and b"multiple of 4" in lib.dsa_last_error()
+    assert lib.dsa_workspace_init(FAKE + 2, 64, None) == 1
+    assert lib.dsa_workspace_init(None, 0, None) == 0  # nothing to do
 
 
 def test_stage_events_must_be_non_null():

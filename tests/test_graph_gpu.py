@@ -23,7 +23,7 @@ def test_graph_replays_match_eager(name, kw):
     out_dtype = G.out_torch_dtype(w)
     prob = dsa.forward_problem(d["q_idx"], d["k_idx"], d["q"], d["kv"], d["seq_lens"], w.top_k, w.v_dim,
                                w.softmax_scale, out_dtype)
-    ws = torch.empty(dsa.forward_workspace_size(prob), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(dsa.forward_workspace_size(prob), dtype=torch.uint8, device="cuda")
     B, T, H = w.batch, w.q_len, w.heads
     outs = {"out": torch.empty((B, T, H, w.v_dim), dtype=out_dtype, device="cuda"),
             "lse": torch.empty((B, T, H), dtype=torch.float32, device="cuda"),

@@ -176,3 +176,34 @@ def test_invisible_positions_never_selected_causal():
         sel = got["topk_idx"][0, t]
         assert got["topk_count"][0, t] == vis
         assert np.array_equal(sel[:vis], np.arange(vis)) and np.all(sel[vis:] == -1)
+
+
+@pytest.mark.parametrize("mode", ["row", "chunk"])
+def test_workspace_reused_and_counters_left_zero(mode):
+    # one workspace serves three different problems of the same shape; the
+    # counters at its start must be zero after every call (the library clears
+    # them as it goes), and every result must still match the oracle
+    os.environ["DSA_TOPK_MODE"] = mode
+    try:
+        ws = None
+        for i, lens in enumerate([(15000, 20000), (9000, 20000), (20000, 20000)]):
+            w = _case("decode128k", batch=3, max_seq_len=20000, len_range=lens, top_k=2048)
+            w.q_idx[...] = np.roll(w.q_idx, i, axis=-1)  # different scores per round
+            if i == 1:
+                w.seq_lens[:] = [1500, 0, 20000]  # fewer visible than K, and an empty sequence
+            d = G.to_device(w)
+            prob = dsa.forward_problem(d["q_idx"], d["k_idx"], d["q"], d["kv"], d["seq_lens"], w.top_k, w.v_dim,
+                                       w.softmax_scale, torch.bfloat16)
+            if ws is None:
+                ws = torch.empty(dsa.forward_workspace_size(prob), dtype=torch.uint8, device="cuda")
+                dsa.workspace_init(ws)
+            r = dsa.dsa_forward(d["q_idx"], d["head_w"], d["k_idx"], d["q"], d["kv"], d["seq_lens"], w.top_k,
+                                w.v_dim, w.softmax_scale, workspace=ws)
+            torch.cuda.synchronize()
+            nz = dsa.workspace_zero_bytes(prob)
+            assert nz > 0 and int(torch.count_nonzero(ws[:nz])) == 0, "counters not cleared"
+            ref = oracle.forward(w)
+            G.check_topk(w, r["topk_idx"].cpu().numpy(), r["topk_count"].cpu().numpy(), ref["idx"], ref["count"])
+            G.check_attention(w, r["out"].float().cpu().numpy(), r["lse"].cpu().numpy(), ref["out"], ref["lse"])
+    finally:
+        del os.environ["DSA_TOPK_MODE"]
