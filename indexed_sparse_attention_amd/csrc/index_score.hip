@@ -57,9 +57,10 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
 // positions [0, vis_end) with vis_end = vis of the group's last token, cut
 // into units of 64 positions (a "segment").  Each segment gets a contiguous
 // run of workgroups in proportion to its units (at least one), and the waves
-// of that run take its units round-robin, so all of them sweep the segment's
-// key rows together through a window of a few MB: neighbouring waves read
-// neighbouring 16 KB blocks, which keeps HBM pages and channels evenly busy.
+// of that run take its 16-position sub-tiles round-robin, so all of them
+// sweep the segment's key rows together through one contiguous window:
+// neighbouring waves read neighbouring 4 KB tiles, which keeps HBM pages and
+// channels evenly busy.  A wave's unit is 4 of its sub-tiles.
 //
 // Per wave and sub-tile of 16 positions, the MFMA computes D[16 heads x 16
 // positions] for each of the 4 head tiles: operand A is the index query (kept
@@ -67,7 +68,8 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
 // from HBM, 16 bytes per lane.  In the 16x16 accumulator layout lane l holds
 // position l%16 and heads 4*(l/16) + e, e < 4, so ReLU, weight and a partial
 // head sum happen in-lane; after 4 sub-tiles a 3-shuffle reduce-scatter across
-// the 4 lane groups leaves lane l with the full score of position 64u + l.
+// the 4 lane groups leaves lane l with the full score of column l%16 of the
+// unit's sub-tile l/16.
 //
 // Operand k-ordering: MFMA A and B share one (lane group, element) -> k
 // assignment, so any fixed permutation of the 128 dims gives the same dot
@@ -264,16 +266,19 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
         }
       }
 
-      const int64_t my_first = iw;
-      const int n_units = iw < seg_n ? (int)((seg_n - iw + n_w - 1) / n_w) : 0;
+      // The segment's 16-position sub-tiles go round-robin over its n_w
+      // waves (sub-tile iw + x n_w is this wave's x-th), so at any moment the
+      // waves read one contiguous window of consecutive 4 KB (bf16) tiles.
+      // A unit is 4 of a wave's sub-tiles: x = 4u .. 4u+3.
+      const int64_t n_sub = iw < 4 * seg_n ? (4 * seg_n - iw + n_w - 1) / n_w : 0;
+      const int n_units = (int)((n_sub + 3) / 4);
       constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
       const uint8_t* kseq = (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes;
       const int last_row = len - 1;
-      // first position this lane loads: unit my_first, sub-tile 0, column lc
-      const int64_t pos_base = my_first * 64 + lc;
+      auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
 
       auto st_ptr = [&](int x) -> const void* {  // key row this lane loads for sub-tile x
-        int64_t pos = pos_base + n_w * 64 * (x >> 2) + 16 * (x & 3);
+        int64_t pos = sub_pos(x) + lc;
         if (pos > last_row) pos = last_row;
         return kseq + pos * kRowBytes;
       };
@@ -297,7 +302,8 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
           const bool live = u0 + ub < n_units;
           // this unit's position for lane l, and (e4m3 keys) its row scale, loaded
           // before the ring refills so waiting for it does not drain them
-          const int64_t pos = (my_first + n_w * (u0 + ub)) * 64 + l;
+          // after the reduce-scatter lane l holds position lc of its sub-tile 4u + lg
+          const int64_t pos = sub_pos(4 * (u0 + ub) + lg) + lc;
           float kscale = 1.0f;
           if constexpr (FP8) kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
           float part[TQ][4];
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
             load_key_tile<FP8>(slot[j], st_ptr(x + NSLOT), lg);
           }
           if (live) {
-            // reduce-scatter over the 4 lane groups: lane l gets position 64u + l
+            // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
 #pragma unroll
             for (int tq = 0; tq < TQ; ++tq) {
               const float r0 = (upper ? part[tq][2] : part[tq][0]) +
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
         // store the batch
 #pragma unroll
         for (int ub = 0; ub < RB; ++ub) {
-          const int64_t pos = (my_first + n_w * (u0 + ub)) * 64 + l;
+          const int64_t pos = sub_pos(4 * (u0 + ub) + lg) + lc;
           if (u0 + ub < n_units && pos < vis_last) {
 #pragma unroll
             for (int tq = 0; tq < TQ; ++tq)
