@@ -135,7 +135,7 @@ bool mla_uses_mfma(const dsa_problem* p) {
 MlaLayout mla_layout(const dsa_problem* p) {
   MlaLayout L;
   const int64_t BT = (int64_t)p->batch * p->q_len;
-  const int tile = 32;
+  const int tile = dsa::mla_row_tile();
   L.splits = 1;
   L.rows_per_split = (int)align_up(p->top_k, tile);
   if (mla_uses_mfma(p)) {

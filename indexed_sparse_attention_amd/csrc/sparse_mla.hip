@@ -114,50 +114,55 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
 
 // ---------------------------------------------------------------------------
 // Matrix-core kernel: qk_dim 576, v_dim 512, 64 heads per workgroup, row tiles
-// of 32 selected rows staged in LDS once and read by every wave.
+// of 64 selected rows staged in LDS once and read by every wave.
 //
 // Four waves, one per SIMD; wave w owns heads 16w .. 16w+15 of the group
 // completely: all 576 dims of the QK^T contraction and all 512 value columns
 // of PV, so no partial logits cross waves and the only barrier per tile is
 // the one that hands over an LDS tile buffer.  With one wave per SIMD the
 // wave may hold up to 512 registers: 72 for its queries and 128 accumulators.
+// Tiles of 64 rows amortise each tile's fixed costs (barrier, copy issue,
+// softmax reductions) over more rows and give 8 independent accumulation
+// chains for QK^T.
 //
-// Row tiles rotate through three LDS buffers: while tile t is computed, tiles
-// t+1 and t+2 are in flight.  A bf16 cache is copied global -> LDS directly
-// (global_load_lds_dwordx4, no registers); an e4m3 cache goes through
-// registers one tile ahead and is decoded to bf16 (x its row scale) on the
-// way in.  A tile is 32 rows x 72 chunks of 16 bytes, stored in 1 KB segments
-// of 8 rows x 8 chunks with the chunk slot XOR-swizzled by row, so that one
-// DMA instruction fills one segment with eight 128-byte row pieces and both
+// Row tiles alternate between two LDS buffers: while tile t is computed, tile
+// t+1 is in flight.  A bf16 cache is copied global -> LDS directly
+// (global_load_lds_dwordx4, no registers); an e4m3 cache is copied the
+// same way as raw codes, each wave then decodes its own rows to bf16 (x the
+// row scale) in place.  A tile
+// is 64 rows x 72 chunks of 16 bytes, stored in 1 KB segments of 8 rows x 8
+// chunks with the chunk slot XOR-swizzled by row, so that one DMA
+// instruction fills one segment with eight 128-byte row pieces and both
 // operand reads below are free of bank conflicts.
 //
 // QK^T is computed transposed, S^T[row, head], with the LDS row tile as MFMA
 // operand A and 16 query heads (registers) as operand B; in the 16x16
-// accumulator lane l holds head l%16 and rows 4*(l/16)+e of each 16-row half.
-// Those 8 probabilities are exactly the A operand the PV product needs for
-// head l%16 (the PV k-slots are a fixed permutation of the tile's rows; the V
-// operand is read from LDS in the same order), so P never leaves registers.
-// The V operand needs 8 rows at one column per lane; gfx950's LDS transpose
-// read (ds_read_b64_tr_b16) delivers that: within each 16-lane group, output
-// lane j receives element j%4 of the 4-element segments addressed by lanes
-// j/4 + 4k, k < 4.  MFMA lane i of 16-row block mt uses tile row
-// perm(mt, i) = 16 mt + 2 (i%4) + (i/4)%2 + 8 (i/8).  Online softmax in base 2
-// with a lazily moved reference max.  Row splits of the index list run in
-// separate workgroups and are merged by mla_combine_kernel from their
+// accumulator lane l holds head l%16 and rows 4*(l/16)+e of each 16-row
+// block.  Those probabilities are exactly the operand the PV product needs
+// for head l%16 (the PV k-slots are a fixed permutation of the tile's rows;
+// the V operand is read from LDS in the same order), so P never leaves
+// registers.  The V operand needs 8 rows at one column per lane; gfx950's LDS
+// transpose read (ds_read_b64_tr_b16) delivers that: within each 16-lane
+// group, output lane j receives element j%4 of the 4-element segments
+// addressed by lanes j/4 + 4k, k < 4.  MFMA lane i of 16-row block mt uses
+// tile row perm(mt, i) = 16 mt + 2 (i%4) + (i/4)%2 + 8 (i/8).  Online softmax
+// in base 2 with a lazily moved reference max.  Row splits of the index list
+// run in separate workgroups and are merged by mla_combine_kernel from their
 // (O, max, sum) partials.
 // ---------------------------------------------------------------------------
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kMlaWaves = 4, kMlaThreads = kMlaWaves * kWave;
 constexpr int kHeadsPerWave = 16, kHeadsPerWG = kMlaWaves * kHeadsPerWave;
-constexpr int kTile = 32;
+constexpr int kTile = 64;
+constexpr int kBlocks = kTile / 16;                      // 16-row MFMA blocks per tile
 constexpr int kChunksPerRow = kDqk / 8;                  // 72 bf16 chunks of 16 bytes
-constexpr int kTileBytes = kTile * kChunksPerRow * 16;   // 36 KB
+constexpr int kTileBytes = kTile * kChunksPerRow * 16;   // 72 KB
 constexpr int kKSteps = kDqk / 32;                       // 18 k-steps of 32 dims
 constexpr int kNTiles = kDv / 16;                        // 32 value tiles of 16 columns
 constexpr int kIdxCap = 2048;                            // most index entries of one split
-constexpr int kIdxPad = 4 * kTile;                       // the last tile's padding + 3 tiles read ahead
+constexpr int kIdxPad = 3 * kTile;                       // the last tile's padding + 2 tiles read ahead
 constexpr float kSlack = 8.0f;                           // log2 headroom before the running max moves
-static_assert(kMlaWaves * 8 == kTile, "one 8-row group of the tile per wave");
+static_assert(kMlaWaves * 16 == kTile, "two 8-row groups of the tile per wave");
 
 int mla_row_tile() { return kTile; }
 int mla_max_rows_per_split() { return kIdxCap; }
@@ -169,27 +174,84 @@ __device__ __forceinline__ int tile_row(int mt, int i) {
   return 16 * mt + 2 * (i & 3) + ((i >> 2) & 1) + 8 * (i >> 3);
 }
 
-// Byte offset of 16-byte chunk c (0..71) of tile row r (0..31).
+// Byte offset of 16-byte chunk c (0..71) of tile row r (0..63).
 __device__ __forceinline__ int chunk_off(int r, int c) {
   return ((r >> 3) * 9 + (c >> 3)) * 1024 + 16 * (8 * (r & 7) + ((c ^ r ^ (r >> 3)) & 7));
 }
 
-// Transpose reads of the PV operand, 4 value tiles (8 reads) per group, in
-// inline asm: the compiler's own wait insertion treats the transpose-read
-// intrinsic as aliasing every pending global->LDS copy and would drain them
-// all before each read.  Here the tile being read is known to be complete
-// (its copies were waited for before the barrier that opened the tile), so
-// only the LDS counter matters: each block issues the next group's reads and
-// then waits until at most those 8 are outstanding, which completes the
-// previous group.  The previous group's registers are in/out operands of
-// that block, so nothing reads them before the wait, and no register of an
-// in-flight read is reused.
+// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane groups
+// holding one head's rows) with the gfx950 lane-swap instructions: VALU
+// work, no LDS round trip.  permlane{16,32}_swap(x, x) returns, per lane,
+// x(l) and x(l ^ 16) (or x(l ^ 32)) in some order.
+__device__ __forceinline__ float group4_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float group4_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Operand reads of a tile go through inline asm: the compiler's own wait
+// insertion treats LDS reads as aliasing every pending global->LDS copy and
+// would drain them all before each read.  The tile being read is known to be
+// complete (its copies were waited for before the barrier that opened it),
+// so only the LDS counter matters.  Reads go in groups; each block issues a
+// later group and then waits until only the groups issued after the one it
+// completes are outstanding.  A completed group's registers are in/out
+// operands of that block, so nothing reads them before the wait, and no
+// register of an in-flight read is reused.
+struct QkGroup {
+  bf16x8 r[4];  // [2 j + k-step parity], 16-row block 2h + j
+};
+
+// QK^T operand A: group (g, h) = k-steps 2g, 2g+1 of 16-row blocks 2h, 2h+1,
+// at addr[j][parity] + g KB.
+template <int G>
+__device__ __forceinline__ void qk_issue(QkGroup& nxt, const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n"
+      "ds_read_b128 %1, %5 offset:%8\n"
+      "ds_read_b128 %2, %6 offset:%8\n"
+      "ds_read_b128 %3, %7 offset:%8"
+      : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024)
+      : "memory");
+}
+
+template <int G>
+__device__ __forceinline__ void qk_issue_wait(QkGroup& nxt, QkGroup& done, const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%12\n"
+      "ds_read_b128 %1, %9 offset:%12\n"
+      "ds_read_b128 %2, %10 offset:%12\n"
+      "ds_read_b128 %3, %11 offset:%12\n"
+      "s_waitcnt lgkmcnt(8)"
+      : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3]), "+v"(done.r[0]), "+v"(done.r[1]),
+        "+v"(done.r[2]), "+v"(done.r[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void qk_wait(QkGroup& done) {
+  asm volatile("s_waitcnt lgkmcnt(%4)"
+               : "+v"(done.r[0]), "+v"(done.r[1]), "+v"(done.r[2]), "+v"(done.r[3])
+               : "i"(N)
+               : "memory");
+}
+
 struct TrGroup {
   i16x4 r[8];  // [2 k + h]: value tile 4 g + k, row half h
 };
 
-// addr[2 k + h]: LDS byte address of value tile k (mod 4), row half h, of the
-// tile's first 4-tile group; group G sits G KB further (immediate offset).
+// PV operand (V^T): addr[2 k + h] = value tile k (mod 4), row half h of the
+// k-step's first 4-tile group; group G sits G KB further.
 template <int G>
 __device__ __forceinline__ void tr_issue_wait(TrGroup& nxt, TrGroup& prev, const uint32_t (&addr)[8]) {
   asm volatile(
@@ -218,135 +280,73 @@ __device__ __forceinline__ void tr_wait_last(TrGroup& prev) {
                : "memory");
 }
 
-// QK^T operand reads in the same style: group g = k-steps 2g, 2g+1 of both
-// 16-row blocks (4 reads of 16 bytes), at base + g KB; three groups in
-// flight, each block issuing group g+2 and completing group g.
-struct QkGroup {
-  bf16x8 r[4];  // [2 mt + k-step parity]
-};
-
-template <int G>
-__device__ __forceinline__ void qk_issue_wait(QkGroup& nxt, QkGroup& done, const uint32_t (&addr)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:%12\n"
-      "ds_read_b128 %1, %9 offset:%12\n"
-      "ds_read_b128 %2, %10 offset:%12\n"
-      "ds_read_b128 %3, %11 offset:%12\n"
-      "s_waitcnt lgkmcnt(8)"
-      : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3]), "+v"(done.r[0]), "+v"(done.r[1]),
-        "+v"(done.r[2]), "+v"(done.r[3])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024)
-      : "memory");
-}
-
-template <int G>
-__device__ __forceinline__ void qk_issue(QkGroup& nxt, const uint32_t (&addr)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%8\n"
-      "ds_read_b128 %1, %5 offset:%8\n"
-      "ds_read_b128 %2, %6 offset:%8\n"
-      "ds_read_b128 %3, %7 offset:%8"
-      : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void qk_wait(QkGroup& done) {
-  asm volatile("s_waitcnt lgkmcnt(%4)"
-               : "+v"(done.r[0]), "+v"(done.r[1]), "+v"(done.r[2]), "+v"(done.r[3])
-               : "i"(N)
-               : "memory");
-}
-
-// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane groups
-// holding one head's rows) with the gfx950 lane-swap instructions: VALU
-// work, no LDS round trip.  permlane{16,32}_swap(x, x) returns, per lane,
-// x(l) and x(l ^ 16) (or x(l ^ 32)) in some order.
-__device__ __forceinline__ float group4_max(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float group4_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 struct MlaShared {
-  uint8_t rows[3][kTileBytes];  // tile buffers (read only through inline asm)
+  uint8_t rows[2][kTileBytes];  // tile buffers (read only through inline asm)
   int32_t idx[kIdxCap + kIdxPad];
-  uint32_t vmask[(kIdxCap + kIdxPad) / kTile];  // bit r of word t: row r of tile t is a valid entry
+  uint64_t vmask[(kIdxCap + kIdxPad) / kTile];  // bit r of word t: row r of tile t is a valid entry
 };
 
 // Opens a tile of the copy pipeline: this wave's copies of the tile have
-// landed (the 9 copies of the next tile may stay in flight) and its earlier
-// LDS accesses are done, then the workgroup barrier.  The barrier is issued
-// bare: __syncthreads() would also drain every copy still in flight, since
-// its release fence covers the copies' pending LDS writes.  All waves share
-// one LDS, so once every wave has passed its own waits, the tile is complete
-// for all of them.
+// landed and its earlier LDS accesses are done, then the workgroup barrier.
+// The barrier is issued bare: __syncthreads() would also drain any copy
+// still in flight, since its release fence covers the copies' pending LDS
+// writes.  All waves share one LDS, so once every wave has passed its own
+// waits, the tile is complete for all of them.
 __device__ __forceinline__ void tile_barrier() {
-  asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// bf16 cache: wave w copies rows 8w .. 8w+7 of a tile with nine 1 KB DMA
-// instructions; pos is the position of this lane's row 8w + l/8 (< 0: row 0).
-__device__ __forceinline__ void tile_dma(uint8_t* dst, const MlaParams& p, int32_t pos, int64_t seq_row0, int wave,
-                                         int l) {
-  const int64_t row = seq_row0 + max(pos, 0);
-  const int cx = ((l & 7) ^ (l >> 3) ^ wave) & 7;  // chunk slot of this lane within each 8-chunk group
-  const uint8_t* src = (const uint8_t*)p.kv + row * (2 * kDqk) + cx * 16;
-  uint8_t* seg = dst + wave * 9 * 1024;
+// Wave w copies rows 16w .. 16w+15 of a tile (two 8-row groups) with
+// eighteen 1 KB DMA instructions; pos[g] is the position of this lane's row
+// 16w + 8g + l/8 (< 0: row 0).  Lane l of copy i of a group fills slot l of
+// segment i, i.e. bf16 chunk 8i + cx of its row.  A bf16 cache copies that
+// chunk.  An e4m3 cache copies the 16 codes that decode to bf16 chunks
+// 2m, 2m+1 (raw chunk m) into the slot of chunk 2m, and the same codes again
+// into the slot of chunk 2m+1, where the decode's second half lands; so each
+// raw chunk sits where its own decoded first half goes, and fp8_decode can
+// expand a wave's rows in place with no exchange between lanes.
+template <bool FP8>
+__device__ __forceinline__ void tile_dma(uint8_t* dst, const MlaParams& p, const int32_t (&pos)[2], int64_t seq_row0,
+                                         int wave, int l) {
 #pragma unroll
-  for (int i = 0; i < 9; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(src + 128 * i),
-                                     (__attribute__((address_space(3))) void*)(seg + 1024 * i), 16, 0, 0);
-}
-
-// e4m3 cache: 32 rows x 36 chunks of 16 codes; thread k-th chunk id = tid + 256 k
-// (ids past the end repeat the last chunk, so loads and stores are unconditional).
-struct Fp8Stage {
-  static constexpr int kChunks = kTile * (kDqk / 16);
-  static constexpr int kPerThread = (kChunks + kMlaThreads - 1) / kMlaThreads;
-  i32x4 v[kPerThread];
-  float sc[kPerThread];
-};
-
-__device__ __forceinline__ void fp8_load(Fp8Stage& st, const MlaParams& p, const int32_t* s_pos, int64_t seq_row0) {
+  for (int g = 0; g < 2; ++g) {
+    const int rg = 2 * wave + g;  // 8-row group
+    const int64_t row = seq_row0 + max(pos[g], 0);
+    const int cx = ((l & 7) ^ (l >> 3) ^ rg) & 7;  // chunk slot of this lane within each 8-chunk group
+    const uint8_t* src = FP8 ? (const uint8_t*)p.kv + row * kDqk + (cx >> 1) * 16
+                             : (const uint8_t*)p.kv + row * (2 * kDqk) + cx * 16;
+    uint8_t* seg = dst + rg * 9 * 1024;
 #pragma unroll
-  for (int k = 0; k < Fp8Stage::kPerThread; ++k) {
-    const int id = min((int)threadIdx.x + k * kMlaThreads, Fp8Stage::kChunks - 1);
-    const int r = id / (kDqk / 16), c = id % (kDqk / 16);
-    const int64_t row = seq_row0 + max(s_pos[r], 0);
-    st.v[k] = *((const i32x4*)((const uint8_t*)p.kv + row * kDqk) + c);
-    st.sc[k] = p.kv_scale[row];
+    for (int i = 0; i < 9; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (FP8 ? 64 : 128) * i),
+                                       (__attribute__((address_space(3))) void*)(seg + 1024 * i), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void fp8_store(const Fp8Stage& st, uint8_t* dst) {
-#pragma unroll
-  for (int k = 0; k < Fp8Stage::kPerThread; ++k) {
-    const int id = min((int)threadIdx.x + k * kMlaThreads, Fp8Stage::kChunks - 1);
-    const int r = id / (kDqk / 16), c = id % (kDqk / 16);
-    // 16 e4m3 codes -> 16 bf16 (exact: code * 2^e fits bf16) = bf16 chunks 2c, 2c+1
+// e4m3 cache: expands, in place, the rows this wave copied: lane l takes row
+// 16w + l/4 (whose scale it holds) and raw chunks m = l%4 + 4k, k < 9.  The
+// wave's copies must have landed (vmcnt(0)).  Code x power-of-two scale is
+// exact in bf16.
+__device__ __forceinline__ void fp8_decode(uint8_t* buf, float scale, int wave, int l) {
+  const int r = 16 * wave + (l >> 2);
+#pragma unroll 1
+  for (int k = 0; k < kDqk / 64; ++k) {
+    const int m = (l & 3) + 4 * k;
+    uint8_t* d0 = buf + chunk_off(r, 2 * m);
+    const i32x4 v = *(const i32x4*)d0;
     uint32_t w[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t word = (uint32_t)st.v[k][q];
+      const uint32_t word = (uint32_t)v[q];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const float a = e4m3_to_f32((word >> (16 * h2)) & 0xFFu) * st.sc[k];
-        const float bb = e4m3_to_f32((word >> (16 * h2 + 8)) & 0xFFu) * st.sc[k];
+        const float a = e4m3_to_f32((word >> (16 * h2)) & 0xFFu) * scale;
+        const float bb = e4m3_to_f32((word >> (16 * h2 + 8)) & 0xFFu) * scale;
         w[2 * q + h2] = (__float_as_uint(a) >> 16) | (__float_as_uint(bb) & 0xFFFF0000u);
       }
     }
-    *(i32x4*)(dst + chunk_off(r, 2 * c)) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    *(i32x4*)(dst + chunk_off(r, 2 * c + 1)) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    *(i32x4*)d0 = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    *(i32x4*)(buf + chunk_off(r, 2 * m + 1)) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
   }
 }
 
@@ -371,19 +371,36 @@ void mla_mfma_kernel(MlaParams p) {
   const int32_t* sel = p.topk_idx + (int64_t)bt * p.K;
   const int j_begin = split * p.rows_per_split;
   const int n_rows = max(0, min(min(p.K, j_begin + p.rows_per_split) - j_begin, kIdxCap));
+  const int my_row = 16 * wave + (l >> 3);  // this lane's row of 8-row group 0 (group 1: +8)
+  // index entry j of the split -> position (-1: none); the load is
+  // unconditional and clamped into the list, so that several of them can be
+  // in flight at once
+  auto resolve = [&](int j) -> int32_t {
+    const int32_t v = sel[min(j_begin + j, p.K - 1)];
+    return (j < n_rows && v >= 0 && v < len) ? v : -1;
+  };
 
-  // resolve the split's index list (the host sizes splits to <= kIdxCap rows)
-  for (int i = tid; i < n_rows; i += kMlaThreads) {
-    const int32_t v = sel[j_begin + i];
-    s_idx[i] = (v >= 0 && v < len) ? v : -1;
-  }
-  // pad the last tile plus the 3 tiles whose positions are read ahead
-  const int n_pad = ((n_rows + kTile - 1) / kTile + 3) * kTile;
-  for (int i = n_rows + tid; i < n_pad; i += kMlaThreads) s_idx[i] = -1;
-  __syncthreads();
-  for (int t = wave; t < n_pad / kTile; t += kMlaWaves) {
-    const uint64_t bal = __ballot(l < kTile && s_idx[t * kTile + (l & (kTile - 1))] >= 0);
-    if (l == 0) sh.vmask[t] = (uint32_t)bal;
+  // Prologue: every load of the split's index list is issued at once (the
+  // host sizes splits to <= kIdxCap rows); once they land the list is stored
+  // to LDS and the first tile's copy starts (its rows come straight from
+  // registers), with the query loads behind it.  The LDS stores go first:
+  // stored after the copy was issued, they would wait for it to land.
+  constexpr int kPer = kIdxCap / kMlaThreads;
+  int32_t iv[kPer];  // entries tid + 256 k
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) iv[k] = resolve(tid + k * kMlaThreads);
+  // the list in LDS, padded with -1 through the last tile plus the 2 tiles
+  // whose positions are read ahead
+  const int n_tiles = (n_rows + kTile - 1) / kTile;
+  const int n_pad = (n_tiles + 2) * kTile;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) s_idx[tid + k * kMlaThreads] = iv[k];  // -1 past the list
+  for (int i = kIdxCap + tid; i < n_pad; i += kMlaThreads) s_idx[i] = -1;
+  float kscale = 0.0f;  // e4m3: scale of row 16 wave + l/4 of the tile being copied
+  {
+    const int32_t pos0[2] = {resolve(my_row), resolve(my_row + 8)};
+    tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
+    if constexpr (FP8) kscale = p.kv_scale[seq_row0 + max(resolve(16 * wave + (l >> 2)), 0)];
   }
 
   // query heads h0 + lc, dims 32 ks + 8 lg .. +8  (operand B of QK^T)
@@ -393,20 +410,31 @@ void mla_mfma_kernel(MlaParams p) {
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qrow[ks * 4 + lg];
   }
+
   const float zscale = p.scale * 1.4426950408889634f;  // logits in base-2 units
+  // the list is complete in LDS; a bare barrier lets the first tile's copy
+  // stay in flight (__syncthreads() would wait for it)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int t = wave; t < n_pad / kTile; t += kMlaWaves) {
+    const uint64_t bal = __ballot(s_idx[t * kTile + l] >= 0);
+    if (l == 0) sh.vmask[t] = bal;
+  }
 
   // LDS byte offsets of this lane's operand reads within a tile
-  int a_off[2][2];  // QK^T operand A: [mt][ks parity], plus 1 KB per pair of k-steps
+  uint32_t a_off[kBlocks][2];  // QK^T operand A: [16-row block][k-step parity], plus 1 KB per 2 k-steps
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < kBlocks; ++mt)
 #pragma unroll
     for (int par = 0; par < 2; ++par) a_off[mt][par] = chunk_off(tile_row(mt, lc), 4 * par + lg);
-  int v_off[2][4];  // PV operand B: [row half][n % 4], plus 1 KB per 4 value tiles
+  uint32_t v_off[2][2][4];  // PV operand: [k-step][row half][n % 4], plus 1 KB per 4 value tiles
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int n4 = 0; n4 < 4; ++n4)
-      v_off[t][n4] = chunk_off(tile_row(t, 4 * lg + (lc >> 2)), 2 * n4 + ((lc & 3) >> 1)) + 8 * (lc & 1);
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int n4 = 0; n4 < 4; ++n4)
+        v_off[kk][hh][n4] =
+            chunk_off(tile_row(2 * kk + hh, 4 * lg + (lc >> 2)), 2 * n4 + ((lc & 3) >> 1)) + 8 * (lc & 1);
 
   f32x4 o[kNTiles];
 #pragma unroll
@@ -414,54 +442,77 @@ void mla_mfma_kernel(MlaParams p) {
   float m_run = -INFINITY, l_run = 0.0f;  // for head h0 + lc
 
   auto compute = [&](const uint8_t* rows, int j0) {
-    const uint32_t vm = sh.vmask[j0 / kTile];  // read early: its latency hides behind QK^T
-    // ---- S^T[32 rows x 16 heads] over all 576 dims (two chains per half) ----
-    f32x4 s[2][2];
+    const uint64_t vm = sh.vmask[j0 / kTile];  // read early: its latency hides behind QK^T
+    const uint32_t base = (uint32_t)(uintptr_t)rows;
+    // ---- S^T[64 rows x 16 heads] over all 576 dims: 8 accumulation chains ----
+    f32x4 s[kBlocks][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < kBlocks; ++mt) {
       s[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    uint32_t qaddr[4];
+    uint32_t qaddr[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int par = 0; par < 2; ++par) qaddr[2 * mt + par] = (uint32_t)(uintptr_t)rows + a_off[mt][par];
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) qaddr[h][2 * j + par] = base + a_off[2 * h + j][par];
     QkGroup qg[3];
-    auto qk_group = [&](const QkGroup& cur, int g) {
+    auto qk_group = [&](const QkGroup& cur, int g, int h) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int par = 0; par < 2; ++par)
-          s[mt][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.r[2 * mt + par], qreg[2 * g + par], s[mt][par], 0,
-                                                               0, 0);
+          s[2 * h + j][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.r[2 * j + par], qreg[2 * g + par],
+                                                                      s[2 * h + j][par], 0, 0, 0);
     };
-    static_assert(kKSteps == 18, "nine groups of two k-steps");
-    qk_issue<0>(qg[0], qaddr);
-    qk_issue<1>(qg[1], qaddr);
-    qk_issue_wait<2>(qg[2], qg[0], qaddr);
-    qk_group(qg[0], 0);
-    qk_issue_wait<3>(qg[0], qg[1], qaddr);
-    qk_group(qg[1], 1);
-    qk_issue_wait<4>(qg[1], qg[2], qaddr);
-    qk_group(qg[2], 2);
-    qk_issue_wait<5>(qg[2], qg[0], qaddr);
-    qk_group(qg[0], 3);
-    qk_issue_wait<6>(qg[0], qg[1], qaddr);
-    qk_group(qg[1], 4);
-    qk_issue_wait<7>(qg[1], qg[2], qaddr);
-    qk_group(qg[2], 5);
-    qk_issue_wait<8>(qg[2], qg[0], qaddr);
-    qk_group(qg[0], 6);
+    static_assert(kKSteps == 18, "nine pairs of k-steps");
+    // 18 groups (g, h) in the order (0,0) (0,1) (1,0) ... (8,1), three in flight
+    qk_issue<0>(qg[0], qaddr[0]);
+    qk_issue<0>(qg[1], qaddr[1]);
+    qk_issue_wait<1>(qg[2], qg[0], qaddr[0]);
+    qk_group(qg[0], 0, 0);
+    qk_issue_wait<1>(qg[0], qg[1], qaddr[1]);
+    qk_group(qg[1], 0, 1);
+    qk_issue_wait<2>(qg[1], qg[2], qaddr[0]);
+    qk_group(qg[2], 1, 0);
+    qk_issue_wait<2>(qg[2], qg[0], qaddr[1]);
+    qk_group(qg[0], 1, 1);
+    qk_issue_wait<3>(qg[0], qg[1], qaddr[0]);
+    qk_group(qg[1], 2, 0);
+    qk_issue_wait<3>(qg[1], qg[2], qaddr[1]);
+    qk_group(qg[2], 2, 1);
+    qk_issue_wait<4>(qg[2], qg[0], qaddr[0]);
+    qk_group(qg[0], 3, 0);
+    qk_issue_wait<4>(qg[0], qg[1], qaddr[1]);
+    qk_group(qg[1], 3, 1);
+    qk_issue_wait<5>(qg[1], qg[2], qaddr[0]);
+    qk_group(qg[2], 4, 0);
+    qk_issue_wait<5>(qg[2], qg[0], qaddr[1]);
+    qk_group(qg[0], 4, 1);
+    qk_issue_wait<6>(qg[0], qg[1], qaddr[0]);
+    qk_group(qg[1], 5, 0);
+    qk_issue_wait<6>(qg[1], qg[2], qaddr[1]);
+    qk_group(qg[2], 5, 1);
+    qk_issue_wait<7>(qg[2], qg[0], qaddr[0]);
+    qk_group(qg[0], 6, 0);
+    qk_issue_wait<7>(qg[0], qg[1], qaddr[1]);
+    qk_group(qg[1], 6, 1);
+    qk_issue_wait<8>(qg[1], qg[2], qaddr[0]);
+    qk_group(qg[2], 7, 0);
+    qk_issue_wait<8>(qg[2], qg[0], qaddr[1]);
+    qk_group(qg[0], 7, 1);
     qk_wait<4>(qg[1]);
-    qk_group(qg[1], 7);
+    qk_group(qg[1], 8, 0);
     qk_wait<0>(qg[2]);
-    qk_group(qg[2], 8);
-    // ---- online softmax for head h0 + lc over rows 4 lg + e (+16) ----
-    float z[2][4];
+    qk_group(qg[2], 8, 1);
+
+    // ---- online softmax for head h0 + lc over rows 4 lg + e of each block ----
+    float z[kBlocks][4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < kBlocks; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool valid = (vm >> tile_row(mt, 4 * lg + e)) & 1u;
@@ -478,9 +529,9 @@ void mla_mfma_kernel(MlaParams p) {
     const float m_new = move ? tmax : m_run;
     const float alpha = move ? exp2f(m_run - m_new) : 1.0f;  // m_run = -inf gives 0
     float psum = 0.0f;
-    float pr[2][4];
+    float pr[kBlocks][4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < kBlocks; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pr[mt][e] = z[mt][e] > -INFINITY ? exp2f(z[mt][e] - m_new) : 0.0f;  // m_new >= z when z is finite
@@ -499,30 +550,34 @@ void mla_mfma_kernel(MlaParams p) {
         for (int e = 0; e < 4; ++e) o[n][e] *= alpha;
     }
 
-    // P^T operand (B of O^T = V^T P^T): head lc, k-slot 8 lg + j <-> row
-    // (j < 4 ? 4 lg + j : 16 + 4 lg + j - 4) of the tile's MFMA row order
-    bf16x8 pa;
-    {
+    // P^T operands (B of O^T = V^T P^T), one per 32-row k-step kk: head lc,
+    // k-slot 8 lg + j <-> row (j < 4 ? block 2kk row 4 lg + j : block 2kk+1 row 4 lg + j - 4)
+    bf16x8 pa[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
       uint16_t pb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[j >> 2][j & 3]);
-      pa = __builtin_bit_cast(bf16x8, pb);
+      for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[2 * kk + (j >> 2)][j & 3]);
+      pa[kk] = __builtin_bit_cast(bf16x8, pb);
     }
     // ---- O^T[512 value columns x 16 heads] += V^T P^T ----
     // The accumulator is O transposed, so lane l holds 4 consecutive columns
     // 16 n + 4 (l/16) .. +4 of head lc: rescaling and normalising need no
     // lane exchange and the write-out is one vector store per value tile.
-    // V^T operand (A): k-slot 8 lg + k (k < 4) is tile row tile_row(0, 4 lg + k),
-    // slot 8 lg + 4 + k is tile_row(1, 4 lg + k): lane lc addresses row k = lc/4
-    // of its group and columns 4 (lc%4) .. +4 of the 16-column tile.
-    uint32_t taddr[8];
+    // V^T operand (A) of k-step kk: k-slot 8 lg + k (k < 4) is tile row
+    // tile_row(2kk, 4 lg + k), slot 8 lg + 4 + k is tile_row(2kk+1, 4 lg + k):
+    // lane lc addresses row k = lc/4 of its group and columns 4 (lc%4) .. +4
+    // of the 16-column tile.
+    uint32_t taddr[2][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      taddr[2 * k] = (uint32_t)(uintptr_t)rows + v_off[0][k];
-      taddr[2 * k + 1] = (uint32_t)(uintptr_t)rows + v_off[1][k];
-    }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        taddr[kk][2 * k] = base + v_off[kk][0][k];
+        taddr[kk][2 * k + 1] = base + v_off[kk][1][k];
+      }
     TrGroup grp[2];
-    auto pv_group = [&](const TrGroup& cur, int g) {
+    auto pv_group = [&](const TrGroup& cur, int g, int kk) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const i16x4 lo = cur.r[2 * k], hi = cur.r[2 * k + 1];
@@ -530,69 +585,83 @@ void mla_mfma_kernel(MlaParams p) {
                                                                __builtin_bit_cast(int, (short2){lo[2], lo[3]}),
                                                                __builtin_bit_cast(int, (short2){hi[0], hi[1]}),
                                                                __builtin_bit_cast(int, (short2){hi[2], hi[3]})});
-        o[4 * g + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pa, o[4 * g + k], 0, 0, 0);
+        o[4 * g + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pa[kk], o[4 * g + k], 0, 0, 0);
       }
     };
-    tr_issue_wait<0>(grp[0], grp[1], taddr);  // grp[1] is a dummy here
-    tr_issue_wait<1>(grp[1], grp[0], taddr);
-    pv_group(grp[0], 0);
-    tr_issue_wait<2>(grp[0], grp[1], taddr);
-    pv_group(grp[1], 1);
-    tr_issue_wait<3>(grp[1], grp[0], taddr);
-    pv_group(grp[0], 2);
-    tr_issue_wait<4>(grp[0], grp[1], taddr);
-    pv_group(grp[1], 3);
-    tr_issue_wait<5>(grp[1], grp[0], taddr);
-    pv_group(grp[0], 4);
-    tr_issue_wait<6>(grp[0], grp[1], taddr);
-    pv_group(grp[1], 5);
-    tr_issue_wait<7>(grp[1], grp[0], taddr);
-    pv_group(grp[0], 6);
+    // 16 groups: k-step 0 then 1, value tiles 4 g .. 4 g + 3 each; one group in flight
+    tr_issue_wait<0>(grp[0], grp[1], taddr[0]);  // grp[1] is a dummy here
+    tr_issue_wait<1>(grp[1], grp[0], taddr[0]);
+    pv_group(grp[0], 0, 0);
+    tr_issue_wait<2>(grp[0], grp[1], taddr[0]);
+    pv_group(grp[1], 1, 0);
+    tr_issue_wait<3>(grp[1], grp[0], taddr[0]);
+    pv_group(grp[0], 2, 0);
+    tr_issue_wait<4>(grp[0], grp[1], taddr[0]);
+    pv_group(grp[1], 3, 0);
+    tr_issue_wait<5>(grp[1], grp[0], taddr[0]);
+    pv_group(grp[0], 4, 0);
+    tr_issue_wait<6>(grp[0], grp[1], taddr[0]);
+    pv_group(grp[1], 5, 0);
+    tr_issue_wait<7>(grp[1], grp[0], taddr[0]);
+    pv_group(grp[0], 6, 0);
+    tr_issue_wait<0>(grp[0], grp[1], taddr[1]);
+    pv_group(grp[1], 7, 0);
+    tr_issue_wait<1>(grp[1], grp[0], taddr[1]);
+    pv_group(grp[0], 0, 1);
+    tr_issue_wait<2>(grp[0], grp[1], taddr[1]);
+    pv_group(grp[1], 1, 1);
+    tr_issue_wait<3>(grp[1], grp[0], taddr[1]);
+    pv_group(grp[0], 2, 1);
+    tr_issue_wait<4>(grp[0], grp[1], taddr[1]);
+    pv_group(grp[1], 3, 1);
+    tr_issue_wait<5>(grp[1], grp[0], taddr[1]);
+    pv_group(grp[0], 4, 1);
+    tr_issue_wait<6>(grp[0], grp[1], taddr[1]);
+    pv_group(grp[1], 5, 1);
+    tr_issue_wait<7>(grp[1], grp[0], taddr[1]);
+    pv_group(grp[0], 6, 1);
     tr_wait_last(grp[1]);
-    pv_group(grp[1], 7);
+    pv_group(grp[1], 7, 1);
   };
 
-  __syncthreads();  // s_idx complete
-  // One compact loop over the tiles: the loop body stays in the instruction
-  // cache, where a fully unrolled schedule would be fetched cold for every
-  // tile.  Tile t sits in buffer t % 3.
-  const int n_tiles = (n_rows + kTile - 1) / kTile;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // vmask complete (copies may be in flight)
+  // One compact loop over the tiles (the body stays in the instruction
+  // cache).  Tile t sits in buffer t % 2.  The rows this lane copies for
+  // tile t are entries 64 t + 16 wave + l/8 (+8); they are read one tile
+  // ahead, so the copy is issued without an LDS round trip.  The copy of the
+  // padding tile past the end reads row 0 and is never computed.
+  int32_t pos[2] = {s_idx[kTile + my_row], s_idx[kTile + my_row + 8]};
+  int cur = 0;
   if constexpr (!FP8) {
-    // Step t: wait for this wave's copy of tile t (the copies of tile t+1 may
-    // stay in flight), barrier (tile t complete; every wave is done with tile
-    // t-1, whose buffer is reused), start copying tile t+2, compute tile t.
-    // The row this lane copies for tile t is entry 32 t + 8 wave + l/8; it is
-    // read one tile ahead, so the copy is issued without an LDS round trip.
-    // Copies of padding tiles past the end read row 0 and are never computed.
-    const int my_row = 8 * wave + (l >> 3);
-    tile_dma(sh.rows[0], p, s_idx[my_row], seq_row0, wave, l);
-    tile_dma(sh.rows[1], p, s_idx[kTile + my_row], seq_row0, wave, l);
-    int32_t pos = s_idx[2 * kTile + my_row];
-    int cur = 0, nxt = 2;  // buffers of tiles t and t+2
+    // Step t: wait for this wave's copy of tile t, barrier (tile t complete;
+    // every wave is done with tile t-1, whose buffer is reused), start
+    // copying tile t+1, compute tile t.
     for (int t = 0; t < n_tiles; ++t) {
       tile_barrier();
-      tile_dma(sh.rows[nxt], p, pos, seq_row0, wave, l);
-      pos = s_idx[(t + 3) * kTile + my_row];
+      tile_dma<false>(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l);
+      pos[0] = s_idx[(t + 2) * kTile + my_row];
+      pos[1] = s_idx[(t + 2) * kTile + my_row + 8];
       compute(sh.rows[cur], t * kTile);
-      cur = cur == 2 ? 0 : cur + 1;
-      nxt = nxt == 2 ? 0 : nxt + 1;
+      cur ^= 1;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // copies of padding tiles land before exit
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the padding tile's copy lands before exit
   } else {
-    // Tile t+1 waits in registers while tile t is computed; step t stores it
-    // (decoded) into buffer (t+1) % 3 and loads tile t+2.
-    Fp8Stage st;
-    fp8_load(st, p, s_idx, seq_row0);
-    fp8_store(st, sh.rows[0]);
-    fp8_load(st, p, s_idx + kTile, seq_row0);
-    int cur = 0, nxt = 1;  // buffers of tiles t and t+1
+    // Step t: barrier (every wave has decoded its rows of tile t and is done
+    // with tile t-1), start copying tile t+1, compute tile t, then wait for
+    // this wave's copy and decode its rows of tile t+1.
+    const int srow = 16 * wave + (l >> 2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    fp8_decode(sh.rows[0], kscale, wave, l);
     for (int t = 0; t < n_tiles; ++t) {
       __syncthreads();
-      fp8_store(st, sh.rows[nxt]);
-      fp8_load(st, p, s_idx + (t + 2) * kTile, seq_row0);
+      tile_dma<true>(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l);
+      kscale = p.kv_scale[seq_row0 + max(s_idx[(t + 1) * kTile + srow], 0)];
+      pos[0] = s_idx[(t + 2) * kTile + my_row];
+      pos[1] = s_idx[(t + 2) * kTile + my_row + 8];
       compute(sh.rows[cur], t * kTile);
-      cur = cur == 2 ? 0 : cur + 1;
-      nxt = nxt == 2 ? 0 : nxt + 1;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      fp8_decode(sh.rows[cur ^ 1], kscale, wave, l);
+      cur ^= 1;
     }
   }
 
