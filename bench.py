@@ -10,8 +10,10 @@ scores over every cached position, Top-K, sparse MLA attention.
 
 Input copies rotate between steps (--rotate, default 3 copies of the index
 keys and latent cache: 4.2 GB) so the 256 MB Infinity Cache cannot serve the
-key stream from one step to the next.  Steps are replayed as HIP graphs (one
-per input copy) unless --no-graph.
+key stream from one step to the next.  Steps are launched eagerly (five
+kernels each; the host stays well ahead of the GPU, so they run back to
+back); --graph replays them as HIP graphs instead (one per input copy), which
+adds the graph launch gap (about 5 us) to every step.
 
 Prints one JSON line.  `roofline` covers the dominant kernel (the indexer
 score kernel, timed live with HIP events on the launch stream); `cpu_baseline`
@@ -41,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode128k")
     ap.add_argument("--rotate", type=int, default=3)
-    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay each step as a HIP graph")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches (the default)")
     ap.add_argument("--stage-steps", type=int, default=50, help="eager steps timed per stage")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline: time the oracle on queries for at least this long (0: skip)")
@@ -234,7 +237,7 @@ def main():
     ref_out = outs["out"].clone()
 
     graphs = None
-    if not args.no_graph:
+    if args.graph and not args.no_graph:
         graphs = []
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())

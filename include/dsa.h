@@ -31,8 +31,8 @@
  *    0 .. vis-1 with vis = len_b - q_len + 1 + t (causal).
  *  - Reentrant; concurrent calls on different streams must not share a
  *    workspace or an output buffer.
- *  - Workspaces of dsa_topk and dsa_forward begin with counters (score
- *    histograms, per-query arrival counts) that must be zero when a call
+ *  - Workspaces of dsa_topk and dsa_forward begin with counters (one
+ *    4096-bin score histogram per query) that must be zero when a call
  *    starts: the first dsa_workspace_zero_bytes(p) bytes.  Every call that
  *    returns DSA_OK leaves them zero again, so a workspace is zeroed once
  *    (dsa_workspace_init, or allocate it zeroed) and then reused without a

@@ -88,12 +88,12 @@ dsa_status validate_problem(const dsa_problem* p) {
 }
 
 // ------------------------------------------------------------------ Top-K layout
-// The counters (histograms, threshold-bin counts, arrivals) come first, at
-// offset 0 of every workspace that holds them: they must be zero when a call
-// starts, and every successful call leaves them zero again.
+// The counters (one score-key histogram per query) come first, at offset 0
+// of every workspace that holds them: they must be zero when a call starts,
+// and every successful call leaves them zero again.
 struct TopkLayout {
   int chunk, n_chunks;
-  int64_t off_hist, off_sub, off_bcnt, off_done, zero_bytes;
+  int64_t off_hist, zero_bytes;
   int64_t off_hdr, off_cnt, off_above, off_cand, off_blist, bytes;
 };
 
@@ -107,16 +107,13 @@ TopkLayout topk_layout(const dsa_problem* p) {
   L.chunk = (int)chunk;
   L.n_chunks = (int)((Lmax + chunk - 1) / chunk);
   L.off_hist = 0;
-  L.off_sub = BT * kHistBins * 4;
-  L.off_bcnt = L.off_sub + BT * kHistBins * 4;
-  L.off_done = L.off_bcnt + BT * 4;
-  L.zero_bytes = L.off_done + BT * 4;
+  L.zero_bytes = BT * kHistBins * 4;
   L.off_hdr = align_up(L.zero_bytes, kAlign);
   L.off_cnt = align_up(L.off_hdr + BT * 8, kAlign);
   L.off_above = align_up(L.off_cnt + BT * L.n_chunks * 4, kAlign);
   L.off_cand = align_up(L.off_above + BT * L.n_chunks * 4, kAlign);
   L.off_blist = align_up(L.off_cand + BT * Lmax * 8, kAlign);
-  L.bytes = align_up(L.off_blist + BT * Lmax * 8, kAlign);
+  L.bytes = align_up(L.off_blist + BT * align_up(Lmax, 4) * 4, kAlign);  // rows of bin keys start 16-byte aligned
   return L;
 }
 
@@ -265,12 +262,9 @@ dsa::TopkParams topk_params(const dsa_problem* p, const TopkLayout& L, uint8_t* 
   t.hist = (uint32_t*)(ws + L.off_hist);
   t.cand = (uint2*)(ws + L.off_cand);
   t.chunk_cnt = (uint32_t*)(ws + L.off_cnt);
-  t.bin_list = (uint2*)(ws + L.off_blist);
-  t.bin_count = (uint32_t*)(ws + L.off_bcnt);
-  t.done = (uint32_t*)(ws + L.off_done);
+  t.bin_keys = (uint32_t*)(ws + L.off_blist);
   t.header = (uint2*)(ws + L.off_hdr);
   t.chunk_above = (uint32_t*)(ws + L.off_above);
-  t.sub_hist = (uint32_t*)(ws + L.off_sub);
   t.topk_idx = idx;
   t.topk_count = cnt;
   t.B = p->batch;

@@ -22,12 +22,9 @@ struct ScoreParams {
 struct TopkParams {
   const float* scores;      // [B,T,Lmax]
   const int32_t* seq_lens;  // [B]
-  uint32_t* hist;           // [B*T, 4096] score-key histograms (complete; cleared after use)
-  uint32_t* sub_hist;       // [B*T, 4096] next-12-bit histograms of the threshold bin (zero on entry)
-  uint2* cand;              // [B*T, Lmax] per-chunk ordered (key, position) candidates
-  uint2* bin_list;          // [B*T, Lmax] the query's threshold-bin entries (unordered)
-  uint32_t* bin_count;      // [B*T] entries in bin_list (zero on entry)
-  uint32_t* done;           // [B*T] emit workgroups of the query finished (zero on entry)
+  uint32_t* hist;           // [B*T, 4096] score-key histograms (complete on entry; cleared after use)
+  uint2* cand;              // [B*T, Lmax] per-chunk ordered (key, position) candidates (bin >= threshold bin)
+  uint32_t* bin_keys;       // [B*T, Lmax rounded up to 4] per-chunk ordered keys in the threshold bin
   uint2* header;            // [B*T] (threshold bin, entries above it)
   uint32_t* chunk_cnt;      // [B*T, n_chunks] candidates per chunk
   uint32_t* chunk_above;    // [B*T, n_chunks] candidates above the threshold bin per chunk

@@ -13,19 +13,20 @@
 //      it and at least K at or above it;
 //   2. select_chunk_kernel: every chunk of every query writes, in position
 //      order, the (key, position) pairs whose bin is >= B (about 2-5K per
-//      query), and adds the next 12 key bits of its bin-B entries to a second
-//      per-query histogram;
-//   3. select_emit_kernel: every chunk again reads that second histogram and
-//      its query's whole candidate list, resolves the exact K-th key tau from
-//      the last 8 bits, counts the entries kept before its own chunk, and
-//      writes its own kept positions: every key > tau plus, in position
+//      query) and, into a region of its own, the keys whose bin is B;
+//   3. select_emit_kernel: every chunk gathers its query's bin-B keys from
+//      all chunks into LDS, resolves the exact K-th key tau from two more
+//      digits of 10 key bits, counts the entries kept before its own chunk,
+//      and writes its own kept positions: every key > tau plus, in position
 //      order, the first K - #{key > tau} keys equal to tau.
+// Both steps are latency-bound (a few KB per workgroup): each issues every
+// load that does not depend on another before using any, and block-wide
+// prefix sums run on cross-lane (DPP) adds.
 // select_row_kernel does all of it in one 1024-thread workgroup per query
 // (used for many short queries, where it saves two launches).
-// The counters (histograms, threshold-bin count) are zero on entry and are
-// cleared again by their last reader: in the emit step the query's last
-// chunk to finish (an arrival ticket taken after its own reads completed),
-// in row mode the query's workgroup.  The workspace is left as it was found.
+// The only counter is the step-1 histogram: zero on entry, cleared by the
+// step that follows its last reader (the emit step's chunk 0; in row mode the
+// query's workgroup).  The workspace is left as it was found.
 #include <stdlib.h>
 #include <string.h>
 
@@ -84,55 +85,82 @@ hipError_t launch_hist(const float* scores, const int32_t* seq_lens, uint32_t* h
 // --------------------------------------------------------------------------
 // block-wide helpers (256 threads = 4 waves)
 // --------------------------------------------------------------------------
-// Inclusive prefix sum of one value per thread, in thread order; *total gets
-// the block total.  s_wave: kSelWaves words of shared scratch.
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+// Inclusive prefix sum over the 64 lanes of a wave with DPP adds: shifts by
+// 1, 2, 4, 8 within each 16-lane row, then the last lane of row 0 is added
+// to row 1 and row 2 to row 3 (row_bcast:15), and lane 31 to rows 2 and 3
+// (row_bcast:31).  Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Inclusive prefix sums of N values per thread, in thread order, over a
+// workgroup of NW waves; total[i] gets the block total of value i.
+// s_wave: N * NW words of shared scratch.
+template <int N, int NW>
+__device__ __forceinline__ void block_scan(uint32_t (&v)[N], uint32_t* s_wave, uint32_t (&total)[N]) {
   const int wave = threadIdx.x / kWave, l = lane_id();
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o, kWave);
-    if (l >= o) v += y;
-  }
-  if (l == kWave - 1) s_wave[wave] = v;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    if (w < wave) off += s_wave[w];
-    tot += s_wave[w];
+  for (int i = 0; i < N; ++i) {
+    v[i] = wave_incl_scan(v[i]);
+    if (l == kWave - 1) s_wave[i * NW + wave] = v[i];
   }
   __syncthreads();
-  *total = tot;
-  return off + v;
-}
-
-// Exclusive prefix of per-element flags in (thread, element) order.
-template <int V>
-__device__ __forceinline__ uint32_t block_prefix_flags(const bool (&flag)[V], uint32_t* s_wave,
-                                                       uint32_t* total) {
-  uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < V; ++j) c += flag[j] ? 1u : 0u;
-  return block_incl_scan(c, s_wave, total) - c;
+  for (int i = 0; i < N; ++i) {
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = s_wave[i * NW + w];
+      if (w < wave) off += x;
+      tot += x;
+    }
+    v[i] += off;
+    total[i] = tot;
+  }
+  __syncthreads();
 }
 
-// Largest bin B of the NB-bin histogram h whose suffix count sum_{i >= B} h[i]
-// reaches `need`; *above = sum_{i > B} h[i].  Thread tid owns the PER bins
-// just below NB - PER*tid, so an inclusive scan in thread order counts the
-// entries at or above each thread's lowest bin.  All threads get the result.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+  uint32_t a[1] = {v}, t[1];
+  block_scan<1, kSelWaves>(a, s_wave, t);
+  *total = t[0];
+  return a[0];
+}
+
+// Thread tid's share of an NB-bin histogram: the PER bins just below
+// NB - PER*tid, highest first.  Loading it is separate from the scan below so
+// that the loads can be in flight together with a kernel's other loads.
 template <int NB>
-__device__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s_wave,
-                                   uint32_t* s_res, uint32_t* bin, uint32_t* above) {
-  constexpr int PER = NB / kSelThreads;
-  const int tid = threadIdx.x;
-  const int top = NB - 1 - PER * tid;  // this thread's highest bin
+struct BinSlice {
+  static constexpr int PER = NB / kSelThreads;
   uint32_t c[PER];
+};
+
+template <int NB>
+__device__ __forceinline__ void load_bin_slice(const uint32_t* h, BinSlice<NB>& s) {
+  const int top = NB - 1 - BinSlice<NB>::PER * (int)threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < BinSlice<NB>::PER; ++i) s.c[i] = h[top - i];
+}
+
+// Largest bin B of the histogram whose suffix count sum_{i >= B} h[i]
+// reaches `need`; *above = sum_{i > B} h[i].  An inclusive scan of the
+// slices in thread order counts the entries at or above each thread's lowest
+// bin.  All threads get the result.
+template <int NB>
+__device__ void threshold_from_slice(const BinSlice<NB>& s, uint32_t need, uint32_t* s_wave, uint32_t* s_res,
+                                     uint32_t* bin, uint32_t* above) {
+  constexpr int PER = BinSlice<NB>::PER;
+  const int top = NB - 1 - PER * (int)threadIdx.x;
   uint32_t own = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = h[top - i];
-    own += c[i];
-  }
+  for (int i = 0; i < PER; ++i) own += s.c[i];
   uint32_t total;
   const uint32_t incl = block_incl_scan(own, s_wave, &total);
   const uint32_t excl = incl - own;
@@ -140,12 +168,12 @@ __device__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s
     uint32_t run = excl;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (run + c[i] >= need) {
+      if (run + s.c[i] >= need) {
         s_res[0] = (uint32_t)(top - i);
         s_res[1] = run;
         break;
       }
-      run += c[i];
+      run += s.c[i];
     }
   }
   __syncthreads();
@@ -154,9 +182,17 @@ __device__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s
   __syncthreads();
 }
 
-constexpr int kSelV = 16;         // consecutive positions per thread per step
-constexpr int kEmitCap = 6000;    // threshold-bin entries the emit step keeps in LDS
-constexpr int kBinBuf = 2048;     // threshold-bin entries a chunk stages in LDS
+template <int NB>
+__device__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s_wave, uint32_t* s_res,
+                                   uint32_t* bin, uint32_t* above) {
+  BinSlice<NB> s;
+  load_bin_slice<NB>(h, s);
+  threshold_from_slice<NB>(s, need, s_wave, s_res, bin, above);
+}
+
+constexpr int kSelV = 16;          // consecutive positions per thread per step
+constexpr int kEmitCap = 10240;    // threshold-bin keys the emit step keeps in LDS
+constexpr int kMaxChunks = 1024;   // chunks per query (the host sizes chunks to respect it)
 
 __device__ __forceinline__ void write_all_visible(int32_t* out, int64_t c_lo, int64_t c_hi, int64_t vis, int K,
                                                   int c, int32_t* count) {
@@ -167,243 +203,356 @@ __device__ __forceinline__ void write_all_visible(int32_t* out, int64_t c_lo, in
   }
 }
 
-// Clears the query's counters (histograms, threshold-bin count, arrivals):
-// run by the last workgroup that reads them.
-__device__ __forceinline__ void clear_query_counters(const TopkParams& p, int bt, int nthreads) {
+// Row stride of the bin-key lists: Lmax rounded up to 4 keys, so that a row
+// starts 16-byte aligned.
+__device__ __forceinline__ int64_t bin_key_stride(int64_t Lmax) { return (Lmax + 3) & ~(int64_t)3; }
+
+// Clears the query's step-1 histogram (run once its last reader has finished).
+__device__ __forceinline__ void clear_query_hist(const TopkParams& p, int bt, int nthreads) {
   uint32_t* h = p.hist + (int64_t)bt * kHistBins;
-  uint32_t* g = p.sub_hist + (int64_t)bt * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += nthreads) {
-    h[i] = 0;
-    g[i] = 0;
-  }
-  if (threadIdx.x == 0) {
-    p.bin_count[bt] = 0;
-    p.done[bt] = 0;
+  for (int i = threadIdx.x; i < kHistBins; i += nthreads) h[i] = 0;
+}
+
+// kSelV consecutive scores from s0; positions >= lim get arbitrary values
+// (the caller masks them).  Every load is unconditional, its address clamped
+// into [.., lim): with per-lane branches the compiler would drain the loads
+// of one branch before issuing the other's.  VEC4: row + s0 is 16-byte
+// aligned and lim - s0 is a multiple of 4 for every lane.
+template <bool VEC4>
+__device__ __forceinline__ void load_scores(const float* row, int64_t s0, int64_t lim, float (&v)[kSelV]) {
+  if constexpr (VEC4) {
+#pragma unroll
+    for (int j = 0; j < kSelV; j += 4) {
+      const f32x4 x = *(const f32x4*)(row + min(s0 + j, lim - 4));
+      v[j] = x[0];
+      v[j + 1] = x[1];
+      v[j + 2] = x[2];
+      v[j + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSelV; ++j) v[j] = row[min(s0 + j, lim - 1)];
   }
 }
 
-// Step 2: candidates of one chunk + second-level histogram of the threshold bin.
+// Step 2: one chunk's candidates.  Writes, in position order, every
+// (key, position) whose bin is >= B to the chunk's slots of `cand`, the keys
+// whose bin is B to its slots of `bin_keys`, and the two counts.
+// VEC4: the scores are 16-byte aligned and Lmax is a multiple of 4.
+template <bool VEC4>
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(TopkParams p) {
-  __shared__ uint32_t s_wave[kSelWaves];
+  __shared__ uint32_t s_wave[2 * kSelWaves];
   __shared__ uint32_t s_res[2];
-  __shared__ uint32_t s_sub[kHistBins];
-  __shared__ uint2 s_binbuf[kBinBuf + 1];
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const int bt = blockIdx.y, b = bt / p.T, t = bt % p.T;
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
-  const int64_t vis = max((int64_t)0, (int64_t)len - p.T + 1 + t);
   const int K = p.K;
-  int32_t* out = p.topk_idx + (int64_t)bt * K;
   const int64_t c_lo = (int64_t)c * p.chunk;
-  const int64_t c_hi = min(c_lo + p.chunk, vis);
-  if (vis <= K) {  // every visible position is selected; nobody reads the counters
-    write_all_visible(out, c_lo, c_hi, vis, K, c, p.topk_count ? p.topk_count + bt : nullptr);
-    if (c == 0) clear_query_counters(p, bt, kSelThreads);
+  const int64_t c_end = min(c_lo + (int64_t)p.chunk, p.Lmax);  // loads stay inside the query's row
+  const float* row = p.scores + (int64_t)bt * p.Lmax;
+  constexpr int kRound = kSelThreads * kSelV;
+
+  // every load that depends on no other: length, histogram slice, first round of scores
+  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  BinSlice<kHistBins> hs;
+  load_bin_slice<kHistBins>(p.hist + (int64_t)bt * kHistBins, hs);
+  float v[kSelV];
+  load_scores<VEC4>(row, c_lo + (int64_t)tid * kSelV, c_end, v);
+
+  const int64_t vis = max((int64_t)0, (int64_t)len - p.T + 1 + t);
+  int32_t* out = p.topk_idx + (int64_t)bt * K;
+  const int64_t c_hi = min(c_end, vis);
+  if (vis <= K) {  // every visible position is selected; the histogram has no other reader
+    write_all_visible(out, c_lo, min(c_lo + (int64_t)p.chunk, vis), vis, K, c,
+                      p.topk_count ? p.topk_count + bt : nullptr);
+    if (c == 0) clear_query_hist(p, bt, kSelThreads);
     return;
   }
   if (c_lo >= c_hi) return;  // beyond this query's visible range
 
-  for (int i = tid; i < kHistBins; i += kSelThreads) s_sub[i] = 0;
   uint32_t bin, above;
-  find_threshold_bin<kHistBins>(p.hist + (int64_t)bt * kHistBins, (uint32_t)K, s_wave, s_res, &bin, &above);
+  threshold_from_slice<kHistBins>(hs, (uint32_t)K, s_wave, s_res, &bin, &above);
   if (c == 0 && tid == 0) p.header[bt] = make_uint2(bin, above);
 
-  const float* row = p.scores + (int64_t)bt * p.Lmax;
   uint2* cand = p.cand + (int64_t)bt * p.Lmax + c_lo;
-  const bool vec_ok = (((uintptr_t)(row + c_lo)) & 15) == 0;
+  uint32_t* blst = p.bin_keys + (int64_t)bt * bin_key_stride(p.Lmax) + c_lo;
   uint32_t n_out = 0, n_bin = 0;
-  for (int64_t base = c_lo; base < c_hi; base += kSelThreads * kSelV) {
+  for (int64_t base = c_lo; base < c_hi; base += kRound) {
     const int64_t s0 = base + (int64_t)tid * kSelV;
-    float v[kSelV];
-    if (vec_ok && s0 + kSelV <= c_hi) {
-#pragma unroll
-      for (int j = 0; j < kSelV; j += 4) {
-        const f32x4 x = *(const f32x4*)(row + s0 + j);
-        v[j] = x[0];
-        v[j + 1] = x[1];
-        v[j + 2] = x[2];
-        v[j + 3] = x[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kSelV; ++j) v[j] = (s0 + j < c_hi) ? row[s0 + j] : 0.0f;
-    }
-    bool f[kSelV], fb[kSelV];
+    const bool more = base + kRound < c_hi;
+    float nx[kSelV];
+    if (more) load_scores<VEC4>(row, s0 + kRound, c_end, nx);
     uint32_t key[kSelV];
+    uint32_t cnt[2] = {0u, 0u}, tot[2];  // entries with bin >= B, with bin == B
 #pragma unroll
     for (int j = 0; j < kSelV; ++j) {
       key[j] = score_key(v[j]);
       const uint32_t kb = key[j] >> kHistShift;
-      f[j] = (s0 + j < c_hi) && (kb >= bin);
-      fb[j] = (s0 + j < c_hi) && (kb == bin);
-      if (fb[j]) atomicAdd(&s_sub[(key[j] >> 8) & 0xFFFu], 1u);
+      const bool in = s0 + j < c_hi;
+      cnt[0] += (in && kb >= bin) ? 1u : 0u;
+      cnt[1] += (in && kb == bin) ? 1u : 0u;
     }
-    uint32_t total, total_b;
-    uint32_t off = n_out + block_prefix_flags<kSelV>(f, s_wave, &total);
-    uint32_t off_b = n_bin + block_prefix_flags<kSelV>(fb, s_wave, &total_b);
+    uint32_t inc[2] = {cnt[0], cnt[1]};
+    block_scan<2, kSelWaves>(inc, s_wave, tot);
+    uint32_t off = n_out + inc[0] - cnt[0], off_b = n_bin + inc[1] - cnt[1];
 #pragma unroll
     for (int j = 0; j < kSelV; ++j) {
-      if (f[j]) cand[off++] = make_uint2(key[j], (uint32_t)(s0 + j));
-      if (fb[j]) s_binbuf[min(off_b++, (uint32_t)kBinBuf)] = make_uint2(key[j], (uint32_t)(s0 + j));
+      const uint32_t kb = key[j] >> kHistShift;
+      const bool in = s0 + j < c_hi;
+      if (in && kb >= bin) cand[off++] = make_uint2(key[j], (uint32_t)(s0 + j));
+      if (in && kb == bin) blst[off_b++] = key[j];
     }
-    n_out += total;
-    n_bin += total_b;
+    n_out += tot[0];
+    n_bin += tot[1];
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < kSelV; ++j) v[j] = nx[j];
+    }
   }
   if (tid == 0) {
     p.chunk_cnt[(int64_t)bt * p.n_chunks + c] = n_out;
     p.chunk_above[(int64_t)bt * p.n_chunks + c] = n_out - n_bin;
-    // reserve this chunk's slots in the query's list of threshold-bin entries
-    s_res[0] = atomicAdd(&p.bin_count[bt], n_bin);
   }
-  __syncthreads();
-  {
-    uint2* dst = p.bin_list + (int64_t)bt * p.Lmax + s_res[0];
-    if (n_bin <= (uint32_t)kBinBuf) {
-      for (uint32_t j = tid; j < n_bin; j += kSelThreads) dst[j] = s_binbuf[j];
-    } else {  // more bin entries than the LDS buffer: copy them from the candidate list
-      // (this workgroup wrote cand; make its stores visible to all its waves first)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      uint32_t w = 0;
-      for (uint32_t j0 = 0; j0 < n_out; j0 += kSelThreads) {
-        const uint32_t j = j0 + tid;
-        const uint2 e = j < n_out ? cand[j] : make_uint2(0u, 0u);
-        bool fl[1] = {j < n_out && (e.x >> kHistShift) == bin};
-        uint32_t tot;
-        const uint32_t o = w + block_prefix_flags<1>(fl, s_wave, &tot);
-        if (fl[0]) dst[o] = e;
-        w += tot;
-      }
-    }
-  }
-  uint32_t* gsub = p.sub_hist + (int64_t)bt * kHistBins;
-  for (int i = tid; i < kHistBins; i += kSelThreads)
-    if (s_sub[i]) atomicAdd(&gsub[i], s_sub[i]);
 }
 
+// The emit step refines the threshold bin B with two more digits of 10 key
+// bits each (12 + 10 + 10 = 32).
+constexpr int kDigitBins = 1024;
+
 struct EmitShared {
-  uint32_t wave[kSelWaves];
-  uint32_t res[2];
-  uint32_t sub[256];
-  uint32_t key[kEmitCap];
-  uint32_t pos[kEmitCap];
+  uint32_t wave[2 * kSelWaves];
+  uint32_t res[3];                  // [2]: most bin-B entries in one chunk
+  uint32_t h2[kDigitBins];          // second digit of the bin-B keys
+  uint32_t h3[kDigitBins];          // third digit of the keys matching the first two
+  uint32_t boff[kMaxChunks + 1];    // bin-B entries in chunks before c' (chunk order)
+  uint32_t aoff[kMaxChunks + 1];    // entries above bin B in chunks before c'
+  uint32_t key[kEmitCap];           // the query's bin-B keys in chunk order
 };
 
 // Step 3: exact threshold, then this chunk's kept positions at their final slots.
-// Reads only contiguous data: the query's threshold-bin entries (unordered),
-// the per-chunk counts of entries above the bin, and this chunk's candidates.
+// Every load is issued before any is used: all chunks' counts, this chunk's
+// first kSelThreads * kEmitE candidates, and the first S (the largest power
+// of two with n_chunks * S <= kEmitFirst) bin-B keys of every chunk, read
+// speculatively four at a time inside their regions and masked afterwards;
+// a typical workgroup waits for memory once (a chunk with more than S bin-B
+// keys costs one more round per S).  The keys are gathered into LDS in chunk
+// order (key j of chunk c' at boff[c'] + j), so "the keys of chunks before
+// c" is an index range.  More than kEmitCap of them (heavy ties) are read
+// from global memory chunk by chunk instead.
+constexpr int kEmitG = 8;                           // speculative groups of 4 bin-B keys per thread
+constexpr int kEmitFirst = kSelThreads * kEmitG * 4;  // 8192
+constexpr int kEmitE = 8;                           // candidates per thread per round
+constexpr int kCntPer = kMaxChunks / kSelThreads;   // chunk counts per thread (chunks 4 tid + i)
+
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t emit_lds[];
   EmitShared& sh = *(EmitShared*)emit_lds;
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const int bt = blockIdx.y, b = bt / p.T, t = bt % p.T;
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
-  const int64_t vis = max((int64_t)0, (int64_t)len - p.T + 1 + t);
   const int K = p.K;
-  const int64_t c_lo = (int64_t)c * p.chunk;
+  const int nch = p.n_chunks;
+  const int64_t chunk = p.chunk;
+  const int64_t c_lo = (int64_t)c * chunk;
+  const int64_t c_len = min(chunk, p.Lmax - c_lo);  // this chunk's candidate slots
+  const int64_t kstride = bin_key_stride(p.Lmax);
+  const uint32_t* bkeys = p.bin_keys + (int64_t)bt * kstride;
+  const uint2* mine = p.cand + (int64_t)bt * p.Lmax + c_lo;
+  const uint32_t* ccnt = p.chunk_cnt + (int64_t)bt * nch;
+  const uint32_t* cabv = p.chunk_above + (int64_t)bt * nch;
+  int log_s = 2;  // S = 2^log_s speculative slots per chunk (>= 8: n_chunks <= 1024)
+  while ((nch << (log_s + 1)) <= kEmitFirst) ++log_s;
+  const uint32_t S = 1u << log_s;
+  // keys j .. j+3 of chunk cc (j % 4 == 0), clamped into the query's row
+  auto keys4 = [&](int cc, uint32_t j) -> uint4 {
+    return *(const uint4*)(bkeys + min((int64_t)min(cc, nch - 1) * chunk + j, kstride - 4));
+  };
+
+  // ---- loads ----
+  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const uint2 hdr = p.header[bt];
+  const uint32_t n_mine = ccnt[c];
+  uint32_t cn[kCntPer], ca[kCntPer];
+#pragma unroll
+  for (int i = 0; i < kCntPer; ++i) {
+    const int cc = min(kCntPer * tid + i, nch - 1);
+    cn[i] = ccnt[cc];
+    ca[i] = cabv[cc];
+  }
+  // group g = tid + 256 i holds slots 4g .. 4g+3; slot sl = key sl % S of chunk sl / S
+  uint4 bk[kEmitG];
+#pragma unroll
+  for (int i = 0; i < kEmitG; ++i) {
+    const int sl = 4 * (tid + i * kSelThreads);
+    bk[i] = keys4(sl >> log_s, sl & (S - 1));
+  }
+  uint2 e[kEmitE];  // candidates kEmitE tid + i of the current round
+#pragma unroll
+  for (int i = 0; i < kEmitE; ++i) e[i] = mine[min((int64_t)(kEmitE * tid + i), c_len - 1)];
+
+  const int64_t vis = max((int64_t)0, (int64_t)len - p.T + 1 + t);
   if (vis <= K || c_lo >= vis) return;
   int32_t* out = p.topk_idx + (int64_t)bt * K;
-
-  const uint2 hdr = p.header[bt];
+  const int n_act = (int)((vis + chunk - 1) / chunk);  // chunks that ran step 2
   const uint32_t bin = hdr.x, need = (uint32_t)K - hdr.y;  // entries to take from bin `bin`
-  const uint32_t M = p.bin_count[bt];
-  const uint2* blist = p.bin_list + (int64_t)bt * p.Lmax;
-  // entries above the bin in chunks before this one
-  uint32_t ab = 0;
-  for (int cc = tid; cc < c; cc += kSelThreads) ab += p.chunk_above[(int64_t)bt * p.n_chunks + cc];
-  uint32_t above_before;
-  block_incl_scan(ab, sh.wave, &above_before);
 
-  uint32_t bin2, above2;
-  find_threshold_bin<kHistBins>(p.sub_hist + (int64_t)bt * kHistBins, need, sh.wave, sh.res, &bin2, &above2);
-  const uint32_t need2 = need - above2;
-  const uint32_t prefix24 = (bin << 12) | bin2;
-
+  // ---- chunk-order offsets of the bin-B keys and of the entries above ----
+  for (int i = tid; i < kDigitBins; i += kSelThreads) {
+    sh.h2[i] = 0;
+    sh.h3[i] = 0;
+  }
+  if (tid == 0) sh.res[2] = 0;
+  uint32_t nb[kCntPer], na[kCntPer];
+  uint32_t sums[2] = {0u, 0u}, tot[2], nb_max = 0;
+#pragma unroll
+  for (int i = 0; i < kCntPer; ++i) {
+    const bool act = kCntPer * tid + i < n_act;
+    nb[i] = act ? cn[i] - ca[i] : 0u;
+    na[i] = act ? ca[i] : 0u;
+    sums[0] += nb[i];
+    sums[1] += na[i];
+    nb_max = max(nb_max, nb[i]);
+  }
+  const uint32_t own[2] = {sums[0], sums[1]};
+  block_scan<2, kSelWaves>(sums, sh.wave, tot);  // (its barriers also cover the clearing above)
+  {
+    uint32_t xb = sums[0] - own[0], xa = sums[1] - own[1];
+#pragma unroll
+    for (int i = 0; i < kCntPer; ++i) {
+      const int cc = kCntPer * tid + i;
+      if (cc <= nch) {
+        sh.boff[cc] = xb;
+        sh.aoff[cc] = xa;
+      }
+      xb += nb[i];
+      xa += na[i];
+    }
+    if (tid == 0) {  // n_chunks == kMaxChunks: the closing offsets
+      sh.boff[kMaxChunks] = tot[0];
+      sh.aoff[kMaxChunks] = tot[1];
+    }
+    if (nb_max > 0) atomicMax(&sh.res[2], nb_max);
+  }
+  __syncthreads();
+  const uint32_t M = tot[0];
+  const uint32_t above_before = sh.aoff[c];
+  const uint32_t max_per_chunk = sh.res[2];
   const bool in_lds = M <= (uint32_t)kEmitCap;
+
+  // ---- bin-B keys into LDS (chunk order) with their second digit counted ----
   if (in_lds) {
-    for (uint32_t n = tid; n < M; n += kSelThreads) {
-      const uint2 e = blist[n];
-      sh.key[n] = e.x;
-      sh.pos[n] = e.y;
-    }
-  }
-  for (int i = tid; i < 256; i += kSelThreads) sh.sub[i] = 0;
-  __syncthreads();
-  auto key_at = [&](uint32_t n) -> uint32_t { return in_lds ? sh.key[n] : blist[n].x; };
-  auto pos_at = [&](uint32_t n) -> uint32_t { return in_lds ? sh.pos[n] : blist[n].y; };
-
-  // last 8 key bits -> exact K-th key tau
-  for (uint32_t n = tid; n < M; n += kSelThreads) {
-    const uint32_t k = key_at(n);
-    if ((k >> 8) == prefix24) atomicAdd(&sh.sub[k & 0xFFu], 1u);
-  }
-  __syncthreads();
-  uint32_t bin3, above3;
-  find_threshold_bin<256>(sh.sub, need2, sh.wave, sh.res, &bin3, &above3);
-  const uint32_t tau = (prefix24 << 8) | bin3;
-  const uint32_t take_ties = need2 - above3;  // ties at tau to keep, lowest positions first
-
-  // bin entries before this chunk: above tau, and equal to tau
-  uint32_t gt = 0, eq = 0;
-  for (uint32_t n = tid; n < M; n += kSelThreads) {
-    if (pos_at(n) < (uint32_t)c_lo) {
-      const uint32_t k = key_at(n);
-      gt += k > tau ? 1u : 0u;
-      eq += k == tau ? 1u : 0u;
-    }
-  }
-  uint32_t gt_bin_before, ties_before;
-  block_incl_scan(gt, sh.wave, &gt_bin_before);
-  block_incl_scan(eq, sh.wave, &ties_before);
-
-  // this chunk's candidates in order (E consecutive per thread)
-  const uint2* mine = p.cand + (int64_t)bt * p.Lmax + c_lo;
-  const uint32_t n_mine = p.chunk_cnt[(int64_t)bt * p.n_chunks + c];
-  constexpr int E = 8;
-  uint32_t gt_seen = above_before + gt_bin_before, ties_seen = ties_before;
-  for (uint32_t n0 = 0; n0 < n_mine; n0 += kSelThreads * E) {
-    const uint32_t nb = n0 + (uint32_t)tid * E;
-    uint2 e[E];
-    uint32_t g = 0, q = 0;
+    auto stage = [&](const uint4 (&k)[kEmitG], uint32_t j0) {
+      uint32_t o[kEmitG], n[kEmitG];  // all offset reads first (independent LDS loads)
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      e[i] = (nb + i < n_mine) ? mine[nb + i] : make_uint2(0u, 0u);
-      g += (nb + i < n_mine && e[i].x > tau) ? 1u : 0u;
-      q += (nb + i < n_mine && e[i].x == tau) ? 1u : 0u;
-    }
-    uint32_t q_tot, g_tot;
-    uint32_t rank = ties_seen + block_incl_scan(q, sh.wave, &q_tot) - q;
-    const uint32_t g_before = gt_seen + block_incl_scan(g, sh.wave, &g_tot) - g;
-    uint32_t o = g_before + min(rank, take_ties);
+      for (int i = 0; i < kEmitG; ++i) {
+        const int cc = min((4 * (tid + i * kSelThreads)) >> log_s, nch);
+        o[i] = sh.boff[cc];
+        n[i] = sh.boff[min(cc + 1, nch)] - o[i];
+      }
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      if (nb + i >= n_mine) break;
-      bool sel = e[i].x > tau;
-      if (e[i].x == tau) sel = rank++ < take_ties;
-      if (sel) {
-        if (o < (uint32_t)K) out[o] = (int32_t)e[i].y;
-        ++o;
+      for (int i = 0; i < kEmitG; ++i) {
+        const int sl = 4 * (tid + i * kSelThreads);
+        const bool act = (sl >> log_s) < n_act;
+        const uint32_t j = j0 + (sl & (S - 1));
+        const uint32_t kv[4] = {k[i].x, k[i].y, k[i].z, k[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (act && j + q < n[i]) {
+            sh.key[o[i] + j + q] = kv[q];
+            atomicAdd(&sh.h2[(kv[q] >> 10) & (kDigitBins - 1)], 1u);
+          }
+        }
+      }
+    };
+    stage(bk, 0);
+    for (uint32_t j0 = S; j0 < max_per_chunk; j0 += S) {  // chunks with more than S bin-B keys
+#pragma unroll
+      for (int i = 0; i < kEmitG; ++i) {
+        const int sl = 4 * (tid + i * kSelThreads);
+        bk[i] = keys4(sl >> log_s, j0 + (sl & (S - 1)));
+      }
+      stage(bk, j0);
+    }
+  } else {
+    for (int cc = 0; cc < n_act; ++cc) {
+      const uint32_t n = sh.boff[cc + 1] - sh.boff[cc];
+      for (uint32_t j = tid; j < n; j += kSelThreads)
+        atomicAdd(&sh.h2[(bkeys[(int64_t)cc * chunk + j] >> 10) & (kDigitBins - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  // calls f(key) for every bin-B key of chunks [0, c_stop)
+  auto for_each_key = [&](int c_stop, auto&& f) {
+    if (in_lds) {
+      const uint32_t n_end = sh.boff[c_stop];
+      for (uint32_t n = tid; n < n_end; n += kSelThreads) f(sh.key[n]);
+    } else {
+      for (int cc = 0; cc < c_stop; ++cc) {
+        const uint32_t n = sh.boff[cc + 1] - sh.boff[cc];
+        for (uint32_t j = tid; j < n; j += kSelThreads) f(bkeys[(int64_t)cc * chunk + j]);
       }
     }
-    gt_seen += g_tot;
-    ties_seen += q_tot;
-  }
-  if (c == 0 && tid == 0 && p.topk_count) p.topk_count[bt] = K;
+  };
 
-  // Arrival ticket, taken once every read of the query's counters by this
-  // workgroup has completed (the fence waits for them): the last chunk of
-  // the query clears them.  Nothing is published, so no cache write-back.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // second digit -> 22-bit prefix of the K-th key
+  uint32_t bin2, above2;
+  find_threshold_bin<kDigitBins>(sh.h2, need, sh.wave, sh.res, &bin2, &above2);
+  const uint32_t need2 = need - above2;
+  const uint32_t prefix22 = (bin << 10) | bin2;
+  // third digit -> exact K-th key tau
+  for_each_key(n_act, [&](uint32_t k) {
+    if ((k >> 10) == prefix22) atomicAdd(&sh.h3[k & (kDigitBins - 1)], 1u);
+  });
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t n_act = (uint32_t)((vis + p.chunk - 1) / p.chunk);
-    sh.res[0] = atomicAdd(&p.done[bt], 1u) + 1u == n_act ? 1u : 0u;
+  uint32_t bin3, above3;
+  find_threshold_bin<kDigitBins>(sh.h3, need2, sh.wave, sh.res, &bin3, &above3);
+  const uint32_t tau = (prefix22 << 10) | bin3;
+  const uint32_t take_ties = need2 - above3;  // ties at tau to keep, lowest positions first
+
+  // bin-B keys of the chunks before this one: above tau, and equal to tau
+  uint32_t ge[2] = {0u, 0u}, ge_tot[2];
+  for_each_key(c, [&](uint32_t k) {
+    ge[0] += k > tau ? 1u : 0u;
+    ge[1] += k == tau ? 1u : 0u;
+  });
+  block_scan<2, kSelWaves>(ge, sh.wave, ge_tot);
+
+  // this chunk's candidates in order (kEmitE consecutive per thread)
+  uint32_t gt_seen = above_before + ge_tot[0], ties_seen = ge_tot[1];
+  for (uint32_t n0 = 0; n0 < n_mine; n0 += kSelThreads * kEmitE) {
+    const uint32_t nbase = n0 + (uint32_t)tid * kEmitE;
+    if (n0 > 0) {
+#pragma unroll
+      for (int i = 0; i < kEmitE; ++i) e[i] = mine[min((int64_t)(nbase + i), c_len - 1)];
+    }
+    uint32_t qg[2] = {0u, 0u}, qg_tot[2];  // ties, keys above tau
+#pragma unroll
+    for (int i = 0; i < kEmitE; ++i) {
+      const bool in = nbase + i < n_mine;
+      qg[0] += (in && e[i].x == tau) ? 1u : 0u;
+      qg[1] += (in && e[i].x > tau) ? 1u : 0u;
+    }
+    uint32_t inc[2] = {qg[0], qg[1]};
+    block_scan<2, kSelWaves>(inc, sh.wave, qg_tot);
+    uint32_t rank = ties_seen + inc[0] - qg[0];
+    const uint32_t g_before = gt_seen + inc[1] - qg[1];
+    uint32_t o = g_before + min(rank, take_ties);
+#pragma unroll
+    for (int i = 0; i < kEmitE; ++i) {
+      const bool in = nbase + i < n_mine;
+      const bool tie = in && e[i].x == tau;
+      const bool sel = in && (e[i].x > tau || (tie && rank < take_ties));
+      rank += tie ? 1u : 0u;
+      if (sel && o < (uint32_t)K) out[o] = (int32_t)e[i].y;
+      o += sel ? 1u : 0u;
+    }
+    gt_seen += qg_tot[1];
+    ties_seen += qg_tot[0];
   }
-  __syncthreads();
-  if (sh.res[0]) clear_query_counters(p, bt, kSelThreads);
+  if (c == 0) {
+    if (tid == 0 && p.topk_count) p.topk_count[bt] = K;
+    clear_query_hist(p, bt, kSelThreads);  // step 2, its only reader, has finished
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -494,7 +643,7 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   if (vis <= K) {  // every visible position is selected
     for (int64_t s = tid; s < K; s += kRowThreads) out[s] = s < vis ? (int32_t)s : -1;
     if (tid == 0 && p.topk_count) p.topk_count[bt] = (int32_t)vis;
-    clear_query_counters(p, bt, kRowThreads);
+    clear_query_hist(p, bt, kRowThreads);
     return;
   }
 
@@ -502,7 +651,7 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   // cleared: this workgroup is their only reader)
   uint32_t bin, above;
   row_threshold_bin<kHistBins>(p.hist + (int64_t)bt * kHistBins, (uint32_t)K, sh.wave, sh.res, &bin, &above);
-  clear_query_counters(p, bt, kRowThreads);
+  clear_query_hist(p, bt, kRowThreads);
 
   // 2. one pass over the scores: candidates in position order into LDS
   const float* row = p.scores + (int64_t)bt * p.Lmax;
@@ -640,8 +789,14 @@ hipError_t launch_select(const TopkParams& p, hipStream_t stream) {
     return hipGetLastError();
   }
   dim3 grid((unsigned)p.n_chunks, (unsigned)(p.B * p.T));
-  hipLaunchKernelGGL(select_chunk_kernel, grid, dim3(kSelThreads), 0, stream, p);
+  if ((((uintptr_t)p.scores) & 15) == 0 && p.Lmax % 4 == 0)
+    hipLaunchKernelGGL(select_chunk_kernel<true>, grid, dim3(kSelThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(select_chunk_kernel<false>, grid, dim3(kSelThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)select_emit_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)sizeof(EmitShared));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kSelThreads), sizeof(EmitShared), stream, p);
   return hipGetLastError();

@@ -136,8 +136,8 @@ def test_workspace_counter_region_and_init_validation():
     lib = dsa.load_library()
     p = good_problem(batch=3, q_len=2)
     z = lib.dsa_workspace_zero_bytes(ctypes.byref(p))
-    # two 4096-bin histograms plus two counters per query, at the start of the workspace
-    assert z == 3 * 2 * (2 * 4096 * 4 + 2 * 4)
+    # one 4096-bin histogram per query, at the start of the workspace
+    assert z == 3 * 2 * 4096 * 4
     assert z < lib.dsa_topk_workspace_size(ctypes.byref(p)) <= lib.dsa_forward_workspace_size(ctypes.byref(p))
     assert lib.dsa_workspace_zero_bytes(None) == 0
     # argument checks happen before any HIP call
