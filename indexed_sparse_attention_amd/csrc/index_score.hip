@@ -127,6 +127,7 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
   __shared__ int64_t s_total;
   __shared__ int64_t s_wsum[kScoreWaves];
   __shared__ int64_t s_excl[kScoreThreads];
+  __shared__ int s_len[kScoreThreads];  // clamped length of each segment's sequence in the current chunk
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -174,6 +175,7 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
   for (int c0 = 0; c0 < n_seg && wg_first(chunk_base) <= wg; c0 += kScoreThreads) {
     const int n_here = min(kScoreThreads, n_seg - c0);
     const int64_t mine = tid < n_here ? seg_units(c0 + tid) : 0;
+    if (tid < n_here) s_len[tid] = clamp_len(p.seq_lens[(c0 + tid) / n_groups], p.Lmax);
     int64_t v = mine;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -206,17 +208,61 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
       // ---------------- one segment: sequence b, tokens t0 .. t0+TQ-1 ----------------
       const int b = seg / n_groups;
       const int t0 = (seg % n_groups) * TQ;
-      const int len = clamp_len(p.seq_lens[b], p.Lmax);
+      const int len = s_len[i];
       const int vis_last = len - p.T + 1 + min(t0 + TQ - 1, p.T - 1);  // >= 1 here
 
-      // index queries -> LDS (e4m3: quantised), then into registers
+      // The segment's 16-position sub-tiles go round-robin over its n_w
+      // waves (sub-tile iw + x n_w is this wave's x-th), so at any moment the
+      // waves read one contiguous window of consecutive 4 KB (bf16) tiles.
+      // A unit is 4 of a wave's sub-tiles: x = 4u .. 4u+3.
+      const int64_t n_sub = iw < 4 * seg_n ? (4 * seg_n - iw + n_w - 1) / n_w : 0;
+      const int n_units = (int)((n_sub + 3) / 4);
+      constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
+      const uint8_t* kseq = (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes;
+      const int last_row = len - 1;
+      auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
+
+      auto st_ptr = [&](int x) -> const void* {  // key row this lane loads for sub-tile x
+        int64_t pos = sub_pos(x) + lc;
+        if (pos > last_row) pos = last_row;
+        return kseq + pos * kRowBytes;
+      };
+
+      // Key tiles stream through a ring of NSLOT sub-tile register slots,
+      // filled first, before the queries are staged: the key stream starts
+      // as soon as the segment is known and its latency hides the staging.  The
+      // scores of RB units are kept in registers and stored together after
+      // each batch: on this target loads and stores share one completion
+      // counter, so any store inside the streaming loop would make every
+      // iteration wait for all loads in flight.
+      constexpr int RB = 8;
+      static_assert((4 * RB) % NSLOT == 0 && NSLOT % 4 == 0, "ring must tile the batch");
+      KeyTile<FP8> slot[NSLOT];
+#pragma unroll
+      for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], st_ptr(j), lg);
+
+      // head weights (used from the first unit on), then the index queries
+      // -> LDS (e4m3: quantised) -> registers
+      float w[TQ][4][4];
+#pragma unroll
+      for (int tq = 0; tq < TQ; ++tq) {
+        const float* wrow = p.head_w + ((int64_t)b * p.T + min(t0 + tq, p.T - 1)) * kHi;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[tq][ht][e] = wrow[ht * 16 + 4 * lg + e];
+      }
       for (int tq = 0; tq < TQ; ++tq) {
         const int t = min(t0 + tq, p.T - 1);
         const int64_t qoff = ((int64_t)b * p.T + t) * kHi * kDi;
         if constexpr (!FP8) {
+          constexpr int kVecs = kHi * kDi / 8 / kScoreThreads;  // 4 per thread, all loads issued first
           const i32x4* src = (const i32x4*)((const uint16_t*)p.q_idx + qoff);
-          for (int i = tid; i < kHi * kDi / 8; i += kScoreThreads)
-            ((i32x4*)(lds_q + tq * kQBytes))[i] = src[i];
+          i32x4 x[kVecs];
+#pragma unroll
+          for (int k = 0; k < kVecs; ++k) x[k] = src[tid + k * kScoreThreads];
+#pragma unroll
+          for (int k = 0; k < kVecs; ++k) ((i32x4*)(lds_q + tq * kQBytes))[tid + k * kScoreThreads] = x[k];
         } else {
           // 4 consecutive values per word; all loads issued before converting
           constexpr int kWords = kHi * kDi / 4 / kScoreThreads;  // 8 per thread
@@ -245,15 +291,10 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
       }
       __syncthreads();
       QRegs<TQ, FP8> q;
-      float w[TQ][4][4];
 #pragma unroll
       for (int tq = 0; tq < TQ; ++tq) {
-        const int t = min(t0 + tq, p.T - 1);
-        const float* wrow = p.head_w + ((int64_t)b * p.T + t) * kHi;
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[tq][ht][e] = wrow[ht * 16 + 4 * lg + e];
           const uint8_t* qrow = lds_q + tq * kQBytes + (ht * 16 + lc) * (kQBytes / kHi);
           if constexpr (!FP8) {
 #pragma unroll
@@ -265,34 +306,6 @@ __global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScorePa
           }
         }
       }
-
-      // The segment's 16-position sub-tiles go round-robin over its n_w
-      // waves (sub-tile iw + x n_w is this wave's x-th), so at any moment the
-      // waves read one contiguous window of consecutive 4 KB (bf16) tiles.
-      // A unit is 4 of a wave's sub-tiles: x = 4u .. 4u+3.
-      const int64_t n_sub = iw < 4 * seg_n ? (4 * seg_n - iw + n_w - 1) / n_w : 0;
-      const int n_units = (int)((n_sub + 3) / 4);
-      constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
-      const uint8_t* kseq = (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes;
-      const int last_row = len - 1;
-      auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
-
-      auto st_ptr = [&](int x) -> const void* {  // key row this lane loads for sub-tile x
-        int64_t pos = sub_pos(x) + lc;
-        if (pos > last_row) pos = last_row;
-        return kseq + pos * kRowBytes;
-      };
-
-      // Key tiles stream through a ring of NSLOT sub-tile register slots.  The
-      // scores of RB units are kept in registers and stored together after
-      // each batch: on this target loads and stores share one completion
-      // counter, so any store inside the streaming loop would make every
-      // iteration wait for all loads in flight.
-      constexpr int RB = 8;
-      static_assert((4 * RB) % NSLOT == 0 && NSLOT % 4 == 0, "ring must tile the batch");
-      KeyTile<FP8> slot[NSLOT];
-#pragma unroll
-      for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], st_ptr(j), lg);
 
       const bool upper = l >= 32, odd = (lg & 1) != 0;
       for (int u0 = 0; u0 < n_units; u0 += RB) {

@@ -116,14 +116,15 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
 // Matrix-core kernel: qk_dim 576, v_dim 512, 64 heads per workgroup, row tiles
 // of 64 selected rows staged in LDS once and read by every wave.
 //
-// Four waves, one per SIMD; wave w owns heads 16w .. 16w+15 of the group
-// completely: all 576 dims of the QK^T contraction and all 512 value columns
-// of PV, so no partial logits cross waves and the only barrier per tile is
-// the one that hands over an LDS tile buffer.  With one wave per SIMD the
-// wave may hold up to 512 registers: 72 for its queries and 128 accumulators.
-// Tiles of 64 rows amortise each tile's fixed costs (barrier, copy issue,
-// softmax reductions) over more rows and give 8 independent accumulation
-// chains for QK^T.
+// Four waves, one per SIMD (so a wave may hold up to 512 registers).  For
+// QK^T and the softmax, wave w owns heads 16w .. 16w+15 over all 576 dims
+// (its queries stay in registers).  For PV it owns value columns 128w ..
+// 128w+127 of all 64 heads: each wave then reads only its quarter of the
+// tile's value columns, and the probabilities of all heads (8 KB of bf16 per
+// tile) plus each head's rescale factor pass through LDS between the two
+// halves, behind one extra barrier.  Tiles of 64 rows amortise each tile's
+// fixed costs (barriers, copy issue, softmax reductions) over more rows and
+// give 8 independent accumulation chains for QK^T.
 //
 // Row tiles alternate between two LDS buffers: while tile t is computed, tile
 // t+1 is in flight.  A bf16 cache is copied global -> LDS directly
@@ -138,11 +139,12 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
 // QK^T is computed transposed, S^T[row, head], with the LDS row tile as MFMA
 // operand A and 16 query heads (registers) as operand B; in the 16x16
 // accumulator lane l holds head l%16 and rows 4*(l/16)+e of each 16-row
-// block.  Those probabilities are exactly the operand the PV product needs
-// for head l%16 (the PV k-slots are a fixed permutation of the tile's rows;
-// the V operand is read from LDS in the same order), so P never leaves
-// registers.  The V operand needs 8 rows at one column per lane; gfx950's LDS
-// transpose read (ds_read_b64_tr_b16) delivers that: within each 16-lane
+// block.  Those probabilities, in bf16, are exactly the B operand the PV
+// product needs for head l%16 (the PV k-slots are a fixed permutation of the
+// tile's rows; the V operand is read from LDS in the same order), so each
+// lane stores them as two 16-byte chunks and every wave reads the four head
+// blocks back.  The V operand needs 8 rows at one column per lane; gfx950's
+// LDS transpose read (ds_read_b64_tr_b16) delivers that: within each 16-lane
 // group, output lane j receives element j%4 of the 4-element segments
 // addressed by lanes j/4 + 4k, k < 4.  MFMA lane i of 16-row block mt uses
 // tile row perm(mt, i) = 16 mt + 2 (i%4) + (i/4)%2 + 8 (i/8).  Online softmax
@@ -158,8 +160,7 @@ constexpr int kBlocks = kTile / 16;                      // 16-row MFMA blocks p
 constexpr int kChunksPerRow = kDqk / 8;                  // 72 bf16 chunks of 16 bytes
 constexpr int kTileBytes = kTile * kChunksPerRow * 16;   // 72 KB
 constexpr int kKSteps = kDqk / 32;                       // 18 k-steps of 32 dims
-constexpr int kNTiles = kDv / 16;                        // 32 value tiles of 16 columns
-constexpr int kIdxCap = 2048;                            // most index entries of one split
+constexpr int kIdxCap = 1536;                            // most index entries of one split
 constexpr int kIdxPad = 3 * kTile;                       // the last tile's padding + 2 tiles read ahead
 constexpr float kSlack = 8.0f;                           // log2 headroom before the running max moves
 static_assert(kMlaWaves * 16 == kTile, "two 8-row groups of the tile per wave");
@@ -224,17 +225,19 @@ __device__ __forceinline__ void qk_issue(QkGroup& nxt, const uint32_t (&addr)[4]
       : "memory");
 }
 
-template <int G>
+// Issues group `nxt` (4 reads at addr + G KB), then waits until the reads
+// still outstanding are the last N (`done`, issued before, is complete).
+template <int G, int N>
 __device__ __forceinline__ void qk_issue_wait(QkGroup& nxt, QkGroup& done, const uint32_t (&addr)[4]) {
   asm volatile(
       "ds_read_b128 %0, %8 offset:%12\n"
       "ds_read_b128 %1, %9 offset:%12\n"
       "ds_read_b128 %2, %10 offset:%12\n"
       "ds_read_b128 %3, %11 offset:%12\n"
-      "s_waitcnt lgkmcnt(8)"
+      "s_waitcnt lgkmcnt(%13)"
       : "=&v"(nxt.r[0]), "=&v"(nxt.r[1]), "=&v"(nxt.r[2]), "=&v"(nxt.r[3]), "+v"(done.r[0]), "+v"(done.r[1]),
         "+v"(done.r[2]), "+v"(done.r[3])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024)
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(G * 1024), "i"(N)
       : "memory");
 }
 
@@ -282,9 +285,27 @@ __device__ __forceinline__ void tr_wait_last(TrGroup& prev) {
 
 struct MlaShared {
   uint8_t rows[2][kTileBytes];  // tile buffers (read only through inline asm)
+  uint8_t pt[kHeadsPerWG * kTile * 2];  // P of the current tile, bf16 [head][PV k-slot], 16-byte chunks swizzled
+  float hv[kHeadsPerWG];        // per head: rescale factor of the current tile, at the end 1 / sum
   int32_t idx[kIdxCap + kIdxPad];
   uint64_t vmask[(kIdxCap + kIdxPad) / kTile];  // bit r of word t: row r of tile t is a valid entry
 };
+static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS");
+
+// P in LDS: row = head of the workgroup (128 bytes = 64 k-slots), chunk c of
+// 8 k-slots stored at slot c ^ (head % 8) so that 16 lanes reading 16 heads'
+// same chunk hit distinct banks.
+__device__ __forceinline__ uint32_t pt_off(int head, int c) { return head * 128 + ((c ^ (head & 7)) << 4); }
+
+// LDS accesses that sit between the tile copies go through inline asm as
+// well: the compiler would make an ordinary LDS access wait for every copy
+// in flight.  The caller waits (lgkmcnt) before using or publishing them.
+__device__ __forceinline__ void lds_store16(uint32_t addr, bf16x8 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store4(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
 
 // Opens a tile of the copy pipeline: this wave's copies of the tile have
 // landed and its earlier LDS accesses are done, then the workgroup barrier.
@@ -322,6 +343,35 @@ __device__ __forceinline__ void tile_dma(uint8_t* dst, const MlaParams& p, const
                                        (__attribute__((address_space(3))) void*)(seg + 1024 * i), 16, 0, 0);
   }
 }
+
+// The same copy, issued one instruction at a time (k = 0 .. 17) between the
+// compute steps of the previous tile: a wave that issued all eighteen at once
+// would stall on the memory pipeline's back-pressure with its MFMA idle.
+// Without a next tile (!live) every lane reads the same 16 bytes (one
+// request per instruction, written to a buffer nobody reads): the issue stays
+// unconditional, and so the code stays one basic block.
+template <bool FP8>
+struct TileCopy {
+  const uint8_t* src[2];
+  uint8_t* seg[2];
+  __device__ __forceinline__ TileCopy(uint8_t* dst, const MlaParams& p, const int32_t (&pos)[2], int64_t seq_row0,
+                                      int wave, int l, bool live) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int rg = 2 * wave + g;
+      const int64_t row = seq_row0 + (live ? max(pos[g], 0) : 0);
+      const int cx = live ? ((l & 7) ^ (l >> 3) ^ rg) & 7 : 0;
+      src[g] = FP8 ? (const uint8_t*)p.kv + row * kDqk + (cx >> 1) * 16
+                   : (const uint8_t*)p.kv + row * (2 * kDqk) + cx * 16;
+      seg[g] = dst + rg * 9 * 1024;
+    }
+  }
+  __device__ __forceinline__ void issue(int k) const {
+    const int g = k / 9, i = k % 9;
+    __builtin_amdgcn_global_load_lds((const void*)(src[g] + (FP8 ? 64 : 128) * i),
+                                     (__attribute__((address_space(3))) void*)(seg[g] + 1024 * i), 16, 0, 0);
+  }
+};
 
 // e4m3 cache: expands, in place, the rows this wave copied: lane l takes row
 // 16w + l/4 (whose scale it holds) and raw chunks m = l%4 + 4k, k < 9.  The
@@ -426,22 +476,27 @@ void mla_mfma_kernel(MlaParams p) {
   for (int mt = 0; mt < kBlocks; ++mt)
 #pragma unroll
     for (int par = 0; par < 2; ++par) a_off[mt][par] = chunk_off(tile_row(mt, lc), 4 * par + lg);
-  uint32_t v_off[2][2][4];  // PV operand: [k-step][row half][n % 4], plus 1 KB per 4 value tiles
+  uint32_t v_off[2][2];  // PV operand, value tile 0: [k-step][row half]
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int n4 = 0; n4 < 4; ++n4)
-        v_off[kk][hh][n4] =
-            chunk_off(tile_row(2 * kk + hh, 4 * lg + (lc >> 2)), 2 * n4 + ((lc & 3) >> 1)) + 8 * (lc & 1);
+      v_off[kk][hh] = chunk_off(tile_row(2 * kk + hh, 4 * lg + (lc >> 2)), (lc & 3) >> 1) + 8 * (lc & 1);
 
-  f32x4 o[kNTiles];
+  // O^T accumulators of the PV product: this wave owns value columns
+  // 128 wave .. +128 of all 64 heads; o[hb][db] = columns 128 wave + 16 db +
+  // 4 lg .. +4 of head 16 hb + lc.
+  f32x4 o[4][8];
 #pragma unroll
-  for (int n = 0; n < kNTiles; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;  // for head h0 + lc
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;  // softmax state of head h0 + lc (this wave's QK heads)
+  const uint32_t pt_base = (uint32_t)(uintptr_t)sh.pt, hv_base = (uint32_t)(uintptr_t)sh.hv;
 
-  auto compute = [&](const uint8_t* rows, int j0) {
+  // dma(k), k = 0 .. 17, is called once after each QK^T step: it issues the
+  // next tile's copy instruction k.
+  auto compute = [&](const uint8_t* rows, int j0, auto&& dma) {
     const uint64_t vm = sh.vmask[j0 / kTile];  // read early: its latency hides behind QK^T
     const uint32_t base = (uint32_t)(uintptr_t)rows;
     // ---- S^T[64 rows x 16 heads] over all 576 dims: 8 accumulation chains ----
@@ -458,7 +513,7 @@ void mla_mfma_kernel(MlaParams p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int par = 0; par < 2; ++par) qaddr[h][2 * j + par] = base + a_off[2 * h + j][par];
-    QkGroup qg[3];
+    QkGroup qg[2];
     auto qk_group = [&](const QkGroup& cur, int g, int h) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -468,45 +523,63 @@ void mla_mfma_kernel(MlaParams p) {
                                                                       s[2 * h + j][par], 0, 0, 0);
     };
     static_assert(kKSteps == 18, "nine pairs of k-steps");
-    // 18 groups (g, h) in the order (0,0) (0,1) (1,0) ... (8,1), three in flight
+    // 18 groups n = (g, h) = (n/2, n%2) in the order (0,0) (0,1) (1,0) ... (8,1),
+    // the next one in flight while one is multiplied
     qk_issue<0>(qg[0], qaddr[0]);
-    qk_issue<0>(qg[1], qaddr[1]);
-    qk_issue_wait<1>(qg[2], qg[0], qaddr[0]);
+    qk_issue_wait<0, 4>(qg[1], qg[0], qaddr[1]);
     qk_group(qg[0], 0, 0);
-    qk_issue_wait<1>(qg[0], qg[1], qaddr[1]);
+    dma(0);
+    qk_issue_wait<1, 4>(qg[0], qg[1], qaddr[0]);
     qk_group(qg[1], 0, 1);
-    qk_issue_wait<2>(qg[1], qg[2], qaddr[0]);
-    qk_group(qg[2], 1, 0);
-    qk_issue_wait<2>(qg[2], qg[0], qaddr[1]);
-    qk_group(qg[0], 1, 1);
-    qk_issue_wait<3>(qg[0], qg[1], qaddr[0]);
-    qk_group(qg[1], 2, 0);
-    qk_issue_wait<3>(qg[1], qg[2], qaddr[1]);
-    qk_group(qg[2], 2, 1);
-    qk_issue_wait<4>(qg[2], qg[0], qaddr[0]);
+    dma(1);
+    qk_issue_wait<1, 4>(qg[1], qg[0], qaddr[1]);
+    qk_group(qg[0], 1, 0);
+    dma(2);
+    qk_issue_wait<2, 4>(qg[0], qg[1], qaddr[0]);
+    qk_group(qg[1], 1, 1);
+    dma(3);
+    qk_issue_wait<2, 4>(qg[1], qg[0], qaddr[1]);
+    qk_group(qg[0], 2, 0);
+    dma(4);
+    qk_issue_wait<3, 4>(qg[0], qg[1], qaddr[0]);
+    qk_group(qg[1], 2, 1);
+    dma(5);
+    qk_issue_wait<3, 4>(qg[1], qg[0], qaddr[1]);
     qk_group(qg[0], 3, 0);
-    qk_issue_wait<4>(qg[0], qg[1], qaddr[1]);
+    dma(6);
+    qk_issue_wait<4, 4>(qg[0], qg[1], qaddr[0]);
     qk_group(qg[1], 3, 1);
-    qk_issue_wait<5>(qg[1], qg[2], qaddr[0]);
-    qk_group(qg[2], 4, 0);
-    qk_issue_wait<5>(qg[2], qg[0], qaddr[1]);
-    qk_group(qg[0], 4, 1);
-    qk_issue_wait<6>(qg[0], qg[1], qaddr[0]);
-    qk_group(qg[1], 5, 0);
-    qk_issue_wait<6>(qg[1], qg[2], qaddr[1]);
-    qk_group(qg[2], 5, 1);
-    qk_issue_wait<7>(qg[2], qg[0], qaddr[0]);
+    dma(7);
+    qk_issue_wait<4, 4>(qg[1], qg[0], qaddr[1]);
+    qk_group(qg[0], 4, 0);
+    dma(8);
+    qk_issue_wait<5, 4>(qg[0], qg[1], qaddr[0]);
+    qk_group(qg[1], 4, 1);
+    dma(9);
+    qk_issue_wait<5, 4>(qg[1], qg[0], qaddr[1]);
+    qk_group(qg[0], 5, 0);
+    dma(10);
+    qk_issue_wait<6, 4>(qg[0], qg[1], qaddr[0]);
+    qk_group(qg[1], 5, 1);
+    dma(11);
+    qk_issue_wait<6, 4>(qg[1], qg[0], qaddr[1]);
     qk_group(qg[0], 6, 0);
-    qk_issue_wait<7>(qg[0], qg[1], qaddr[1]);
+    dma(12);
+    qk_issue_wait<7, 4>(qg[0], qg[1], qaddr[0]);
     qk_group(qg[1], 6, 1);
-    qk_issue_wait<8>(qg[1], qg[2], qaddr[0]);
-    qk_group(qg[2], 7, 0);
-    qk_issue_wait<8>(qg[2], qg[0], qaddr[1]);
-    qk_group(qg[0], 7, 1);
-    qk_wait<4>(qg[1]);
-    qk_group(qg[1], 8, 0);
-    qk_wait<0>(qg[2]);
-    qk_group(qg[2], 8, 1);
+    dma(13);
+    qk_issue_wait<7, 4>(qg[1], qg[0], qaddr[1]);
+    qk_group(qg[0], 7, 0);
+    dma(14);
+    qk_issue_wait<8, 4>(qg[0], qg[1], qaddr[0]);
+    qk_group(qg[1], 7, 1);
+    dma(15);
+    qk_issue_wait<8, 4>(qg[1], qg[0], qaddr[1]);
+    qk_group(qg[0], 8, 0);
+    dma(16);
+    qk_wait<0>(qg[1]);
+    qk_group(qg[1], 8, 1);
+    dma(17);
 
     // ---- online softmax for head h0 + lc over rows 4 lg + e of each block ----
     float z[kBlocks][4];
@@ -541,43 +614,52 @@ void mla_mfma_kernel(MlaParams p) {
     l_run = l_run * alpha + psum;
     m_run = m_new;
 
-    // rescale this lane's outputs (all of head h0 + lc) by alpha, only when
-    // some head of the wave moved its max past a nonzero O
-    if (__any(move && alpha != 0.0f)) {
+    // ---- hand P and the rescale factors to every wave ----
+    // P^T operand of k-step kk for head lc: k-slot 8 lg + j <-> row
+    // (j < 4 ? block 2kk row 4 lg + j : block 2kk+1 row 4 lg + j - 4), i.e.
+    // chunk 4 kk + lg of the head's P row.
+    {
+      const int hl = wave * kHeadsPerWave + lc;  // this lane's head within the workgroup
 #pragma unroll
-      for (int n = 0; n < kNTiles; ++n)
+      for (int kk = 0; kk < 2; ++kk) {
+        uint16_t pb[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[n][e] *= alpha;
+        for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[2 * kk + (j >> 2)][j & 3]);
+        lds_store16(pt_base + pt_off(hl, 4 * kk + lg), __builtin_bit_cast(bf16x8, pb));
+      }
+      if (lg == 0) lds_store4(hv_base + 4 * hl, alpha);
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // P and factors complete (copies may be in flight)
 
-    // P^T operands (B of O^T = V^T P^T), one per 32-row k-step kk: head lc,
-    // k-slot 8 lg + j <-> row (j < 4 ? block 2kk row 4 lg + j : block 2kk+1 row 4 lg + j - 4)
-    bf16x8 pa[2];
+    // ---- O^T[128 value columns x 64 heads] += V^T P^T ----
+    // Rescale factors of this lane's 4 heads 16 hb + lc.  Only heads whose
+    // reference max moved past a nonzero O need work (a factor of 0 meets an
+    // O that is still 0), which is rare after the first tiles.
+    float al[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint16_t pb[8];
+    for (int hb = 0; hb < 4; ++hb)
+      asm volatile("ds_read_b32 %0, %1" : "=&v"(al[hb]) : "v"(hv_base + 4 * (16 * hb + lc)) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(al[0]), "+v"(al[1]), "+v"(al[2]), "+v"(al[3])::"memory");
+    if (__any((al[0] != 1.0f && al[0] != 0.0f) || (al[1] != 1.0f && al[1] != 0.0f) ||
+              (al[2] != 1.0f && al[2] != 0.0f) || (al[3] != 1.0f && al[3] != 0.0f))) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[2 * kk + (j >> 2)][j & 3]);
-      pa[kk] = __builtin_bit_cast(bf16x8, pb);
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[hb][db][e] *= al[hb];
     }
-    // ---- O^T[512 value columns x 16 heads] += V^T P^T ----
-    // The accumulator is O transposed, so lane l holds 4 consecutive columns
-    // 16 n + 4 (l/16) .. +4 of head lc: rescaling and normalising need no
-    // lane exchange and the write-out is one vector store per value tile.
     // V^T operand (A) of k-step kk: k-slot 8 lg + k (k < 4) is tile row
     // tile_row(2kk, 4 lg + k), slot 8 lg + 4 + k is tile_row(2kk+1, 4 lg + k):
     // lane lc addresses row k = lc/4 of its group and columns 4 (lc%4) .. +4
-    // of the 16-column tile.
-    uint32_t taddr[2][8];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        taddr[kk][2 * k] = base + v_off[kk][0][k];
-        taddr[kk][2 * k + 1] = base + v_off[kk][1][k];
-      }
+    // of the 16-column tile.  This wave's value tiles 8 wave + db sit 2 wave
+    // KB (plus 1 KB per 4 tiles) past those of tiles 0 .. 3; within a KB the
+    // tiles' offsets differ in bits 5-6 only (the swizzle is an XOR), so
+    // tile n4's offset is that of tile 0 XOR 32 n4.
+    const uint32_t vbase = base + 2048 * wave;
     TrGroup grp[2];
-    auto pv_group = [&](const TrGroup& cur, int g, int kk) {
+    bf16x8 pbt[4];  // P^T operands of the current k-step, head blocks 0..3
+    auto pv_group = [&](const TrGroup& cur, int g) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const i16x4 lo = cur.r[2 * k], hi = cur.r[2 * k + 1];
@@ -585,66 +667,52 @@ void mla_mfma_kernel(MlaParams p) {
                                                                __builtin_bit_cast(int, (short2){lo[2], lo[3]}),
                                                                __builtin_bit_cast(int, (short2){hi[0], hi[1]}),
                                                                __builtin_bit_cast(int, (short2){hi[2], hi[3]})});
-        o[4 * g + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pa[kk], o[4 * g + k], 0, 0, 0);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[hb][4 * g + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pbt[hb], o[hb][4 * g + k], 0, 0, 0);
       }
     };
-    // 16 groups: k-step 0 then 1, value tiles 4 g .. 4 g + 3 each; one group in flight
-    tr_issue_wait<0>(grp[0], grp[1], taddr[0]);  // grp[1] is a dummy here
-    tr_issue_wait<1>(grp[1], grp[0], taddr[0]);
-    pv_group(grp[0], 0, 0);
-    tr_issue_wait<2>(grp[0], grp[1], taddr[0]);
-    pv_group(grp[1], 1, 0);
-    tr_issue_wait<3>(grp[1], grp[0], taddr[0]);
-    pv_group(grp[0], 2, 0);
-    tr_issue_wait<4>(grp[0], grp[1], taddr[0]);
-    pv_group(grp[1], 3, 0);
-    tr_issue_wait<5>(grp[1], grp[0], taddr[0]);
-    pv_group(grp[0], 4, 0);
-    tr_issue_wait<6>(grp[0], grp[1], taddr[0]);
-    pv_group(grp[1], 5, 0);
-    tr_issue_wait<7>(grp[1], grp[0], taddr[0]);
-    pv_group(grp[0], 6, 0);
-    tr_issue_wait<0>(grp[0], grp[1], taddr[1]);
-    pv_group(grp[1], 7, 0);
-    tr_issue_wait<1>(grp[1], grp[0], taddr[1]);
-    pv_group(grp[0], 0, 1);
-    tr_issue_wait<2>(grp[0], grp[1], taddr[1]);
-    pv_group(grp[1], 1, 1);
-    tr_issue_wait<3>(grp[1], grp[0], taddr[1]);
-    pv_group(grp[0], 2, 1);
-    tr_issue_wait<4>(grp[0], grp[1], taddr[1]);
-    pv_group(grp[1], 3, 1);
-    tr_issue_wait<5>(grp[1], grp[0], taddr[1]);
-    pv_group(grp[0], 4, 1);
-    tr_issue_wait<6>(grp[0], grp[1], taddr[1]);
-    pv_group(grp[1], 5, 1);
-    tr_issue_wait<7>(grp[1], grp[0], taddr[1]);
-    pv_group(grp[0], 6, 1);
-    tr_wait_last(grp[1]);
-    pv_group(grp[1], 7, 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t taddr[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        taddr[2 * k] = vbase + (v_off[kk][0] ^ (32 * k));
+        taddr[2 * k + 1] = vbase + (v_off[kk][1] ^ (32 * k));
+      }
+      // P^T of head block hb, k-step kk: head 16 hb + lc, chunk 4 kk + lg
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        asm volatile("ds_read_b128 %0, %1" : "=&v"(pbt[hb]) : "v"(pt_base + pt_off(16 * hb + lc, 4 * kk + lg)) : "memory");
+      tr_issue_wait<0>(grp[0], grp[1], taddr);  // (waits for the P^T reads; grp[1] is not live here)
+      tr_issue_wait<1>(grp[1], grp[0], taddr);
+      pv_group(grp[0], 0);
+      tr_wait_last(grp[1]);
+      pv_group(grp[1], 1);
+    }
   };
 
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // vmask complete (copies may be in flight)
   // One compact loop over the tiles (the body stays in the instruction
   // cache).  Tile t sits in buffer t % 2.  The rows this lane copies for
   // tile t are entries 64 t + 16 wave + l/8 (+8); they are read one tile
-  // ahead, so the copy is issued without an LDS round trip.  The copy of the
-  // padding tile past the end reads row 0 and is never computed.
+  // ahead, so the copy is issued without an LDS round trip.
   int32_t pos[2] = {s_idx[kTile + my_row], s_idx[kTile + my_row + 8]};
   int cur = 0;
   if constexpr (!FP8) {
     // Step t: wait for this wave's copy of tile t, barrier (tile t complete;
-    // every wave is done with tile t-1, whose buffer is reused), start
-    // copying tile t+1, compute tile t.
+    // every wave is done with tile t-1, whose buffer is reused), compute tile
+    // t while issuing the copy of tile t+1 step by step (a token copy after
+    // the last tile).
     for (int t = 0; t < n_tiles; ++t) {
       tile_barrier();
-      tile_dma<false>(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l);
+      const TileCopy<false> next(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l, t + 1 < n_tiles);
       pos[0] = s_idx[(t + 2) * kTile + my_row];
       pos[1] = s_idx[(t + 2) * kTile + my_row + 8];
-      compute(sh.rows[cur], t * kTile);
+      compute(sh.rows[cur], t * kTile, [&](int k) { next.issue(k); });
       cur ^= 1;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the padding tile's copy lands before exit
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the token copy lands before the LDS is reused
   } else {
     // Step t: barrier (every wave has decoded its rows of tile t and is done
     // with tile t-1), start copying tile t+1, compute tile t, then wait for
@@ -658,42 +726,58 @@ void mla_mfma_kernel(MlaParams p) {
       kscale = p.kv_scale[seq_row0 + max(s_idx[(t + 1) * kTile + srow], 0)];
       pos[0] = s_idx[(t + 2) * kTile + my_row];
       pos[1] = s_idx[(t + 2) * kTile + my_row + 8];
-      compute(sh.rows[cur], t * kTile);
+      compute(sh.rows[cur], t * kTile, [](int) {});
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       fp8_decode(sh.rows[cur ^ 1], kscale, wave, l);
       cur ^= 1;
     }
   }
 
-  // ---- write-out: lane l holds head h0 + lc, columns 16 n + 4 lg .. +4 ----
-  const int h = h0 + lc;
-  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  if (p.splits == 1) {
-    const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + 4 * lg;
-    if (p.out_dtype == kF32) {
-#pragma unroll
-      for (int n = 0; n < kNTiles; ++n)
-        *(f32x4*)((float*)p.out + ooff + 16 * n) = f32x4{o[n][0] * inv, o[n][1] * inv, o[n][2] * inv, o[n][3] * inv};
-    } else {
-#pragma unroll
-      for (int n = 0; n < kNTiles; ++n)
-        *(i32x2*)((uint16_t*)p.out + ooff + 16 * n) =
-            i32x2{(int)(f32_to_bf16_bits(o[n][0] * inv) | (f32_to_bf16_bits(o[n][1] * inv) << 16)),
-                  (int)(f32_to_bf16_bits(o[n][2] * inv) | (f32_to_bf16_bits(o[n][3] * inv) << 16))};
-    }
-    if (p.lse && lg == 0)
-      p.lse[(int64_t)bt * p.H + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
-  } else {
-    const int64_t slot = ((int64_t)split * p.B * p.T + bt) * p.H + h;
-    uint16_t* po = p.part_o + slot * kDv + 4 * lg;
-#pragma unroll
-    for (int n = 0; n < kNTiles; ++n)
-      *(i32x2*)(po + 16 * n) =
-          i32x2{(int)(f32_to_bf16_bits(o[n][0] * inv) | (f32_to_bf16_bits(o[n][1] * inv) << 16)),
-                (int)(f32_to_bf16_bits(o[n][2] * inv) | (f32_to_bf16_bits(o[n][3] * inv) << 16))};
-    if (lg == 0) {
+  // ---- write-out ----
+  // The owner wave of each head publishes 1 / sum (after every wave's last
+  // read of the rescale factors) and writes the head's statistics; lane l
+  // then holds columns 128 wave + 16 db + 4 lg .. +4 of heads 16 hb + lc.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (lg == 0) sh.hv[wave * kHeadsPerWave + lc] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  {
+    const int h = h0 + lc;
+    if (p.splits == 1) {
+      if (p.lse && lg == 0)
+        p.lse[(int64_t)bt * p.H + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+    } else if (lg == 0) {
+      const int64_t slot = ((int64_t)split * p.B * p.T + bt) * p.H + h;
       p.part_ml[slot * 2] = m_run;
       p.part_ml[slot * 2 + 1] = l_run;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int h = hg * kHeadsPerWG + 16 * hb + lc;
+    const float inv = sh.hv[16 * hb + lc];
+    const int col0 = 128 * wave + 4 * lg;
+    if (p.splits == 1) {
+      const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + col0;
+      if (p.out_dtype == kF32) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *(f32x4*)((float*)p.out + ooff + 16 * db) =
+              f32x4{o[hb][db][0] * inv, o[hb][db][1] * inv, o[hb][db][2] * inv, o[hb][db][3] * inv};
+      } else {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *(i32x2*)((uint16_t*)p.out + ooff + 16 * db) =
+              i32x2{(int)(f32_to_bf16_bits(o[hb][db][0] * inv) | (f32_to_bf16_bits(o[hb][db][1] * inv) << 16)),
+                    (int)(f32_to_bf16_bits(o[hb][db][2] * inv) | (f32_to_bf16_bits(o[hb][db][3] * inv) << 16))};
+      }
+    } else {
+      const int64_t slot = ((int64_t)split * p.B * p.T + bt) * p.H + h;
+      uint16_t* po = p.part_o + slot * kDv + col0;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *(i32x2*)(po + 16 * db) =
+            i32x2{(int)(f32_to_bf16_bits(o[hb][db][0] * inv) | (f32_to_bf16_bits(o[hb][db][1] * inv) << 16)),
+                  (int)(f32_to_bf16_bits(o[hb][db][2] * inv) | (f32_to_bf16_bits(o[hb][db][3] * inv) << 16))};
     }
   }
 }
