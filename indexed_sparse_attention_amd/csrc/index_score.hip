@@ -77,8 +77,6 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
 // dims 32 j .. +32 (e4m3, single k-step of 128).
 // ---------------------------------------------------------------------------
 constexpr int kHi = 64, kDi = 128;
-constexpr int kScoreThreads = 256;
-constexpr int kScoreWaves = kScoreThreads / kWave;
 
 template <bool FP8>
 struct KeyTile;
@@ -116,8 +114,9 @@ struct QRegs<TQ, true> {
   i32x8 a[TQ][4];  // [token][head tile], 32 e4m3 codes
 };
 
-template <int TQ, int NSLOT, bool FP8, int MINB>
-__global__ __launch_bounds__(kScoreThreads, MINB) void score_mfma_kernel(ScoreParams p) {
+template <int TQ, int NSLOT, bool FP8, int MINB, int NT>
+__global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
+  constexpr int kScoreThreads = NT, kScoreWaves = NT / kWave;
   // LDS: [TQ] index queries in operand order (bf16: 64 x 128 x 2 B; e4m3: 64 x 128 B),
   // then [TQ][kHistBins] histogram counters when p.hist.
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
@@ -422,11 +421,11 @@ bool score_mfma_supported(const ScoreParams& p) {
   return p.k_dtype == kE4M3;
 }
 
-template <int TQ, int NSLOT, bool FP8, int MINB = 2>
+template <int TQ, int NSLOT, bool FP8, int MINB = 2, int NT = 256>
 static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream) {
   constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
   const size_t lds = TQ * kQBytes + (p.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
-  hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB>), dim3(grid), dim3(kScoreThreads), lds, stream, p);
+  hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT>), dim3(grid), dim3(NT), lds, stream, p);
 }
 
 static int env_int(const char* name, int dflt) {
@@ -444,12 +443,13 @@ static int env_int(const char* name, int dflt) {
 hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream) {
   if (allow_mfma && score_mfma_supported(p)) {
     const int variant = env_int("DSA_SCORE_VARIANT", 0);
-    const int per_cu = (p.k_dtype == kBF16 && variant == 0) ? 2 : 1;
+    const int per_cu = (p.k_dtype == kBF16 && variant == 0) ? 2 : 1;  // variant 2: 8 waves, 1/CU
     int grid = max(1, env_int("DSA_SCORE_WGS_PER_CU", per_cu)) * num_cus;
     if (env_int("DSA_SCORE_WGS", 0) > 0) grid = env_int("DSA_SCORE_WGS", 0);
     if (p.k_dtype == kBF16) {
       switch (variant) {
         case 1: launch_mfma<1, 8, false, 1>(p, grid, stream); break;
+        case 2: launch_mfma<1, 4, false, 1, 512>(p, grid, stream); break;
         default: launch_mfma<1, 4, false, 2>(p, grid, stream); break;
       }
     } else if (p.T == 1) {
