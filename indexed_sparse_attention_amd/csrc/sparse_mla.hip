@@ -739,6 +739,7 @@ void mla_mfma_kernel(MlaParams p) {
   // then holds columns 128 wave + 16 db + 4 lg .. +4 of heads 16 hb + lc.
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (lg == 0) sh.hv[wave * kHeadsPerWave + lc] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   {
     const int h = h0 + lc;
     if (p.splits == 1) {
@@ -750,7 +751,6 @@ void mla_mfma_kernel(MlaParams p) {
       p.part_ml[slot * 2 + 1] = l_run;
     }
   }
-  __syncthreads();
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const int h = hg * kHeadsPerWG + 16 * hb + lc;
