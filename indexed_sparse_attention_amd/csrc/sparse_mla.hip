@@ -791,45 +791,48 @@ void mla_mfma_kernel(MlaParams p) {
 constexpr int kCombineBatch = 16;
 
 __global__ __launch_bounds__(64) void mla_combine_kernel(MlaParams p) {
-  __shared__ float s_w[kWave];
   const int h = blockIdx.x, bt = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t BT = (int64_t)p.B * p.T;
   const int64_t slot0 = (int64_t)bt * p.H + h;
   const int64_t slot_stride = BT * p.H;
-  float ms = -INFINITY, ls = 0.0f;
-  if (tid < p.splits) {
-    ms = p.part_ml[(slot0 + tid * slot_stride) * 2];
-    ls = p.part_ml[(slot0 + tid * slot_stride) * 2 + 1];
-  }
+  const int d = min(tid * 8, p.Dv - 8);  // this lane's 8 value columns (lanes past Dv repeat the last 8)
+  const uint16_t* po = p.part_o + slot0 * p.Dv + d;
+  const int64_t stride = slot_stride * p.Dv;
+  // The first batch of partials is loaded together with the statistics (the
+  // addresses do not depend on them), so the workgroup waits for memory once.
+  i32x4 v[kCombineBatch];
+#pragma unroll
+  for (int j = 0; j < kCombineBatch; ++j)  // splits past the end reread split 0 (weight 0)
+    v[j] = *(const i32x4*)(po + (j < p.splits ? j : 0) * stride);
+  const int sl = min(tid, p.splits - 1);
+  const float ms_raw = p.part_ml[(slot0 + sl * slot_stride) * 2];
+  const float ls_raw = p.part_ml[(slot0 + sl * slot_stride) * 2 + 1];
+  const float ms = tid < p.splits ? ms_raw : -INFINITY, ls = tid < p.splits ? ls_raw : 0.0f;
   const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
   const float wgt = (ls > 0.0f) ? ls * exp2f(ms - M) : 0.0f;
   const float L = wave_sum(wgt);
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  s_w[tid] = wgt * inv;
-  __syncthreads();
-  const int d = tid * 8;
-  if (d < p.Dv) {
-    float acc[8];
+  const float wn = L > 0.0f ? wgt / L : 0.0f;  // lane s: normalised weight of split s
+  float acc[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-    const uint16_t* po = p.part_o + slot0 * p.Dv + d;
-    const int64_t stride = slot_stride * p.Dv;
-    for (int s0 = 0; s0 < p.splits; s0 += kCombineBatch) {
-      i32x4 v[kCombineBatch];
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+  for (int s0 = 0; s0 < p.splits; s0 += kCombineBatch) {
+    if (s0 > 0) {
 #pragma unroll
-      for (int j = 0; j < kCombineBatch; ++j)  // splits past the end reread split s0 (weight 0)
+      for (int j = 0; j < kCombineBatch; ++j)
         v[j] = *(const i32x4*)(po + (s0 + j < p.splits ? s0 + j : s0) * stride);
+    }
 #pragma unroll
-      for (int j = 0; j < kCombineBatch; ++j) {
-        const float w = s0 + j < p.splits ? s_w[s0 + j] : 0.0f;
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const float w = s0 + j < p.splits ? __shfl(wn, s0 + j, kWave) : 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[2 * k] = fmaf(bf16_bits_to_f32((uint32_t)v[j][k] & 0xFFFFu), w, acc[2 * k]);
-          acc[2 * k + 1] = fmaf(bf16_bits_to_f32((uint32_t)v[j][k] >> 16), w, acc[2 * k + 1]);
-        }
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = fmaf(bf16_bits_to_f32((uint32_t)v[j][k] & 0xFFFFu), w, acc[2 * k]);
+        acc[2 * k + 1] = fmaf(bf16_bits_to_f32((uint32_t)v[j][k] >> 16), w, acc[2 * k + 1]);
       }
     }
+  }
+  if (tid * 8 < p.Dv) {
     const int64_t ooff = slot0 * p.Dv + d;
     if (p.out_dtype == kF32) {
       *(f32x4*)((float*)p.out + ooff) = f32x4{acc[0], acc[1], acc[2], acc[3]};
