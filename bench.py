@@ -327,7 +327,7 @@ def main():
     line = {
         "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.idx_key_dtype == synth.BF16 else "fp8-e4m3/bf16",
+        "vs_baseline": None, "dtype": {synth.F32: "f32", synth.BF16: "bf16"}.get(w.idx_key_dtype, "fp8-e4m3/bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_len": T, "max_seq_len": w.max_seq_len,
                    "mean_len": float(np.mean(w.seq_lens)), "top_k": w.top_k,
