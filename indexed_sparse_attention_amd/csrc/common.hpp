@@ -26,9 +26,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 
 // Round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);  // v_cvt_pk_bf16_f32: round to nearest even
+}
+
+// Two fp32 -> bf16 (round to nearest even) packed lo | hi << 16: one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, b2v));
 }
 
 // OCP E4M3 code -> f32 (exact).  s eeee mmm: e == 0 gives m * 2^-9, otherwise

@@ -622,10 +622,11 @@ void mla_mfma_kernel(MlaParams p) {
       const int hl = wave * kHeadsPerWave + lc;  // this lane's head within the workgroup
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        uint16_t pb[8];
+        uint32_t pw[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (uint16_t)f32_to_bf16_bits(pr[2 * kk + (j >> 2)][j & 3]);
-        lds_store16(pt_base + pt_off(hl, 4 * kk + lg), __builtin_bit_cast(bf16x8, pb));
+        for (int j = 0; j < 4; ++j)
+          pw[j] = pack_bf16x2(pr[2 * kk + (j >> 1)][2 * (j & 1)], pr[2 * kk + (j >> 1)][2 * (j & 1) + 1]);
+        lds_store16(pt_base + pt_off(hl, 4 * kk + lg), __builtin_bit_cast(bf16x8, pw));
       }
       if (lg == 0) lds_store4(hv_base + 4 * hl, alpha);
     }
@@ -767,8 +768,8 @@ void mla_mfma_kernel(MlaParams p) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
           *(i32x2*)((uint16_t*)p.out + ooff + 16 * db) =
-              i32x2{(int)(f32_to_bf16_bits(o[hb][db][0] * inv) | (f32_to_bf16_bits(o[hb][db][1] * inv) << 16)),
-                    (int)(f32_to_bf16_bits(o[hb][db][2] * inv) | (f32_to_bf16_bits(o[hb][db][3] * inv) << 16))};
+              i32x2{(int)pack_bf16x2(o[hb][db][0] * inv, o[hb][db][1] * inv),
+                    (int)pack_bf16x2(o[hb][db][2] * inv, o[hb][db][3] * inv)};
       }
     } else {
       const int64_t slot = ((int64_t)split * p.B * p.T + bt) * p.H + h;
@@ -776,8 +777,8 @@ void mla_mfma_kernel(MlaParams p) {
 #pragma unroll
       for (int db = 0; db < 8; ++db)
         *(i32x2*)(po + 16 * db) =
-            i32x2{(int)(f32_to_bf16_bits(o[hb][db][0] * inv) | (f32_to_bf16_bits(o[hb][db][1] * inv) << 16)),
-                  (int)(f32_to_bf16_bits(o[hb][db][2] * inv) | (f32_to_bf16_bits(o[hb][db][3] * inv) << 16))};
+            i32x2{(int)pack_bf16x2(o[hb][db][0] * inv, o[hb][db][1] * inv),
+                  (int)pack_bf16x2(o[hb][db][2] * inv, o[hb][db][3] * inv)};
     }
   }
 }
@@ -841,7 +842,7 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(MlaParams p) {
       i32x4 ob;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        ob[k] = (int)(f32_to_bf16_bits(acc[2 * k]) | (f32_to_bf16_bits(acc[2 * k + 1]) << 16));
+        ob[k] = (int)pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
       *(i32x4*)((uint16_t*)p.out + ooff) = ob;
     }
   }
