@@ -582,13 +582,15 @@ void mla_mfma_kernel(MlaParams p) {
     dma(17);
 
     // ---- online softmax for head h0 + lc over rows 4 lg + e of each block ----
+    // this lane's rows are tile_row(mt, 4 lg + e) = 16 mt + 2 e + (lg & 1) + 8 (lg >> 1)
+    const uint64_t vml = vm >> ((lg & 1) + 8 * (lg >> 1));
     float z[kBlocks][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < kBlocks; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool valid = (vm >> tile_row(mt, 4 * lg + e)) & 1u;
+        const bool valid = (vml >> (16 * mt + 2 * e)) & 1u;
         z[mt][e] = valid ? (s[mt][0][e] + s[mt][1][e]) * zscale : -INFINITY;
         tmax = fmaxf(tmax, z[mt][e]);
       }
@@ -600,14 +602,17 @@ void mla_mfma_kernel(MlaParams p) {
     // 128 accumulators; with a stable max that pass is skipped for the wave.
     const bool move = tmax > m_run + kSlack;
     const float m_new = move ? tmax : m_run;
-    const float alpha = move ? exp2f(m_run - m_new) : 1.0f;  // m_run = -inf gives 0
+    // v_exp_f32 directly: exp2(-inf) = 0, and results below 2^-126 (which
+    // cannot matter next to the reference max) may flush to 0
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // m_run = -inf gives 0
+    const float m_ref = m_new > -INFINITY ? m_new : 0.0f;  // no row valid yet: every z is -inf
     float psum = 0.0f;
     float pr[kBlocks][4];
 #pragma unroll
     for (int mt = 0; mt < kBlocks; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pr[mt][e] = z[mt][e] > -INFINITY ? exp2f(z[mt][e] - m_new) : 0.0f;  // m_new >= z when z is finite
+        pr[mt][e] = __builtin_amdgcn_exp2f(z[mt][e] - m_ref);  // m_ref >= z when z is finite
         psum += pr[mt][e];
       }
     psum = group4_sum(psum);
