@@ -648,12 +648,17 @@ void mla_mfma_kernel(MlaParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(al[0]), "+v"(al[1]), "+v"(al[2]), "+v"(al[3])::"memory");
     if (__any((al[0] != 1.0f && al[0] != 0.0f) || (al[1] != 1.0f && al[1] != 0.0f) ||
               (al[2] != 1.0f && al[2] != 0.0f) || (al[3] != 1.0f && al[3] != 0.0f))) {
+      // Each scaled accumulator goes back through an MFMA with zero operands
+      // (0 x 0 + C = C): the accumulators then leave this block, like the PV
+      // product, as MFMA results, and the compiler keeps them in the
+      // accumulation registers on every path instead of copying all 128 of
+      // them out and back every tile.
+      const bf16x8 zero = {};
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[hb][db][e] *= al[hb];
+          o[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero, zero, o[hb][db] * al[hb], 0, 0, 0);
     }
     // V^T operand (A) of k-step kk: k-slot 8 lg + k (k < 4) is tile row
     // tile_row(2kk, 4 lg + k), slot 8 lg + 4 + k is tile_row(2kk+1, 4 lg + k):
