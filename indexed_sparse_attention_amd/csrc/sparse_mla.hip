@@ -649,16 +649,21 @@ void mla_mfma_kernel(MlaParams p) {
     if (__any((al[0] != 1.0f && al[0] != 0.0f) || (al[1] != 1.0f && al[1] != 0.0f) ||
               (al[2] != 1.0f && al[2] != 0.0f) || (al[3] != 1.0f && al[3] != 0.0f))) {
       // Each scaled accumulator goes back through an MFMA with zero operands
-      // (0 x 0 + C = C): the accumulators then leave this block, like the PV
-      // product, as MFMA results, and the compiler keeps them in the
-      // accumulation registers on every path instead of copying all 128 of
-      // them out and back every tile.
+      // (0 x 0 + C = C), so it leaves this block, like the PV product, as an
+      // MFMA result and stays in the accumulation registers on both paths.
+      // The empty asm pins each accumulator's input to those registers
+      // inside this block: the copies to ordinary registers that the
+      // multiply needs are then made here, on the rare path, and not in the
+      // score phase of every tile.
       const bf16x8 zero = {};
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-          o[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero, zero, o[hb][db] * al[hb], 0, 0, 0);
+        for (int db = 0; db < 8; ++db) {
+          f32x4 acc = o[hb][db];
+          asm volatile("" : "+a"(acc));
+          o[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero, zero, acc * al[hb], 0, 0, 0);
+        }
     }
     // V^T operand (A) of k-step kk: k-slot 8 lg + k (k < 4) is tile row
     // tile_row(2kk, 4 lg + k), slot 8 lg + 4 + k is tile_row(2kk+1, 4 lg + k):
