@@ -159,6 +159,10 @@ constexpr int kTile = 64;
 constexpr int kBlocks = kTile / 16;                      // 16-row MFMA blocks per tile
 constexpr int kChunksPerRow = kDqk / 8;                  // 72 bf16 chunks of 16 bytes
 constexpr int kTileBytes = kTile * kChunksPerRow * 16;   // 72 KB
+// row stride of the output block staged in LDS at write-out: 32 B of padding
+// per 1 KB row spreads the sixteen rows one store instruction touches over
+// the banks
+constexpr int kStageRow = 2 * kDv + 32;
 constexpr int kKSteps = kDqk / 32;                       // 18 k-steps of 32 dims
 constexpr int kIdxCap = 1536;                            // most index entries of one split
 constexpr int kIdxPad = 3 * kTile;                       // the last tile's padding + 2 tiles read ahead
@@ -291,6 +295,7 @@ struct MlaShared {
   uint64_t vmask[(kIdxCap + kIdxPad) / kTile];  // bit r of word t: row r of tile t is a valid entry
 };
 static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS");
+static_assert(kHeadsPerWG * kStageRow <= kTileBytes, "write-out block fits in a tile buffer");
 
 // P in LDS: row = head of the workgroup (128 bytes = 64 k-slots), chunk c of
 // 8 k-slots stored at slot c ^ (head % 8) so that 16 lanes reading 16 heads'
@@ -767,34 +772,44 @@ void mla_mfma_kernel(MlaParams p) {
       p.part_ml[slot * 2 + 1] = l_run;
     }
   }
+  if (p.splits == 1 && p.out_dtype == kF32) {
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const int h = hg * kHeadsPerWG + 16 * hb + lc;
-    const float inv = sh.hv[16 * hb + lc];
-    const int col0 = 128 * wave + 4 * lg;
-    if (p.splits == 1) {
-      const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + col0;
-      if (p.out_dtype == kF32) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-          *(f32x4*)((float*)p.out + ooff + 16 * db) =
-              f32x4{o[hb][db][0] * inv, o[hb][db][1] * inv, o[hb][db][2] * inv, o[hb][db][3] * inv};
-      } else {
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-          *(i32x2*)((uint16_t*)p.out + ooff + 16 * db) =
-              i32x2{(int)pack_bf16x2(o[hb][db][0] * inv, o[hb][db][1] * inv),
-                    (int)pack_bf16x2(o[hb][db][2] * inv, o[hb][db][3] * inv)};
-      }
-    } else {
-      const int64_t slot = ((int64_t)split * p.B * p.T + bt) * p.H + h;
-      uint16_t* po = p.part_o + slot * kDv + col0;
+    for (int hb = 0; hb < 4; ++hb) {
+      const int h = hg * kHeadsPerWG + 16 * hb + lc;
+      const float inv = sh.hv[16 * hb + lc];
+      const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + 128 * wave + 4 * lg;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        *(i32x2*)(po + 16 * db) =
-            i32x2{(int)pack_bf16x2(o[hb][db][0] * inv, o[hb][db][1] * inv),
-                  (int)pack_bf16x2(o[hb][db][2] * inv, o[hb][db][3] * inv)};
+        *(f32x4*)((float*)p.out + ooff + 16 * db) =
+            f32x4{o[hb][db][0] * inv, o[hb][db][1] * inv, o[hb][db][2] * inv, o[hb][db][3] * inv};
     }
+    return;
+  }
+  // bf16 rows: the workgroup's 64 heads are 64 consecutive rows of Dv values
+  // in the output and in the split's partial alike, so the block is staged in
+  // LDS (the tile buffers are free now) and written back as whole rows, one
+  // 1 KB row per wave instruction.  Written straight from the accumulator
+  // layout, every store instruction would cover sixteen 32-byte pieces of
+  // sixteen rows.
+  uint8_t* stage = sh.rows[0];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int hl = 16 * hb + lc;
+    const float inv = sh.hv[hl];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *(i32x2*)(stage + hl * kStageRow + 2 * (128 * wave + 16 * db + 4 * lg)) =
+          i32x2{(int)pack_bf16x2(o[hb][db][0] * inv, o[hb][db][1] * inv),
+                (int)pack_bf16x2(o[hb][db][2] * inv, o[hb][db][3] * inv)};
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  uint16_t* dst = p.splits == 1
+                      ? (uint16_t*)p.out + ((int64_t)bt * p.H + hg * kHeadsPerWG) * kDv
+                      : p.part_o + (((int64_t)split * p.B * p.T + bt) * p.H + hg * kHeadsPerWG) * kDv;
+#pragma unroll
+  for (int r = 0; r < kHeadsPerWG / kMlaWaves; ++r) {
+    const int hl = kMlaWaves * r + wave;
+    *(i32x4*)(dst + (int64_t)hl * kDv + 8 * l) = *(const i32x4*)(stage + hl * kStageRow + 16 * l);
   }
 }
 
