@@ -89,16 +89,25 @@ struct KeyTile<true> {  // e4m3: one k-step of 128 dims, 32 bytes
   i32x8 v;
 };
 
+// Key rows are read through a buffer resource over the sequence's filled rows
+// (num_records = len x row bytes): a read at or past that bound returns zeros
+// without touching memory.  The ring reads ahead past a wave's last sub-tile
+// and its last sub-tile may run past the sequence's end; those reads cost
+// nothing this way, with no branch around the loads (a branch would make the
+// compiler wait for the whole ring at every use).
+constexpr uint32_t kNoRow = 0x80000000u;  // offset of a read that must not happen
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+
 template <bool FP8>
-__device__ __forceinline__ void load_key_tile(KeyTile<FP8>& kt, const void* base_row, int lg) {
-  if constexpr (!FP8) {
-    const bf16x8* r = (const bf16x8*)base_row;  // 128 bf16 = 16 x bf16x8
+__device__ __forceinline__ void load_key_tile(KeyTile<FP8>& kt, __amdgpu_buffer_rsrc_t rows, uint32_t row_off,
+                                              int lg) {
+  if constexpr (!FP8) {  // 128 bf16 = 16 x 16 B
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kt.v[ks] = __builtin_nontemporal_load(r + ks * 4 + lg);
-  } else {
-    const i32x4* r = (const i32x4*)base_row;  // 128 bytes = 8 x 16 B
-    i32x4 a = __builtin_nontemporal_load(r + 2 * lg);
-    i32x4 c = __builtin_nontemporal_load(r + 2 * lg + 1);
+    for (int ks = 0; ks < 4; ++ks)
+      kt.v[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 16 * (ks * 4 + lg), 0, 0));
+  } else {  // 128 bytes = 8 x 16 B
+    const i32x4 a = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 32 * lg, 0, 0));
+    const i32x4 c = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 32 * lg + 16, 0, 0));
     kt.v = i32x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
   }
 }
@@ -217,14 +226,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       const int64_t n_sub = iw < 4 * seg_n ? (4 * seg_n - iw + n_w - 1) / n_w : 0;
       const int n_units = (int)((n_sub + 3) / 4);
       constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
-      const uint8_t* kseq = (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes;
+      const __amdgpu_buffer_rsrc_t krows = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes), (short)0, len * kRowBytes, kBufferFlags);
       const int last_row = len - 1;
       auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
 
-      auto st_ptr = [&](int x) -> const void* {  // key row this lane loads for sub-tile x
-        int64_t pos = sub_pos(x) + lc;
-        if (pos > last_row) pos = last_row;
-        return kseq + pos * kRowBytes;
+      auto st_off = [&](int x) -> uint32_t {  // offset of the key row this lane loads for sub-tile x
+        const int64_t pos = sub_pos(x) + lc;
+        return (x < n_sub && pos < len) ? (uint32_t)(pos * kRowBytes) : kNoRow;
       };
 
       // Key tiles stream through a ring of NSLOT sub-tile register slots,
@@ -239,7 +248,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       KeyTile<FP8> slot[NSLOT];
       auto fill_ring = [&]() {
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], st_ptr(j), lg);
+        for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], krows, st_off(j), lg);
       };
 
       // head weights (used from the first unit on), then the index queries
@@ -360,8 +369,9 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                 part[tq][st] = sacc;
               }
             }
-            // refill this slot with the sub-tile NSLOT ahead (rows past the end are clamped)
-            load_key_tile<FP8>(slot[j], st_ptr(x + NSLOT), lg);
+            // refill this slot with the sub-tile NSLOT ahead (nothing is read
+            // past the wave's sub-tiles or the sequence's end)
+            load_key_tile<FP8>(slot[j], krows, st_off(x + NSLOT), lg);
           }
           if (live) {
             // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
@@ -417,6 +427,9 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 // ---------------------------------------------------------------------------
 bool score_mfma_supported(const ScoreParams& p) {
   if (p.Hi != kHi || p.Di != kDi) return false;
+  // key rows are addressed by 32-bit byte offsets within a sequence
+  const int64_t row_bytes = p.k_dtype == kBF16 ? 2 * kDi : kDi;
+  if ((int64_t)p.Lmax * row_bytes >= (int64_t)kNoRow) return false;
   if (p.k_dtype == kBF16) return p.q_dtype == kBF16;
   return p.k_dtype == kE4M3;
 }
