@@ -145,16 +145,22 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   const int n_groups = (p.T + TQ - 1) / TQ;
   const int n_seg = p.B * n_groups;
 
-  auto seg_units = [&](int seg) -> int64_t {
-    const int b = seg / n_groups, g = seg % n_groups;
+  auto seg_units_len = [&](int seg, int len) -> int64_t {
+    const int g = seg % n_groups;
     const int t_last = min(g * TQ + TQ - 1, p.T - 1);
-    const int64_t vis_end = (int64_t)clamp_len(p.seq_lens[b], p.Lmax) - p.T + 1 + t_last;
+    const int64_t vis_end = (int64_t)len - p.T + 1 + t_last;
     return vis_end > 0 ? (vis_end + 63) / 64 : 0;
   };
+  auto seg_units = [&](int seg) -> int64_t {
+    return seg_units_len(seg, clamp_len(p.seq_lens[seg / n_groups], p.Lmax));
+  };
 
-  // Pass 1: total units.
-  int64_t acc = 0;
-  for (int s = tid; s < n_seg; s += kScoreThreads) acc += seg_units(s);
+  // Pass 1: total units.  Segment tid's length and units are kept for the
+  // first chunk of pass 2, which then starts without another memory round trip.
+  const int len0 = tid < n_seg ? clamp_len(p.seq_lens[tid / n_groups], p.Lmax) : 0;
+  const int64_t units0 = tid < n_seg ? seg_units_len(tid, len0) : 0;
+  int64_t acc = units0;
+  for (int s = tid + kScoreThreads; s < n_seg; s += kScoreThreads) acc += seg_units(s);
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
   if (l == 0) s_wsum[wave] = acc;
   __syncthreads();
@@ -182,8 +188,8 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   int64_t chunk_base = 0;
   for (int c0 = 0; c0 < n_seg && wg_first(chunk_base) <= wg; c0 += kScoreThreads) {
     const int n_here = min(kScoreThreads, n_seg - c0);
-    const int64_t mine = tid < n_here ? seg_units(c0 + tid) : 0;
-    if (tid < n_here) s_len[tid] = clamp_len(p.seq_lens[(c0 + tid) / n_groups], p.Lmax);
+    const int64_t mine = tid < n_here ? (c0 == 0 ? units0 : seg_units(c0 + tid)) : 0;
+    if (tid < n_here) s_len[tid] = c0 == 0 ? len0 : clamp_len(p.seq_lens[(c0 + tid) / n_groups], p.Lmax);
     int64_t v = mine;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
