@@ -733,7 +733,9 @@ void mla_mfma_kernel(MlaParams p) {
       compute(sh.rows[cur], t * kTile, [&](int k) { next.issue(k); });
       cur ^= 1;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the token copy lands before the LDS is reused
+    // the token copy after the last tile is still in flight into rows[cur]:
+    // the write-out stages its block in the other buffer and waits for the
+    // copy only at the very end
   } else {
     // Step t: barrier (every wave has decoded its rows of tile t and is done
     // with tile t-1), start copying tile t+1, compute tile t, then wait for
@@ -783,15 +785,16 @@ void mla_mfma_kernel(MlaParams p) {
         *(f32x4*)((float*)p.out + ooff + 16 * db) =
             f32x4{o[hb][db][0] * inv, o[hb][db][1] * inv, o[hb][db][2] * inv, o[hb][db][3] * inv};
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy into LDS outlives the workgroup
     return;
   }
   // bf16 rows: the workgroup's 64 heads are 64 consecutive rows of Dv values
   // in the output and in the split's partial alike, so the block is staged in
-  // LDS (the tile buffers are free now) and written back as whole rows, one
-  // 1 KB row per wave instruction.  Written straight from the accumulator
+  // LDS (in the last tile's buffer, free after the barrier above) and written
+  // back as whole rows, one 1 KB row per wave instruction.  Written straight from the accumulator
   // layout, every store instruction would cover sixteen 32-byte pieces of
   // sixteen rows.
-  uint8_t* stage = sh.rows[0];
+  uint8_t* stage = sh.rows[cur ^ 1];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const int hl = 16 * hb + lc;
@@ -811,6 +814,7 @@ void mla_mfma_kernel(MlaParams p) {
     const int hl = kMlaWaves * r + wave;
     *(i32x4*)(dst + (int64_t)hl * kDv + 8 * l) = *(const i32x4*)(stage + hl * kStageRow + 16 * l);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy into LDS outlives the workgroup
 }
 
 // Merge the per-split partials of one (query, head): split s holds its
