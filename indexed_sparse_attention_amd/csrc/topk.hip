@@ -192,6 +192,7 @@ __device__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s
 
 constexpr int kSelV = 16;          // consecutive positions per thread per step
 constexpr int kEmitCap = 10240;    // threshold-bin keys the emit step keeps in LDS
+static_assert(kEmitCap % 4 == 0, "keys are read four at a time");
 constexpr int kMaxChunks = 1024;   // chunks per query (the host sizes chunks to respect it)
 
 __device__ __forceinline__ void write_all_visible(int32_t* out, int64_t c_lo, int64_t c_hi, int64_t vis, int K,
@@ -326,7 +327,7 @@ struct EmitShared {
   uint32_t h3[kDigitBins];          // third digit of the keys matching the first two
   uint32_t boff[kMaxChunks + 1];    // bin-B entries in chunks before c' (chunk order)
   uint32_t aoff[kMaxChunks + 1];    // entries above bin B in chunks before c'
-  uint32_t key[kEmitCap];           // the query's bin-B keys in chunk order
+  alignas(16) uint32_t key[kEmitCap];  // the query's bin-B keys in chunk order
 };
 
 // Step 3: exact threshold, then this chunk's kept positions at their final slots.
@@ -483,9 +484,15 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) 
   __syncthreads();
   // calls f(key) for every bin-B key of chunks [0, c_stop)
   auto for_each_key = [&](int c_stop, auto&& f) {
-    if (in_lds) {
+    if (in_lds) {  // four keys per LDS read (kEmitCap is a multiple of 4)
       const uint32_t n_end = sh.boff[c_stop];
-      for (uint32_t n = tid; n < n_end; n += kSelThreads) f(sh.key[n]);
+      for (uint32_t n = 4 * tid; n < n_end; n += 4 * kSelThreads) {
+        const uint4 k4 = *(const uint4*)&sh.key[n];
+        f(k4.x);
+        if (n + 1 < n_end) f(k4.y);
+        if (n + 2 < n_end) f(k4.z);
+        if (n + 3 < n_end) f(k4.w);
+      }
     } else {
       for (int cc = 0; cc < c_stop; ++cc) {
         const uint32_t n = sh.boff[cc + 1] - sh.boff[cc];
