@@ -211,7 +211,9 @@ size_t dsa_forward_workspace_size(const dsa_problem* p);
  *                is recorded on `stream` just before the score kernel, and
  *                event i after
  *                stage i (1 = scores, 2 = Top-K, 3 = attention), for per-stage
- *                timing.
+ *                timing.  With the matrix-core score kernel, events 0 and 1
+ *                are taken by that kernel's dispatch at its own start and end,
+ *                so they time the kernel alone.
  */
 dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
                        const void* k_idx, const float* k_scale, const void* q, const void* kv,

@@ -452,17 +452,24 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
   };
 
   // the counters at the start of the workspace are zero on entry (and on return)
-  if ((st = rec(0)) != DSA_OK) return st;
-  // stage 1: scores (+ fused histogram when the matrix-core kernel runs)
+  // stage 1: scores (+ fused histogram when the matrix-core kernel runs, whose
+  // dispatch then takes events 0 and 1 at the kernel's own start and end)
   const bool mfma_score = score_uses_mfma(p);
   auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, sc, hist);
-  if (!mfma_score) sp.hist = nullptr;
-  if ((st = hip_check(dsa::launch_score(sp, mfma_score, num_cus(), s), "index score")) != DSA_OK) return st;
-  if (!mfma_score &&
-      (st = hip_check(dsa::launch_hist(sc, seq_lens, hist, p->batch, p->q_len, p->max_seq_len, s),
-                      "histogram")) != DSA_OK)
+  if (!mfma_score) {
+    sp.hist = nullptr;
+    if ((st = rec(0)) != DSA_OK) return st;
+  }
+  hipEvent_t ev0 = mfma_score && stage_events ? (hipEvent_t)stage_events[0] : nullptr;
+  hipEvent_t ev1 = mfma_score && stage_events ? (hipEvent_t)stage_events[1] : nullptr;
+  if ((st = hip_check(dsa::launch_score(sp, mfma_score, num_cus(), s, ev0, ev1), "index score")) != DSA_OK)
     return st;
-  if ((st = rec(1)) != DSA_OK) return st;
+  if (!mfma_score) {
+    if ((st = hip_check(dsa::launch_hist(sc, seq_lens, hist, p->batch, p->q_len, p->max_seq_len, s),
+                        "histogram")) != DSA_OK)
+      return st;
+    if ((st = rec(1)) != DSA_OK) return st;
+  }
   // stage 2: Top-K
   auto tp = topk_params(p, F.tk, w + F.off_topk, sc, seq_lens, idx, topk_count);
   if ((st = hip_check(dsa::launch_select(tp, s), "select")) != DSA_OK) return st;

@@ -8,6 +8,7 @@
 // the weights and the head sum applied to the accumulators in registers.  The
 // same pass builds the per-query histogram of the top 12 bits of each score's
 // order-preserving key, which the Top-K threshold search consumes.
+#include <hip/hip_ext.h>
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -441,10 +442,14 @@ bool score_mfma_supported(const ScoreParams& p) {
 }
 
 template <int TQ, int NSLOT, bool FP8, int MINB = 2, int NT = 256>
-static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream) {
+static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
   const size_t lds = TQ * kQBytes + (p.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
-  hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT>), dim3(grid), dim3(NT), lds, stream, p);
+  if (ev_start || ev_stop)  // events taken by the dispatch itself at the kernel's start and end
+    hipExtLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT>), dim3(grid), dim3(NT), lds, stream, ev_start,
+                          ev_stop, 0, p);
+  else
+    hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT>), dim3(grid), dim3(NT), lds, stream, p);
 }
 
 static int env_int(const char* name, int dflt) {
@@ -459,7 +464,8 @@ static int env_int(const char* name, int dflt) {
 // workgroups per CU and DSA_SCORE_WGS the total.  (Measured at the 128K
 // decode shape: variant 0 at 2/CU streams the keys about 4 % faster than
 // variant 1 at 1/CU.)
-hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream) {
+hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream, hipEvent_t ev_start,
+                        hipEvent_t ev_stop) {
   if (allow_mfma && score_mfma_supported(p)) {
     const int variant = env_int("DSA_SCORE_VARIANT", 0);
     const int per_cu = (p.k_dtype == kBF16 && variant == 0) ? 2 : 1;  // variant 2: 8 waves, 1/CU
@@ -467,14 +473,14 @@ hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipS
     if (env_int("DSA_SCORE_WGS", 0) > 0) grid = env_int("DSA_SCORE_WGS", 0);
     if (p.k_dtype == kBF16) {
       switch (variant) {
-        case 1: launch_mfma<1, 8, false, 1>(p, grid, stream); break;
-        case 2: launch_mfma<1, 4, false, 1, 512>(p, grid, stream); break;
-        default: launch_mfma<1, 4, false, 2>(p, grid, stream); break;
+        case 1: launch_mfma<1, 8, false, 1>(p, grid, stream, ev_start, ev_stop); break;
+        case 2: launch_mfma<1, 4, false, 1, 512>(p, grid, stream, ev_start, ev_stop); break;
+        default: launch_mfma<1, 4, false, 2>(p, grid, stream, ev_start, ev_stop); break;
       }
     } else if (p.T == 1) {
-      launch_mfma<1, 8, true>(p, grid, stream);
+      launch_mfma<1, 8, true>(p, grid, stream, ev_start, ev_stop);
     } else {
-      launch_mfma<2, 4, true>(p, grid, stream);
+      launch_mfma<2, 4, true>(p, grid, stream, ev_start, ev_stop);
     }
   } else {
     dim3 grid((unsigned)((p.Lmax + 255) / 256), (unsigned)(p.B * p.T));

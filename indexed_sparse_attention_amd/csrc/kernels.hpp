@@ -56,7 +56,10 @@ struct MlaParams {
 
 // index_score.hip
 bool score_mfma_supported(const ScoreParams& p);
-hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream);
+// With the matrix-core kernel, ev_start / ev_stop (either may be null) are
+// recorded by the dispatch itself at the kernel's start and end.
+hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream,
+                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // topk.hip
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
