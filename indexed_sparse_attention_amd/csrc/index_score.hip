@@ -223,7 +223,9 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       // ---------------- one segment: sequence b, tokens t0 .. t0+TQ-1 ----------------
       const int b = seg / n_groups;
       const int t0 = (seg % n_groups) * TQ;
-      const int len = s_len[i];
+      // (read back from LDS, so the compiler cannot tell it is uniform; the
+      // key buffer resource built from it must sit in scalar registers)
+      const int len = __builtin_amdgcn_readfirstlane(s_len[i]);
       const int vis_last = len - p.T + 1 + min(t0 + TQ - 1, p.T - 1);  // >= 1 here
 
       // The segment's 16-position sub-tiles go round-robin over its n_w
