@@ -470,7 +470,8 @@ hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipS
                         hipEvent_t ev_stop) {
   if (allow_mfma && score_mfma_supported(p)) {
     const int variant = env_int("DSA_SCORE_VARIANT", 0);
-    const int per_cu = (p.k_dtype == kBF16 && variant == 0) ? 2 : 1;  // variant 2: 8 waves, 1/CU
+    // two workgroups per CU (bf16 variants 1 and 2: one, with 8-deep rings or 8 waves)
+    const int per_cu = (p.k_dtype != kBF16 || variant == 0) ? 2 : 1;
     int grid = max(1, env_int("DSA_SCORE_WGS_PER_CU", per_cu)) * num_cus;
     if (env_int("DSA_SCORE_WGS", 0) > 0) grid = env_int("DSA_SCORE_WGS", 0);
     if (p.k_dtype == kBF16) {
