@@ -100,7 +100,11 @@ struct TopkLayout {
 TopkLayout topk_layout(const dsa_problem* p) {
   TopkLayout L;
   const int64_t BT = (int64_t)p->batch * p->q_len, Lmax = p->max_seq_len;
-  int64_t chunk = std::max<int64_t>(4096, (Lmax * BT + 2047) / 2048);
+  // about 512 (query, chunk) workgroups in all, two per CU: every emit
+  // workgroup resolves its query's threshold again, so more chunks than that
+  // only add redundant work (at 1M positions x 8 queries, 2048 chunks of 4096
+  // took twice as long as 512 of 16384)
+  int64_t chunk = std::max<int64_t>(4096, (Lmax * BT + 511) / 512);
   chunk = std::max<int64_t>(chunk, (Lmax + 1023) / 1024);  // at most 1024 chunks per query
   chunk = align_up(chunk, 1024);
   if (chunk > align_up(Lmax, 1024)) chunk = align_up(Lmax, 1024);
