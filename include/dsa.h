@@ -181,6 +181,9 @@ size_t dsa_sparse_mla_workspace_size(const dsa_problem* p);
  *   q        [B,T,H,Dqk]  q_dtype queries (already absorbed into the latent space).
  *   kv       [B,Lmax,Dqk] kv_dtype latent cache rows.
  *   kv_scale [B,Lmax]     fp32 positive per-row scale when kv is FP8, else NULL.
+ *                         A power of two (the per-token scales of the format)
+ *                         expands a row to bf16 exactly; any other value is
+ *                         applied in fp32 and the product rounded to bf16.
  *   topk_idx [B,T,K]      int32 rows to attend over; entries outside [0, len_b)
  *                         are ignored, so -1 padding is allowed.
  *   out      [B,T,H,Dv]   out_dtype output.  No valid entry: out = 0.

@@ -103,6 +103,21 @@ def test_fp8_generic_path_matches_oracle():
         del os.environ["DSA_FORCE_GENERIC"]
 
 
+def test_fp8_cache_scales_not_powers_of_two():
+    # The matrix-core path expands e4m3 rows with the hardware's scaled
+    # conversion, which takes only a scale's exponent; a row whose scale is
+    # not a power of two is converted unscaled and multiplied in fp32.  Half
+    # the rows (at random, so waves mix both kinds) get such a scale: the
+    # power of two times a factor in [0.55, 0.95], which keeps the values at
+    # most as large as the power-of-two rows' (the fp8 bound is absolute),
+    # while taking the exponent alone would be off by 10-45 %.
+    w = _case("fp8_1m", batch=2, max_seq_len=6000, len_range=(4000, 6000), top_k=512)
+    rng = np.random.default_rng(7)
+    factor = rng.uniform(0.55, 0.95, size=w.kv_scale.shape).astype(np.float32)
+    w.kv_scale[:] = np.where(rng.random(w.kv_scale.shape) < 0.5, w.kv_scale, w.kv_scale * factor)
+    _full_check(w)
+
+
 def test_edge_fewer_visible_than_k_and_empty():
     # sequence 0: 100 rows (< K), sequence 1: 0 rows (nothing visible), sequence 2: exactly Lmax
     w = _case("decode8k", batch=3, max_seq_len=1024, top_k=512)
