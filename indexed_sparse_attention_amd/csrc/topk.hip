@@ -32,12 +32,11 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace dsa {
 
-constexpr int kSelThreads = 256;
 constexpr int64_t kRowMaxLen = 262144;  // longest query range handled by one workgroup
-constexpr int kSelWaves = kSelThreads / kWave;
 
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -82,118 +81,7 @@ hipError_t launch_hist(const float* scores, const int32_t* seq_lens, uint32_t* h
   return hipGetLastError();
 }
 
-// --------------------------------------------------------------------------
-// block-wide helpers (256 threads = 4 waves)
-// --------------------------------------------------------------------------
-// Inclusive prefix sum over the 64 lanes of a wave with DPP adds: shifts by
-// 1, 2, 4, 8 within each 16-lane row, then the last lane of row 0 is added
-// to row 1 and row 2 to row 3 (row_bcast:15), and lane 31 to rows 2 and 3
-// (row_bcast:31).  Lanes without a source add 0.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
-
-// Inclusive prefix sums of N values per thread, in thread order, over a
-// workgroup of NW waves; total[i] gets the block total of value i.
-// s_wave: N * NW words of shared scratch.
-template <int N, int NW>
-__device__ __forceinline__ void block_scan(uint32_t (&v)[N], uint32_t* s_wave, uint32_t (&total)[N]) {
-  const int wave = threadIdx.x / kWave, l = lane_id();
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    v[i] = wave_incl_scan(v[i]);
-    if (l == kWave - 1) s_wave[i * NW + wave] = v[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t x = s_wave[i * NW + w];
-      if (w < wave) off += x;
-      tot += x;
-    }
-    v[i] += off;
-    total[i] = tot;
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
-  uint32_t a[1] = {v}, t[1];
-  block_scan<1, kSelWaves>(a, s_wave, t);
-  *total = t[0];
-  return a[0];
-}
-
-// Thread tid's share of an NB-bin histogram: the PER bins just below
-// NB - PER*tid, highest first.  Loading it is separate from the scan below so
-// that the loads can be in flight together with a kernel's other loads.
-template <int NB>
-struct BinSlice {
-  static constexpr int PER = NB / kSelThreads;
-  uint32_t c[PER];
-};
-
-template <int NB>
-__device__ __forceinline__ void load_bin_slice(const uint32_t* h, BinSlice<NB>& s) {
-  const int top = NB - 1 - BinSlice<NB>::PER * (int)threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < BinSlice<NB>::PER; ++i) s.c[i] = h[top - i];
-}
-
-// Largest bin B of the histogram whose suffix count sum_{i >= B} h[i]
-// reaches `need`; *above = sum_{i > B} h[i].  An inclusive scan of the
-// slices in thread order counts the entries at or above each thread's lowest
-// bin.  All threads get the result.
-template <int NB>
-__device__ void threshold_from_slice(const BinSlice<NB>& s, uint32_t need, uint32_t* s_wave, uint32_t* s_res,
-                                     uint32_t* bin, uint32_t* above) {
-  constexpr int PER = BinSlice<NB>::PER;
-  const int top = NB - 1 - PER * (int)threadIdx.x;
-  uint32_t own = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) own += s.c[i];
-  uint32_t total;
-  const uint32_t incl = block_incl_scan(own, s_wave, &total);
-  const uint32_t excl = incl - own;
-  if (excl < need && need <= incl) {
-    uint32_t run = excl;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (run + s.c[i] >= need) {
-        s_res[0] = (uint32_t)(top - i);
-        s_res[1] = run;
-        break;
-      }
-      run += s.c[i];
-    }
-  }
-  __syncthreads();
-  *bin = s_res[0];
-  *above = s_res[1];
-  __syncthreads();
-}
-
-template <int NB>
-__device__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s_wave, uint32_t* s_res,
-                                   uint32_t* bin, uint32_t* above) {
-  BinSlice<NB> s;
-  load_bin_slice<NB>(h, s);
-  threshold_from_slice<NB>(s, need, s_wave, s_res, bin, above);
-}
-
 constexpr int kSelV = 16;          // consecutive positions per thread per step
-constexpr int kEmitCap = 10240;    // threshold-bin keys the emit step keeps in LDS
-static_assert(kEmitCap % 4 == 0, "keys are read four at a time");
-constexpr int kMaxChunks = 1024;   // chunks per query (the host sizes chunks to respect it)
 
 __device__ __forceinline__ void write_all_visible(int32_t* out, int64_t c_lo, int64_t c_hi, int64_t vis, int K,
                                                   int c, int32_t* count) {
@@ -202,16 +90,6 @@ __device__ __forceinline__ void write_all_visible(int32_t* out, int64_t c_lo, in
     for (int64_t j = vis + threadIdx.x; j < K; j += blockDim.x) out[j] = -1;
     if (threadIdx.x == 0 && count) *count = (int32_t)vis;
   }
-}
-
-// Row stride of the bin-key lists: Lmax rounded up to 4 keys, so that a row
-// starts 16-byte aligned.
-__device__ __forceinline__ int64_t bin_key_stride(int64_t Lmax) { return (Lmax + 3) & ~(int64_t)3; }
-
-// Clears the query's step-1 histogram (run once its last reader has finished).
-__device__ __forceinline__ void clear_query_hist(const TopkParams& p, int bt, int nthreads) {
-  uint32_t* h = p.hist + (int64_t)bt * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += nthreads) h[i] = 0;
 }
 
 // kSelV consecutive scores from s0; positions >= lim get arbitrary values
@@ -316,35 +194,11 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(TopkParams p)
   }
 }
 
-// The emit step refines the threshold bin B with two more digits of 10 key
-// bits each (12 + 10 + 10 = 32).
-constexpr int kDigitBins = 1024;
-
-struct EmitShared {
-  uint32_t wave[2 * kSelWaves];
-  uint32_t res[3];                  // [2]: most bin-B entries in one chunk
-  uint32_t h2[kDigitBins];          // second digit of the bin-B keys
-  uint32_t h3[kDigitBins];          // third digit of the keys matching the first two
-  uint32_t boff[kMaxChunks + 1];    // bin-B entries in chunks before c' (chunk order)
-  uint32_t aoff[kMaxChunks + 1];    // entries above bin B in chunks before c'
-  alignas(16) uint32_t key[kEmitCap];  // the query's bin-B keys in chunk order
-};
-
-// Step 3: exact threshold, then this chunk's kept positions at their final slots.
-// Every load is issued before any is used: all chunks' counts, this chunk's
-// first kSelThreads * kEmitE candidates, and the first S (the largest power
-// of two with n_chunks * S <= kEmitFirst) bin-B keys of every chunk, read
-// speculatively four at a time inside their regions and masked afterwards;
-// a typical workgroup waits for memory once (a chunk with more than S bin-B
-// keys costs one more round per S).  The keys are gathered into LDS in chunk
-// order (key j of chunk c' at boff[c'] + j), so "the keys of chunks before
-// c" is an index range.  More than kEmitCap of them (heavy ties) are read
-// from global memory chunk by chunk instead.
-constexpr int kEmitG = 8;                           // speculative groups of 4 bin-B keys per thread
-constexpr int kEmitFirst = kSelThreads * kEmitG * 4;  // 8192
-constexpr int kEmitE = 8;                           // candidates per thread per round
-constexpr int kCntPer = kMaxChunks / kSelThreads;   // chunk counts per thread (chunks 4 tid + i)
-
+// Step 3: exact threshold, then this chunk's kept positions at their final
+// slots.  Every load is issued before any is used: the threshold
+// resolution's (all chunks' counts, the first bin-B keys of every chunk) and
+// this chunk's first kSelThreads * kEmitE candidates; a typical workgroup
+// waits for memory once.
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t emit_lds[];
   EmitShared& sh = *(EmitShared*)emit_lds;
@@ -352,41 +206,16 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) 
   const int c = blockIdx.x;
   const int bt = blockIdx.y, b = bt / p.T, t = bt % p.T;
   const int K = p.K;
-  const int nch = p.n_chunks;
   const int64_t chunk = p.chunk;
   const int64_t c_lo = (int64_t)c * chunk;
   const int64_t c_len = min(chunk, p.Lmax - c_lo);  // this chunk's candidate slots
-  const int64_t kstride = bin_key_stride(p.Lmax);
-  const uint32_t* bkeys = p.bin_keys + (int64_t)bt * kstride;
   const uint2* mine = p.cand + (int64_t)bt * p.Lmax + c_lo;
-  const uint32_t* ccnt = p.chunk_cnt + (int64_t)bt * nch;
-  const uint32_t* cabv = p.chunk_above + (int64_t)bt * nch;
-  int log_s = 2;  // S = 2^log_s speculative slots per chunk (>= 8: n_chunks <= 1024)
-  while ((nch << (log_s + 1)) <= kEmitFirst) ++log_s;
-  const uint32_t S = 1u << log_s;
-  // keys j .. j+3 of chunk cc (j % 4 == 0), clamped into the query's row
-  auto keys4 = [&](int cc, uint32_t j) -> uint4 {
-    return *(const uint4*)(bkeys + min((int64_t)min(cc, nch - 1) * chunk + j, kstride - 4));
-  };
 
   // ---- loads ----
   const int len = clamp_len(p.seq_lens[b], p.Lmax);
-  const uint2 hdr = p.header[bt];
-  const uint32_t n_mine = ccnt[c];
-  uint32_t cn[kCntPer], ca[kCntPer];
-#pragma unroll
-  for (int i = 0; i < kCntPer; ++i) {
-    const int cc = min(kCntPer * tid + i, nch - 1);
-    cn[i] = ccnt[cc];
-    ca[i] = cabv[cc];
-  }
-  // group g = tid + 256 i holds slots 4g .. 4g+3; slot sl = key sl % S of chunk sl / S
-  uint4 bk[kEmitG];
-#pragma unroll
-  for (int i = 0; i < kEmitG; ++i) {
-    const int sl = 4 * (tid + i * kSelThreads);
-    bk[i] = keys4(sl >> log_s, sl & (S - 1));
-  }
+  const uint32_t n_mine = p.chunk_cnt[(int64_t)bt * p.n_chunks + c];
+  ResolveLoads rl;
+  issue_resolve_loads(p, bt, rl);
   uint2 e[kEmitE];  // candidates kEmitE tid + i of the current round
 #pragma unroll
   for (int i = 0; i < kEmitE; ++i) e[i] = mine[min((int64_t)(kEmitE * tid + i), c_len - 1)];
@@ -394,135 +223,17 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) 
   const int64_t vis = max((int64_t)0, (int64_t)len - p.T + 1 + t);
   if (vis <= K || c_lo >= vis) return;
   int32_t* out = p.topk_idx + (int64_t)bt * K;
-  const int n_act = (int)((vis + chunk - 1) / chunk);  // chunks that ran step 2
-  const uint32_t bin = hdr.x, need = (uint32_t)K - hdr.y;  // entries to take from bin `bin`
-
-  // ---- chunk-order offsets of the bin-B keys and of the entries above ----
-  for (int i = tid; i < kDigitBins; i += kSelThreads) {
-    sh.h2[i] = 0;
-    sh.h3[i] = 0;
-  }
-  if (tid == 0) sh.res[2] = 0;
-  uint32_t nb[kCntPer], na[kCntPer];
-  uint32_t sums[2] = {0u, 0u}, tot[2], nb_max = 0;
-#pragma unroll
-  for (int i = 0; i < kCntPer; ++i) {
-    const bool act = kCntPer * tid + i < n_act;
-    nb[i] = act ? cn[i] - ca[i] : 0u;
-    na[i] = act ? ca[i] : 0u;
-    sums[0] += nb[i];
-    sums[1] += na[i];
-    nb_max = max(nb_max, nb[i]);
-  }
-  const uint32_t own[2] = {sums[0], sums[1]};
-  block_scan<2, kSelWaves>(sums, sh.wave, tot);  // (its barriers also cover the clearing above)
-  {
-    uint32_t xb = sums[0] - own[0], xa = sums[1] - own[1];
-#pragma unroll
-    for (int i = 0; i < kCntPer; ++i) {
-      const int cc = kCntPer * tid + i;
-      if (cc <= nch) {
-        sh.boff[cc] = xb;
-        sh.aoff[cc] = xa;
-      }
-      xb += nb[i];
-      xa += na[i];
-    }
-    if (tid == 0) {  // n_chunks == kMaxChunks: the closing offsets
-      sh.boff[kMaxChunks] = tot[0];
-      sh.aoff[kMaxChunks] = tot[1];
-    }
-    if (nb_max > 0) atomicMax(&sh.res[2], nb_max);
-  }
-  __syncthreads();
-  const uint32_t M = tot[0];
-  const uint32_t above_before = sh.aoff[c];
-  const uint32_t max_per_chunk = sh.res[2];
-  const bool in_lds = M <= (uint32_t)kEmitCap;
-
-  // ---- bin-B keys into LDS (chunk order) with their second digit counted ----
-  if (in_lds) {
-    auto stage = [&](const uint4 (&k)[kEmitG], uint32_t j0) {
-      uint32_t o[kEmitG], n[kEmitG];  // all offset reads first (independent LDS loads)
-#pragma unroll
-      for (int i = 0; i < kEmitG; ++i) {
-        const int cc = min((4 * (tid + i * kSelThreads)) >> log_s, nch);
-        o[i] = sh.boff[cc];
-        n[i] = sh.boff[min(cc + 1, nch)] - o[i];
-      }
-#pragma unroll
-      for (int i = 0; i < kEmitG; ++i) {
-        const int sl = 4 * (tid + i * kSelThreads);
-        const bool act = (sl >> log_s) < n_act;
-        const uint32_t j = j0 + (sl & (S - 1));
-        const uint32_t kv[4] = {k[i].x, k[i].y, k[i].z, k[i].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (act && j + q < n[i]) {
-            sh.key[o[i] + j + q] = kv[q];
-            atomicAdd(&sh.h2[(kv[q] >> 10) & (kDigitBins - 1)], 1u);
-          }
-        }
-      }
-    };
-    stage(bk, 0);
-    for (uint32_t j0 = S; j0 < max_per_chunk; j0 += S) {  // chunks with more than S bin-B keys
-#pragma unroll
-      for (int i = 0; i < kEmitG; ++i) {
-        const int sl = 4 * (tid + i * kSelThreads);
-        bk[i] = keys4(sl >> log_s, j0 + (sl & (S - 1)));
-      }
-      stage(bk, j0);
-    }
-  } else {
-    for (int cc = 0; cc < n_act; ++cc) {
-      const uint32_t n = sh.boff[cc + 1] - sh.boff[cc];
-      for (uint32_t j = tid; j < n; j += kSelThreads)
-        atomicAdd(&sh.h2[(bkeys[(int64_t)cc * chunk + j] >> 10) & (kDigitBins - 1)], 1u);
-    }
-  }
-  __syncthreads();
-  // calls f(key) for every bin-B key of chunks [0, c_stop)
-  auto for_each_key = [&](int c_stop, auto&& f) {
-    if (in_lds) {  // four keys per LDS read (kEmitCap is a multiple of 4)
-      const uint32_t n_end = sh.boff[c_stop];
-      for (uint32_t n = 4 * tid; n < n_end; n += 4 * kSelThreads) {
-        const uint4 k4 = *(const uint4*)&sh.key[n];
-        f(k4.x);
-        if (n + 1 < n_end) f(k4.y);
-        if (n + 2 < n_end) f(k4.z);
-        if (n + 3 < n_end) f(k4.w);
-      }
-    } else {
-      for (int cc = 0; cc < c_stop; ++cc) {
-        const uint32_t n = sh.boff[cc + 1] - sh.boff[cc];
-        for (uint32_t j = tid; j < n; j += kSelThreads) f(bkeys[(int64_t)cc * chunk + j]);
-      }
-    }
-  };
-
-  // second digit -> 22-bit prefix of the K-th key
-  uint32_t bin2, above2;
-  find_threshold_bin<kDigitBins>(sh.h2, need, sh.wave, sh.res, &bin2, &above2);
-  const uint32_t need2 = need - above2;
-  const uint32_t prefix22 = (bin << 10) | bin2;
-  // third digit -> exact K-th key tau
-  for_each_key(n_act, [&](uint32_t k) {
-    if ((k >> 10) == prefix22) atomicAdd(&sh.h3[k & (kDigitBins - 1)], 1u);
-  });
-  __syncthreads();
-  uint32_t bin3, above3;
-  find_threshold_bin<kDigitBins>(sh.h3, need2, sh.wave, sh.res, &bin3, &above3);
-  const uint32_t tau = (prefix22 << 10) | bin3;
-  const uint32_t take_ties = need2 - above3;  // ties at tau to keep, lowest positions first
+  const Resolved rs = resolve_threshold(p, bt, vis, rl, sh);
+  const uint32_t tau = rs.tau, take_ties = rs.take_ties;
 
   // bin-B keys of the chunks before this one: above tau, and equal to tau
   uint32_t ge[2] = {0u, 0u}, ge_tot[2];
-  for_each_key(c, [&](uint32_t k) {
+  for_each_bin_key(p, bt, sh, rs.in_lds, c, [&](uint32_t k) {
     ge[0] += k > tau ? 1u : 0u;
     ge[1] += k == tau ? 1u : 0u;
   });
   block_scan<2, kSelWaves>(ge, sh.wave, ge_tot);
+  const uint32_t above_before = sh.aoff[c];
 
   // this chunk's candidates in order (kEmitE consecutive per thread)
   uint32_t gt_seen = above_before + ge_tot[0], ties_seen = ge_tot[1];
