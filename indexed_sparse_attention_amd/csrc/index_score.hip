@@ -137,6 +137,8 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   __shared__ int64_t s_wsum[kScoreWaves];
   __shared__ int64_t s_excl[kScoreThreads];
   __shared__ int s_len[kScoreThreads];  // clamped length of each segment's sequence in the current chunk
+  __shared__ int s_list[kScoreThreads];  // the segments of the current chunk this workgroup serves, in order
+  __shared__ int s_wcnt[kScoreWaves];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -206,16 +208,38 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       chunk_total += s_wsum[w];
     }
     s_excl[tid] = off + v - mine;
+    // The segments this workgroup serves (those whose workgroup range holds
+    // wg): every thread tests its own segment, and the hits are listed in
+    // order.  (Testing them one after another, with a 64-bit division each,
+    // held the workgroups of the last segments back for microseconds before
+    // their first key load.)
+    // wg_first(st) <= wg < wg_end(st, n), without the divisions:
+    //   floor(st G / U) <= wg        <=>  st G < (wg + 1) U
+    //   wg < floor(st G / U) + 1     <=>  wg U <= st G
+    //   wg < floor((st + n) G / U)   <=>  (wg + 1) U <= (st + n) G
+    bool serves = false;
+    if (tid < n_here && mine > 0) {
+      const int64_t st = chunk_base + off + v - mine;
+      serves = st * G < (wg + 1) * U && (wg * U <= st * G || (wg + 1) * U <= (st + mine) * G);
+    }
+    const uint64_t hits = __ballot(serves);
+    if (l == 0) s_wcnt[wave] = __popcll(hits);
+    __syncthreads();
+    int n_list = 0, list_base = 0;
+#pragma unroll
+    for (int w = 0; w < kScoreWaves; ++w) {
+      if (w < wave) list_base += s_wcnt[w];
+      n_list += s_wcnt[w];
+    }
+    if (serves) s_list[list_base + __popcll(hits & ((1ull << l) - 1))] = tid;
     __syncthreads();
 
-    for (int i = 0; i < n_here; ++i) {
+    for (int k = 0; k < n_list; ++k) {
+      const int i = __builtin_amdgcn_readfirstlane(s_list[k]);  // (uniform: it selects the key buffer)
       const int64_t seg_start = chunk_base + s_excl[i];
       const int seg = c0 + i;
-      if (wg_first(seg_start) > wg) break;
       const int64_t seg_n = (i + 1 < n_here ? s_excl[i + 1] : chunk_total) - s_excl[i];
-      if (seg_n == 0) continue;
       const int64_t g0 = wg_first(seg_start), g1 = wg_end(seg_start, seg_n);
-      if (wg >= g1) continue;
       // this wave's units: iw, iw + n_w, iw + 2 n_w, ... of the segment
       const int64_t n_w = (g1 - g0) * kScoreWaves;
       const int64_t iw = (wg - g0) * kScoreWaves + wave;
