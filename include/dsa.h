@@ -115,7 +115,7 @@ typedef struct dsa_problem {
   int32_t out_dtype;    /* DSA_F32 | DSA_BF16 */
 } dsa_problem;
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 #define DSA_FORWARD_STAGES 3 /* indexer scores, Top-K, sparse attention */
 
 int dsa_abi_version(void);
@@ -224,6 +224,56 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
                        int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
                        size_t ws_bytes, struct ihipStream_t* stream,
                        struct ihipEvent_t* const* stage_events);
+
+/*
+ * Paged caches.  The pages have the fused indexer read the paged key cache
+ * directly and the sparse attention gather its selected rows from the paged
+ * KV cache, with the paged metadata prepared beside the query projection
+ * ("Optimizing Next-Gen LLM Inference" §3.1; "Inference Acceleration for New
+ * Large Model Architectures" §3.1 and §3.3).  Here one block table serves the
+ * index-key cache and the latent cache: logical row s of sequence b is row
+ * s % page_size of physical page block_table[b * max_pages + s / page_size]
+ * in both, and in their per-row scales.
+ *
+ *   block_table  device int32 [batch, max_pages].  Entries are device data:
+ *                kernels clamp them into [0, num_pages), so a bad entry gives
+ *                meaningless results, never an out-of-bounds read.
+ *   page_size    rows per page: a power of two, at least 64 (a page then holds
+ *                whole 64-row score units).
+ *   max_pages    columns of block_table; max_pages * page_size >= max_seq_len.
+ *   num_pages    physical pages in each cache; num_pages * page_size * row bytes
+ *                < 2^31 for each cache.
+ *
+ * The _paged entry points take, in place of k_idx / k_scale / kv / kv_scale,
+ *   k_pages   [num_pages, page_size, idx_dim]     (idx_key_dtype)
+ *   k_scales  [num_pages, page_size] fp32 when the keys are FP8, else NULL
+ *   kv_pages  [num_pages, page_size, qk_dim]      (kv_dtype)
+ *   kv_scales [num_pages, page_size] fp32 when the cache is FP8, else NULL
+ * and are otherwise the calls above (same workspaces, outputs and timing
+ * events; topk_idx stays in logical positions).  They need the matrix-core
+ * kernels (64 x 128 indexer, 576/512 MLA, bf16 or FP8 caches): other problems
+ * return DSA_ERR_UNSUPPORTED, as does DSA_FORCE_GENERIC.
+ */
+typedef struct dsa_paging {
+  const int32_t* block_table;
+  int32_t page_size;
+  int32_t max_pages;
+  int64_t num_pages;
+} dsa_paging;
+
+dsa_status dsa_index_score_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
+                                 const float* head_w, const void* k_pages, const float* k_scales,
+                                 const int32_t* seq_lens, float* scores, struct ihipStream_t* stream);
+dsa_status dsa_sparse_mla_decode_paged(const dsa_problem* p, const dsa_paging* pg, const void* q,
+                                       const void* kv_pages, const float* kv_scales,
+                                       const int32_t* topk_idx, const int32_t* seq_lens, void* out,
+                                       float* lse, void* ws, size_t ws_bytes, struct ihipStream_t* stream);
+dsa_status dsa_forward_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
+                             const float* head_w, const void* k_pages, const float* k_scales,
+                             const void* q, const void* kv_pages, const float* kv_scales,
+                             const int32_t* seq_lens, float* scores, int32_t* topk_idx,
+                             int32_t* topk_count, void* out, float* lse, void* ws, size_t ws_bytes,
+                             struct ihipStream_t* stream, struct ihipEvent_t* const* stage_events);
 
 /*
  * Diagnostics.  dsa_kernel_choice() names the kernels dsa_forward would launch

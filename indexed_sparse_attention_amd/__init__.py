@@ -55,6 +55,17 @@ class Problem(ctypes.Structure):
 _lib = None
 
 
+class Paging(ctypes.Structure):
+    """dsa_paging: block table (device int32 [batch, max_pages]) of paged caches."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int64)]
+
+
+def make_paging(block_table: torch.Tensor, page_size: int, num_pages: int) -> Paging:
+    assert block_table.dim() == 2 and block_table.dtype == torch.int32 and block_table.is_contiguous()
+    return Paging(block_table.data_ptr(), page_size, block_table.shape[1], num_pages)
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libdsa.so (torch is imported first so both share one HIP runtime)."""
     global _lib
@@ -80,8 +91,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_forward_workspace_size.argtypes = [PP]
     lib.dsa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
     lib.dsa_kernel_choice.argtypes = [PP, ctypes.c_char_p, ctypes.c_size_t]
+    PG = ctypes.POINTER(Paging)
+    lib.dsa_index_score_paged.argtypes = [PP, PG, P, P, P, P, P, P, P]
+    lib.dsa_sparse_mla_decode_paged.argtypes = [PP, PG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.dsa_forward_paged.argtypes = [PP, PG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
     for f in (lib.dsa_index_score, lib.dsa_topk, lib.dsa_sparse_mla_decode, lib.dsa_forward,
-              lib.dsa_kernel_choice):
+              lib.dsa_kernel_choice, lib.dsa_index_score_paged, lib.dsa_sparse_mla_decode_paged,
+              lib.dsa_forward_paged):
         f.restype = ctypes.c_int
     for f in (lib.dsa_topk_workspace_size, lib.dsa_sparse_mla_workspace_size,
               lib.dsa_forward_workspace_size, lib.dsa_workspace_zero_bytes):
@@ -243,6 +259,63 @@ def forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale=N
     d.update(heads=H, qk_dim=Dqk, v_dim=v_dim, softmax_scale=softmax_scale, q_dtype=dtype_code(q),
              kv_dtype=dtype_code(kv), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
     return make_problem(**d)
+
+
+def _forward_outputs(p: Problem, dev, top_k: int, v_dim: int, return_scores: bool, return_lse: bool,
+                     out: Optional[dict]) -> dict:
+    B, T, H = p.batch, p.q_len, p.heads
+    o = dict(out or {})
+    if "out" not in o:
+        o["out"] = torch.empty((B, T, H, v_dim), dtype=_torch_dtype(p.out_dtype), device=dev)
+    if return_lse and "lse" not in o:
+        o["lse"] = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    if "topk_idx" not in o:
+        o["topk_idx"] = torch.empty((B, T, top_k), dtype=torch.int32, device=dev)
+    if "topk_count" not in o:
+        o["topk_count"] = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if return_scores and "scores" not in o:
+        o["scores"] = torch.empty((B, T, p.max_seq_len), dtype=torch.float32, device=dev)
+    return o
+
+
+def _events(stage_events):
+    if stage_events is None:
+        return None
+    assert len(stage_events) == FORWARD_STAGES + 1
+    return (ctypes.c_void_p * (FORWARD_STAGES + 1))(*[e.cuda_event for e in stage_events])
+
+
+def dsa_forward_paged(q_idx: torch.Tensor, head_w: torch.Tensor, k_pages: torch.Tensor, q: torch.Tensor,
+                      kv_pages: torch.Tensor, seq_lens: torch.Tensor, block_table: torch.Tensor,
+                      top_k: int, v_dim: int, max_seq_len: int, softmax_scale: Optional[float] = None,
+                      k_scales: Optional[torch.Tensor] = None, kv_scales: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None, return_scores: bool = False,
+                      return_lse: bool = True, out: Optional[dict] = None,
+                      workspace: Optional[torch.Tensor] = None, stage_events: Optional[Sequence] = None,
+                      stream=None) -> dict:
+    """Whole path over paged caches: k_pages [num_pages, page_size, Di],
+    kv_pages [num_pages, page_size, Dqk] (scales [num_pages, page_size]),
+    block_table int32 [batch, max_pages] shared by both caches."""
+    lib = load_library()
+    num_pages, page_size, Di = k_pages.shape
+    assert kv_pages.shape[:2] == (num_pages, page_size)
+    B, T, Hi, _ = q_idx.shape
+    _, _, H, Dqk = q.shape
+    if out_dtype is None:
+        out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    p = make_problem(batch=B, q_len=T, max_seq_len=max_seq_len, idx_heads=Hi, idx_dim=Di, heads=H,
+                     qk_dim=Dqk, v_dim=v_dim, top_k=top_k, softmax_scale=softmax_scale,
+                     q_idx_dtype=dtype_code(q_idx), idx_key_dtype=dtype_code(k_pages), q_dtype=dtype_code(q),
+                     kv_dtype=dtype_code(kv_pages), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
+    pg = make_paging(block_table, page_size, num_pages)
+    o = _forward_outputs(p, q.device, top_k, v_dim, return_scores, return_lse, out)
+    ws = _workspace(lib.dsa_forward_workspace_size(ctypes.byref(p)), q.device, workspace)
+    _check(lib.dsa_forward_paged(ctypes.byref(p), ctypes.byref(pg), _ptr(q_idx), _ptr(head_w), _ptr(k_pages),
+                                 _ptr(k_scales), _ptr(q), _ptr(kv_pages), _ptr(kv_scales), _ptr(seq_lens),
+                                 _ptr(o.get("scores")), _ptr(o["topk_idx"]), _ptr(o["topk_count"]),
+                                 _ptr(o["out"]), _ptr(o.get("lse")), _ptr(ws), ws.numel(), _stream(stream),
+                                 _events(stage_events)))
+    return o
 
 
 def dsa_forward(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor, q: torch.Tensor,

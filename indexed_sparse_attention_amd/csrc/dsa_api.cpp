@@ -255,6 +255,10 @@ dsa::ScoreParams score_params(const dsa_problem* p, const void* q_idx, const flo
   s.Lmax = p->max_seq_len;
   s.q_dtype = p->q_idx_dtype;
   s.k_dtype = p->idx_key_dtype;
+  s.block_table = nullptr;
+  s.num_pages = 0;
+  s.max_pages = 0;
+  s.page_shift = 0;
   return s;
 }
 
@@ -306,7 +310,59 @@ dsa::MlaParams mla_params(const dsa_problem* p, const MlaLayout& L, uint8_t* ws,
   m.out_dtype = p->out_dtype;
   m.splits = L.splits;
   m.rows_per_split = L.rows_per_split;
+  m.block_table = nullptr;
+  m.num_pages = 0;
+  m.max_pages = 0;
+  m.page_shift = 0;
   return m;
+}
+
+int log2_exact(int64_t v) {
+  int s = 0;
+  while (((int64_t)1 << s) < v) ++s;
+  return s;
+}
+
+bool score_uses_mfma(const dsa_problem* p);
+
+// Paging descriptor checks; the cache-side checks for the index keys
+// (index != 0) and / or the latent cache (mla != 0).
+dsa_status check_paging(const dsa_problem* p, const dsa_paging* pg, bool index, bool mla) {
+  REQUIRE(pg, "pg must be non-NULL");
+  REQUIRE(pg->block_table && aligned(pg->block_table, 4), "block_table must be non-NULL and 4-byte aligned");
+  REQUIRE(pg->page_size >= 64 && (pg->page_size & (pg->page_size - 1)) == 0,
+          "page_size must be a power of two >= 64 (got %d)", pg->page_size);
+  REQUIRE(pg->max_pages >= 1 && (int64_t)pg->max_pages * pg->page_size >= p->max_seq_len,
+          "max_pages * page_size must cover max_seq_len (%d x %d < %d)", pg->max_pages, pg->page_size,
+          p->max_seq_len);
+  REQUIRE(pg->num_pages >= 1, "num_pages must be >= 1");
+  REQUIRE(pg->num_pages * pg->page_size < ((int64_t)1 << 31), "num_pages * page_size must be < 2^31 rows");
+  if (index) {
+    if (!score_uses_mfma(p))
+      return fail(DSA_ERR_UNSUPPORTED, "paged caches need the matrix-core index kernel (64 x 128, bf16 or FP8 keys)");
+    const int64_t row_bytes = (int64_t)p->idx_dim * (p->idx_key_dtype == DSA_BF16 ? 2 : 1);
+    REQUIRE(pg->num_pages * pg->page_size * row_bytes < ((int64_t)1 << 31),
+            "the paged index-key cache must be < 2 GiB");
+  }
+  if (mla && !mla_uses_mfma(p))
+    return fail(DSA_ERR_UNSUPPORTED, "paged caches need the matrix-core attention kernel (576/512, bf16 q)");
+  return DSA_OK;
+}
+
+void apply_paging(dsa::ScoreParams& s, const dsa_paging* pg) {
+  if (!pg) return;
+  s.block_table = pg->block_table;
+  s.num_pages = pg->num_pages;
+  s.max_pages = pg->max_pages;
+  s.page_shift = log2_exact(pg->page_size);
+}
+
+void apply_paging(dsa::MlaParams& m, const dsa_paging* pg) {
+  if (!pg) return;
+  m.block_table = pg->block_table;
+  m.num_pages = pg->num_pages;
+  m.max_pages = pg->max_pages;
+  m.page_shift = log2_exact(pg->page_size);
 }
 
 bool score_uses_mfma(const dsa_problem* p) {
@@ -339,17 +395,32 @@ const char* dsa_status_string(dsa_status s) {
 
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
-dsa_status dsa_index_score(const dsa_problem* p, const void* q_idx, const float* head_w,
-                           const void* k_idx, const float* k_scale, const int32_t* seq_lens,
-                           float* scores, struct ihipStream_t* stream) {
+static dsa_status index_score_impl(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
+                                   const float* head_w, const void* k_idx, const float* k_scale,
+                                   const int32_t* seq_lens, float* scores, hipStream_t stream) {
   dsa_status st = validate_problem(p);
   if (st != DSA_OK) return st;
   if ((st = check_index_inputs(p, q_idx, head_w, k_idx, k_scale, seq_lens)) != DSA_OK) return st;
+  if (pg && (st = check_paging(p, pg, true, false)) != DSA_OK) return st;
   REQUIRE(scores && aligned(scores, 16), "scores must be non-NULL and 16-byte aligned");
   auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, scores, nullptr);
+  apply_paging(sp, pg);
   if ((st = hip_check(dsa::launch_score(sp, !force_generic(), num_cus(), stream), "index score launch")) != DSA_OK)
     return st;
   return ok();
+}
+
+dsa_status dsa_index_score(const dsa_problem* p, const void* q_idx, const float* head_w,
+                           const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                           float* scores, struct ihipStream_t* stream) {
+  return index_score_impl(p, nullptr, q_idx, head_w, k_idx, k_scale, seq_lens, scores, stream);
+}
+
+dsa_status dsa_index_score_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
+                                 const float* head_w, const void* k_pages, const float* k_scales,
+                                 const int32_t* seq_lens, float* scores, struct ihipStream_t* stream) {
+  if (!pg) return fail(DSA_ERR_INVALID_ARG, "pg must be non-NULL");
+  return index_score_impl(p, pg, q_idx, head_w, k_pages, k_scales, seq_lens, scores, stream);
 }
 
 size_t dsa_topk_workspace_size(const dsa_problem* p) {
@@ -400,13 +471,13 @@ size_t dsa_sparse_mla_workspace_size(const dsa_problem* p) {
   return (size_t)mla_layout(p).bytes;
 }
 
-dsa_status dsa_sparse_mla_decode(const dsa_problem* p, const void* q, const void* kv,
-                                 const float* kv_scale, const int32_t* topk_idx,
-                                 const int32_t* seq_lens, void* out, float* lse, void* ws,
-                                 size_t ws_bytes, struct ihipStream_t* stream) {
+static dsa_status sparse_mla_impl(const dsa_problem* p, const dsa_paging* pg, const void* q, const void* kv,
+                                  const float* kv_scale, const int32_t* topk_idx, const int32_t* seq_lens,
+                                  void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   dsa_status st = validate_problem(p);
   if (st != DSA_OK) return st;
   if ((st = check_mla_inputs(p, q, kv, kv_scale, seq_lens, out, lse)) != DSA_OK) return st;
+  if (pg && (st = check_paging(p, pg, false, true)) != DSA_OK) return st;
   REQUIRE(topk_idx && aligned(topk_idx, 4), "topk_idx must be non-NULL and 4-byte aligned");
   const MlaLayout L = mla_layout(p);
   if ((int64_t)ws_bytes < L.bytes)
@@ -414,8 +485,24 @@ dsa_status dsa_sparse_mla_decode(const dsa_problem* p, const void* q, const void
                 (long long)L.bytes, ws_bytes);
   REQUIRE(L.bytes == 0 || (ws && aligned(ws, 16)), "ws must be non-NULL and 16-byte aligned");
   auto mp = mla_params(p, L, (uint8_t*)ws, q, kv, kv_scale, topk_idx, seq_lens, out, lse);
+  apply_paging(mp, pg);
   if ((st = hip_check(dsa::launch_mla(mp, mla_uses_mfma(p), stream), "sparse attention")) != DSA_OK) return st;
   return ok();
+}
+
+dsa_status dsa_sparse_mla_decode(const dsa_problem* p, const void* q, const void* kv,
+                                 const float* kv_scale, const int32_t* topk_idx,
+                                 const int32_t* seq_lens, void* out, float* lse, void* ws,
+                                 size_t ws_bytes, struct ihipStream_t* stream) {
+  return sparse_mla_impl(p, nullptr, q, kv, kv_scale, topk_idx, seq_lens, out, lse, ws, ws_bytes, stream);
+}
+
+dsa_status dsa_sparse_mla_decode_paged(const dsa_problem* p, const dsa_paging* pg, const void* q,
+                                       const void* kv_pages, const float* kv_scales,
+                                       const int32_t* topk_idx, const int32_t* seq_lens, void* out,
+                                       float* lse, void* ws, size_t ws_bytes, struct ihipStream_t* stream) {
+  if (!pg) return fail(DSA_ERR_INVALID_ARG, "pg must be non-NULL");
+  return sparse_mla_impl(p, pg, q, kv_pages, kv_scales, topk_idx, seq_lens, out, lse, ws, ws_bytes, stream);
 }
 
 size_t dsa_forward_workspace_size(const dsa_problem* p) {
@@ -423,16 +510,16 @@ size_t dsa_forward_workspace_size(const dsa_problem* p) {
   return (size_t)fwd_layout(p).bytes;
 }
 
-dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
-                       const void* k_idx, const float* k_scale, const void* q, const void* kv,
-                       const float* kv_scale, const int32_t* seq_lens, float* scores,
-                       int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
-                       size_t ws_bytes, struct ihipStream_t* stream,
-                       struct ihipEvent_t* const* stage_events) {
+static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
+                               const float* head_w, const void* k_idx, const float* k_scale, const void* q,
+                               const void* kv, const float* kv_scale, const int32_t* seq_lens, float* scores,
+                               int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream, struct ihipEvent_t* const* stage_events) {
   dsa_status st = validate_problem(p);
   if (st != DSA_OK) return st;
   if ((st = check_index_inputs(p, q_idx, head_w, k_idx, k_scale, seq_lens)) != DSA_OK) return st;
   if ((st = check_mla_inputs(p, q, kv, kv_scale, seq_lens, out, lse)) != DSA_OK) return st;
+  if (pg && (st = check_paging(p, pg, true, true)) != DSA_OK) return st;
   REQUIRE(!scores || aligned(scores, 16), "scores must be 16-byte aligned");
   REQUIRE(!topk_idx || aligned(topk_idx, 4), "topk_idx must be 4-byte aligned");
   REQUIRE(!topk_count || aligned(topk_count, 4), "topk_count must be 4-byte aligned");
@@ -460,6 +547,7 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
   // dispatch then takes events 0 and 1 at the kernel's own start and end)
   const bool mfma_score = score_uses_mfma(p);
   auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, sc, hist);
+  apply_paging(sp, pg);
   if (!mfma_score) {
     sp.hist = nullptr;
     if ((st = rec(0)) != DSA_OK) return st;
@@ -480,9 +568,31 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
   if ((st = rec(2)) != DSA_OK) return st;
   // stage 3: sparse MLA attention
   auto mp = mla_params(p, F.mla, w + F.off_mla, q, kv, kv_scale, idx, seq_lens, out, lse);
+  apply_paging(mp, pg);
   if ((st = hip_check(dsa::launch_mla(mp, mla_uses_mfma(p), s), "sparse attention")) != DSA_OK) return st;
   if ((st = rec(3)) != DSA_OK) return st;
   return ok();
+}
+
+dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
+                       const void* k_idx, const float* k_scale, const void* q, const void* kv,
+                       const float* kv_scale, const int32_t* seq_lens, float* scores,
+                       int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
+                       size_t ws_bytes, struct ihipStream_t* stream,
+                       struct ihipEvent_t* const* stage_events) {
+  return forward_impl(p, nullptr, q_idx, head_w, k_idx, k_scale, q, kv, kv_scale, seq_lens, scores, topk_idx,
+                      topk_count, out, lse, ws, ws_bytes, stream, stage_events);
+}
+
+dsa_status dsa_forward_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
+                             const float* head_w, const void* k_pages, const float* k_scales,
+                             const void* q, const void* kv_pages, const float* kv_scales,
+                             const int32_t* seq_lens, float* scores, int32_t* topk_idx,
+                             int32_t* topk_count, void* out, float* lse, void* ws, size_t ws_bytes,
+                             struct ihipStream_t* stream, struct ihipEvent_t* const* stage_events) {
+  if (!pg) return fail(DSA_ERR_INVALID_ARG, "pg must be non-NULL");
+  return forward_impl(p, pg, q_idx, head_w, k_pages, k_scales, q, kv_pages, kv_scales, seq_lens, scores, topk_idx,
+                      topk_count, out, lse, ws, ws_bytes, stream, stage_events);
 }
 
 int dsa_kernel_choice(const dsa_problem* p, char* buf, size_t len) {

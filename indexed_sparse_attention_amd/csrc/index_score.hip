@@ -124,7 +124,7 @@ struct QRegs<TQ, true> {
   i32x8 a[TQ][4];  // [token][head tile], 32 e4m3 codes
 };
 
-template <int TQ, int NSLOT, bool FP8, int MINB, int NT>
+template <int TQ, int NSLOT, bool FP8, int MINB, int NT, bool PAGED>
 __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   constexpr int kScoreThreads = NT, kScoreWaves = NT / kWave;
   // LDS: [TQ] index queries in operand order (bf16: 64 x 128 x 2 B; e4m3: 64 x 128 B),
@@ -264,10 +264,34 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       const int last_row = len - 1;
       auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
 
+      // Paged caches: a 16-row sub-tile never straddles a page (pages hold a
+      // multiple of 64 rows), so each sub-tile's rows are read through a
+      // buffer resource over its page.  The block-table entries of the
+      // sub-tiles NSLOT ahead of the ring are loaded one ring's length before
+      // they are needed (their wait then costs nothing: the ring's own waits
+      // already cover them).
+      const int64_t page_rows = PAGED ? ((int64_t)1 << p.page_shift) : 1;
+      const int32_t* btab = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+      auto page_entry = [&](int x) -> int32_t {  // block-table entry of sub-tile x (clamped into the wave's)
+        const int64_t xs = min((int64_t)x, max(n_sub - 1, (int64_t)0));
+        return btab[min(sub_pos(xs) >> p.page_shift, (int64_t)p.max_pages - 1)];
+      };
+      auto phys_page = [&](int32_t entry) -> int64_t { return min(max((int64_t)entry, (int64_t)0), p.num_pages - 1); };
+      auto key_rsrc = [&](int32_t entry) -> __amdgpu_buffer_rsrc_t {
+        if constexpr (!PAGED) {
+          return krows;
+        } else {
+          const int64_t pp = phys_page(__builtin_amdgcn_readfirstlane(entry));
+          return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.k_idx + pp * page_rows * kRowBytes),
+                                                   (short)0, (int)(page_rows * kRowBytes), kBufferFlags);
+        }
+      };
       auto st_off = [&](int x) -> uint32_t {  // offset of the key row this lane loads for sub-tile x
         const int64_t pos = sub_pos(x) + lc;
-        return (x < n_sub && pos < len) ? (uint32_t)(pos * kRowBytes) : kNoRow;
+        const int64_t r = PAGED ? (pos & (page_rows - 1)) : pos;
+        return (x < n_sub && pos < len) ? (uint32_t)(r * kRowBytes) : kNoRow;
       };
+      int32_t pg_cur[NSLOT], pg_next[NSLOT];  // (paged) entries of the slots' sub-tiles and of those NSLOT ahead
 
       // Key tiles stream through a ring of NSLOT sub-tile register slots,
       // filled first, before the queries are staged: the key stream starts
@@ -280,8 +304,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       static_assert((4 * RB) % NSLOT == 0 && NSLOT % 4 == 0, "ring must tile the batch");
       KeyTile<FP8> slot[NSLOT];
       auto fill_ring = [&]() {
+        if constexpr (PAGED) {
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], krows, st_off(j), lg);
+          for (int j = 0; j < NSLOT; ++j) pg_cur[j] = page_entry(j);
+#pragma unroll
+          for (int j = 0; j < NSLOT; ++j) pg_next[j] = page_entry(j + NSLOT);
+        }
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], key_rsrc(pg_cur[j]), st_off(j), lg);
       };
 
       // head weights (used from the first unit on), then the index queries
@@ -375,7 +405,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           // after the reduce-scatter lane l holds position lc of its sub-tile 4u + lg
           const int64_t pos = sub_pos(4 * (u0 + ub) + lg) + lc;
           float kscale = 1.0f;
-          if constexpr (FP8) kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
+          if constexpr (FP8 && !PAGED) {
+            kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
+          } else if constexpr (FP8) {
+            // this lane's sub-tile 4u + lg sits in slot (4 ub + lg) % NSLOT (u0 is a multiple of NSLOT)
+            const int s0 = (4 * ub) % NSLOT;
+            const int32_t e = lg == 0 ? pg_cur[s0] : lg == 1 ? pg_cur[s0 + 1] : lg == 2 ? pg_cur[s0 + 2] : pg_cur[s0 + 3];
+            kscale = p.k_scale[phys_page(e) * page_rows + (pos < len ? (pos & (page_rows - 1)) : 0)];
+          }
           float part[TQ][4];
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
@@ -404,7 +441,9 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
             }
             // refill this slot with the sub-tile NSLOT ahead (nothing is read
             // past the wave's sub-tiles or the sequence's end)
-            load_key_tile<FP8>(slot[j], krows, st_off(x + NSLOT), lg);
+            if constexpr (PAGED) pg_cur[j] = pg_next[j];
+            load_key_tile<FP8>(slot[j], key_rsrc(pg_cur[j]), st_off(x + NSLOT), lg);
+            if constexpr (PAGED) pg_next[j] = page_entry(x + 2 * NSLOT);
           }
           if (live) {
             // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
@@ -462,20 +501,29 @@ bool score_mfma_supported(const ScoreParams& p) {
   if (p.Hi != kHi || p.Di != kDi) return false;
   // key rows are addressed by 32-bit byte offsets within a sequence
   const int64_t row_bytes = p.k_dtype == kBF16 ? 2 * kDi : kDi;
-  if ((int64_t)p.Lmax * row_bytes >= (int64_t)kNoRow) return false;
+  if (!p.block_table && (int64_t)p.Lmax * row_bytes >= (int64_t)kNoRow) return false;  // (paged: one page at a time)
   if (p.k_dtype == kBF16) return p.q_dtype == kBF16;
   return p.k_dtype == kE4M3;
 }
 
-template <int TQ, int NSLOT, bool FP8, int MINB = 2, int NT = 256>
-static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+template <int TQ, int NSLOT, bool FP8, int MINB, int NT, bool PAGED>
+static void launch_mfma_k(const ScoreParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
+                          hipEvent_t ev_stop) {
   constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
   const size_t lds = TQ * kQBytes + (p.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
   if (ev_start || ev_stop)  // events taken by the dispatch itself at the kernel's start and end
-    hipExtLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT>), dim3(grid), dim3(NT), lds, stream, ev_start,
-                          ev_stop, 0, p);
+    hipExtLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT, PAGED>), dim3(grid), dim3(NT), lds, stream,
+                          ev_start, ev_stop, 0, p);
   else
-    hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT>), dim3(grid), dim3(NT), lds, stream, p);
+    hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT, PAGED>), dim3(grid), dim3(NT), lds, stream, p);
+}
+
+template <int TQ, int NSLOT, bool FP8, int MINB = 2, int NT = 256>
+static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (p.block_table)
+    launch_mfma_k<TQ, NSLOT, FP8, MINB, NT, true>(p, grid, stream, ev_start, ev_stop);
+  else
+    launch_mfma_k<TQ, NSLOT, FP8, MINB, NT, false>(p, grid, stream, ev_start, ev_stop);
 }
 
 static int env_int(const char* name, int dflt) {

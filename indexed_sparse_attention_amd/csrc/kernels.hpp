@@ -17,6 +17,12 @@ struct ScoreParams {
   int B, T, Hi, Di;
   int64_t Lmax;
   int q_dtype, k_dtype;
+  // Paged caches (block_table non-null): k_idx [num_pages, 2^page_shift, Di]
+  // and k_scale [num_pages, 2^page_shift]; row s of sequence b lives in
+  // physical page block_table[b * max_pages + s >> page_shift].
+  const int32_t* block_table;
+  int64_t num_pages;
+  int max_pages, page_shift;
 };
 
 struct TopkParams {
@@ -52,6 +58,11 @@ struct MlaParams {
   int q_dtype, kv_dtype, out_dtype;
   int splits;               // row splits per query
   int rows_per_split;       // multiple of the row tile
+  // Paged cache (block_table non-null): kv [num_pages, 2^page_shift, Dqk]
+  // and kv_scale [num_pages, 2^page_shift], addressed as for ScoreParams.
+  const int32_t* block_table;
+  int64_t num_pages;
+  int max_pages, page_shift;
 };
 
 // index_score.hip

@@ -431,7 +431,10 @@ void mla_mfma_kernel(MlaParams p) {
   const int lg = l >> 4, lc = l & 15;
   const int len = clamp_len(p.seq_lens[b], p.Lmax);
   const int h0 = hg * kHeadsPerWG + wave * kHeadsPerWave;  // this wave's first head
-  const int64_t seq_row0 = (int64_t)b * p.Lmax;
+  // row index of position 0 of this sequence (paged cache: rows are
+  // translated to physical rows when the index list is loaded)
+  const bool paged = p.block_table != nullptr;
+  const int64_t seq_row0 = paged ? 0 : (int64_t)b * p.Lmax;
   const int32_t* sel = p.topk_idx + (int64_t)bt * p.K;
   const int j_begin = split * p.rows_per_split;
   const int n_rows = max(0, min(min(p.K, j_begin + p.rows_per_split) - j_begin, kIdxCap));
@@ -453,6 +456,20 @@ void mla_mfma_kernel(MlaParams p) {
   int32_t iv[kPer];  // entries tid + 256 k
 #pragma unroll
   for (int k = 0; k < kPer; ++k) iv[k] = resolve(tid + k * kMlaThreads);
+  if (paged) {
+    // position -> physical row: page table[b][pos / page] (clamped into the
+    // cache), row pos % page within it; every entry's load is issued first
+    const int64_t prow = (int64_t)1 << p.page_shift;
+    const int32_t* btab = p.block_table + (int64_t)b * p.max_pages;
+    int32_t pe[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) pe[k] = btab[min((int64_t)(max(iv[k], 0) >> p.page_shift), (int64_t)p.max_pages - 1)];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t pp = min(max((int64_t)pe[k], (int64_t)0), p.num_pages - 1);
+      iv[k] = iv[k] >= 0 ? (int32_t)(pp * prow + (iv[k] & (prow - 1))) : -1;
+    }
+  }
   // the list in LDS, padded with -1 through the last tile plus the 2 tiles
   // whose positions are read ahead
   const int n_tiles = (n_rows + kTile - 1) / kTile;
@@ -461,7 +478,12 @@ void mla_mfma_kernel(MlaParams p) {
   for (int k = 0; k < kPer; ++k) s_idx[tid + k * kMlaThreads] = iv[k];  // -1 past the list
   for (int i = kIdxCap + tid; i < n_pad; i += kMlaThreads) s_idx[i] = -1;
   float kscale = 0.0f;  // e4m3: scale of row 16 wave + l/4 of the tile being copied
-  {
+  if (paged) {  // the first tile's rows come back from LDS
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int32_t pos0[2] = {s_idx[my_row], s_idx[my_row + 8]};
+    tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
+    if constexpr (FP8) kscale = p.kv_scale[max(s_idx[16 * wave + (l >> 2)], 0)];
+  } else {
     const int32_t pos0[2] = {resolve(my_row), resolve(my_row + 8)};
     tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
     if constexpr (FP8) kscale = p.kv_scale[seq_row0 + max(resolve(16 * wave + (l >> 2)), 0)];

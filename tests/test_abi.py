@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = dsa.load_library()
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
     assert lib.dsa_status_string(0) == b"DSA_OK"
     assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
 
@@ -171,3 +171,46 @@ def test_kernel_choice_reports_paths():
         assert "score=generic" in dsa.kernel_choice(p) and "mla=generic" in dsa.kernel_choice(p)
     finally:
         del os.environ["DSA_FORCE_GENERIC"]
+
+
+def _paging(table=FAKE, page_size=64, max_pages=64, num_pages=1024):
+    return dsa.Paging(table, page_size, max_pages, num_pages)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(table=None), b"block_table"),
+    (dict(table=FAKE + 2), b"block_table"),
+    (dict(page_size=32), b"page_size"),
+    (dict(page_size=96), b"page_size"),
+    (dict(max_pages=63), b"max_pages"),
+    (dict(num_pages=0), b"num_pages"),
+    (dict(num_pages=1 << 26, page_size=64), b"2^31"),
+])
+def test_paging_descriptor_checked_before_launch(kw, msg):
+    # 4096 rows = 64 pages of 64; every call fails validation before any HIP call
+    lib = dsa.load_library()
+    p = good_problem()
+    P = ctypes.byref(p)
+    pg = _paging(**kw)
+    f = FAKE
+    need = lib.dsa_forward_workspace_size(P)
+    for st in (lib.dsa_index_score_paged(P, ctypes.byref(pg), f, f, f, None, f, f, None),
+               lib.dsa_sparse_mla_decode_paged(P, ctypes.byref(pg), f, f, None, f, f, f, f, f, 1 << 40, None),
+               lib.dsa_forward_paged(P, ctypes.byref(pg), f, f, f, None, f, f, None, f, None, None, None, f, f,
+                                     0x100000, need, None, None)):
+        assert st == 1, lib.dsa_last_error()
+        assert msg in lib.dsa_last_error(), lib.dsa_last_error()
+    assert lib.dsa_forward_paged(P, None, f, f, f, None, f, f, None, f, None, None, None, f, f, 0x100000, need,
+                                 None, None) == 1
+
+
+def test_paging_needs_the_matrix_core_kernels():
+    lib = dsa.load_library()
+    tiny = dsa.make_problem(batch=1, q_len=1, max_seq_len=256, idx_heads=4, idx_dim=32, heads=4,
+                            qk_dim=80, v_dim=64, top_k=32, q_idx_dtype=0, idx_key_dtype=0, q_dtype=0,
+                            kv_dtype=0, out_dtype=0)
+    pg = _paging(max_pages=4)
+    f = FAKE
+    assert lib.dsa_index_score_paged(ctypes.byref(tiny), ctypes.byref(pg), f, f, f, None, f, f, None) == 2
+    assert lib.dsa_sparse_mla_decode_paged(ctypes.byref(tiny), ctypes.byref(pg), f, f, None, f, f, f, f, f,
+                                           1 << 40, None) == 2
