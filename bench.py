@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode128k")
     ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
+                    help="read both caches through a block table with pages of this many rows "
+                         "(0: contiguous caches, the default)")
     ap.add_argument("--graph", action="store_true", help="replay each step as a HIP graph")
     ap.add_argument("--no-graph", action="store_true", help="eager launches (the default)")
     ap.add_argument("--stage-steps", type=int, default=50, help="eager steps timed per stage")
@@ -218,7 +221,39 @@ def main():
             "topk_idx": torch.empty((B, T, w.top_k), dtype=torch.int32, device=dev),
             "topk_count": torch.empty((B, T), dtype=torch.int32, device=dev)}
 
+    if args.paged:
+        # The same caches in pages of a physical pool, in a random page order
+        # (seeded), with one block table for both; every rotating copy is a pool.
+        P = args.paged
+        max_pages = (w.max_seq_len + P - 1) // P
+        num_pages = B * max_pages
+        gen = torch.Generator().manual_seed(0xD5A0)
+        table = torch.randperm(num_pages, generator=gen).to(torch.int32).view(B, max_pages).to(dev)
+        flat = table.view(-1).long()
+
+        def pool(x, row):
+            if x is None:
+                return None
+            x = x.view((B, w.max_seq_len) + row)
+            pad = max_pages * P - w.max_seq_len
+            if pad:
+                x = torch.cat([x, torch.zeros((B, pad) + row, dtype=x.dtype, device=dev)], dim=1)
+            out = torch.empty((num_pages, P) + row, dtype=x.dtype, device=dev)
+            out[flat] = x.reshape((num_pages, P) + row)
+            return out
+
+        k_copies = [pool(k, (w.idx_dim,)) for k in k_copies]
+        kv_copies = [pool(kv, (w.qk_dim,)) for kv in kv_copies]
+        k_scale, kv_scale = pool(k_scale, ()), pool(kv_scale, ())
+        torch.cuda.synchronize()
+
     def step(r, stage_events=None):
+        if args.paged:
+            dsa.dsa_forward_paged(q_idx, head_w, k_copies[r], q, kv_copies[r], seq_lens, table, w.top_k,
+                                  w.v_dim, w.max_seq_len, w.softmax_scale, k_scales=k_scale,
+                                  kv_scales=kv_scale, out_dtype=out_dtype, out=outs, workspace=ws,
+                                  stage_events=stage_events)
+            return
         dsa.dsa_forward(q_idx, head_w, k_copies[r], q, kv_copies[r], seq_lens, w.top_k, w.v_dim,
                         w.softmax_scale, k_scale=k_scale, kv_scale=kv_scale, out_dtype=out_dtype,
                         out=outs, workspace=ws, stage_events=stage_events)
@@ -332,7 +367,7 @@ def main():
         "config": {"workload": args.workload, "batch": B, "q_len": T, "max_seq_len": w.max_seq_len,
                    "mean_len": float(np.mean(w.seq_lens)), "top_k": w.top_k,
                    "indexer": f"{w.idx_heads}x{w.idx_dim}", "mla_heads": H, "qk_dim": w.qk_dim,
-                   "v_dim": w.v_dim, "graph": graphs is not None, "rotate": R,
+                   "v_dim": w.v_dim, "graph": graphs is not None, "rotate": R, "paged": args.paged,
                    "kernels": dsa.kernel_choice(prob)},
         "hbm_gbps_e2e": e2e_gbps, "hbm_frac_e2e": e2e_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": ab["total"],
