@@ -256,33 +256,28 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       // waves (sub-tile iw + x n_w is this wave's x-th), so at any moment the
       // waves read one contiguous window of consecutive 4 KB (bf16) tiles.
       // A unit is 4 of a wave's sub-tiles: x = 4u .. 4u+3.
-      // (paged caches: whole units go round-robin instead, so that a wave's
-      // unit of 64 positions sits in one page: one block-table entry per unit)
-      const int64_t n_sub = PAGED ? (iw < seg_n ? 4 * ((seg_n - iw + n_w - 1) / n_w) : 0)
-                                  : (iw < 4 * seg_n ? (4 * seg_n - iw + n_w - 1) / n_w : 0);
+      const int64_t n_sub = iw < 4 * seg_n ? (4 * seg_n - iw + n_w - 1) / n_w : 0;
       const int n_units = (int)((n_sub + 3) / 4);
       constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
       const __amdgpu_buffer_rsrc_t krows = __builtin_amdgcn_make_buffer_rsrc(
           (void*)((const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes), (short)0, len * kRowBytes, kBufferFlags);
       const int last_row = len - 1;
-      auto sub_pos = [&](int64_t x) -> int64_t {  // first position of sub-tile x
-        if constexpr (PAGED) return ((iw + (x >> 2) * n_w) * 4 + (x & 3)) * 16;
-        return (iw + x * n_w) * 16;
-      };
+      auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
 
-      // Paged caches: a unit of 64 positions never straddles a page (pages hold
-      // a multiple of 64 rows), so each unit's rows are read through a buffer
-      // resource over its page.  The block-table entries of the units ahead
-      // of the ring are loaded one unit before they are needed (their wait
-      // then costs nothing: the ring's own waits already cover them).
+      // Paged caches: a 16-row sub-tile never straddles a page (pages hold a
+      // multiple of 64 rows), so each sub-tile's rows are read through a
+      // buffer resource over its page.  The block-table entries of the
+      // sub-tiles NSLOT ahead of the ring are loaded one ring's length before
+      // they are needed (their wait then costs nothing: the ring's own waits
+      // already cover them).
       const int64_t page_rows = PAGED ? ((int64_t)1 << p.page_shift) : 1;
       // (read as constant memory: with a uniform index these are scalar loads,
       // so the entries sit in scalar registers)
       typedef const __attribute__((address_space(4))) int32_t* const_i32p;
       const const_i32p btab = PAGED ? (const_i32p)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
-      auto page_entry = [&](int u) -> int32_t {  // block-table entry of the wave's unit u (clamped into its units)
-        const int64_t us = min((int64_t)u, max(n_sub / 4 - 1, (int64_t)0));
-        return btab[__builtin_amdgcn_readfirstlane((int)min(sub_pos(4 * us) >> p.page_shift, (int64_t)p.max_pages - 1))];
+      auto page_entry = [&](int x) -> int32_t {  // block-table entry of sub-tile x (clamped into the wave's)
+        const int64_t xs = min((int64_t)x, max(n_sub - 1, (int64_t)0));
+        return btab[__builtin_amdgcn_readfirstlane((int)min(sub_pos(xs) >> p.page_shift, (int64_t)p.max_pages - 1))];
       };
       auto phys_page = [&](int32_t entry) -> int64_t { return min(max((int64_t)entry, (int64_t)0), p.num_pages - 1); };
       auto key_rsrc = [&](int32_t entry) -> __amdgpu_buffer_rsrc_t {
@@ -299,11 +294,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         const int64_t r = PAGED ? (pos & (page_rows - 1)) : pos;
         return (x < n_sub && pos < len) ? (uint32_t)(r * kRowBytes) : kNoRow;
       };
-      // (paged) block-table entries of the wave's units u .. u + RU + 1, u the
-      // unit being computed: the ring holds units u .. u + RU - 1 and is refilled
-      // with unit u + RU; the last one is in flight
-      constexpr int RU = NSLOT / 4;
-      int32_t pgu[RU + 2];
+      int32_t pg_cur[NSLOT], pg_next[NSLOT];  // (paged) entries of the slots' sub-tiles and of those NSLOT ahead
 
       // Key tiles stream through a ring of NSLOT sub-tile register slots,
       // filled first, before the queries are staged: the key stream starts
@@ -318,10 +309,12 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       auto fill_ring = [&]() {
         if constexpr (PAGED) {
 #pragma unroll
-          for (int k = 0; k < RU + 2; ++k) pgu[k] = page_entry(k);
+          for (int j = 0; j < NSLOT; ++j) pg_cur[j] = page_entry(j);
+#pragma unroll
+          for (int j = 0; j < NSLOT; ++j) pg_next[j] = page_entry(j + NSLOT);
         }
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], key_rsrc(PAGED ? pgu[j >> 2] : 0), st_off(j), lg);
+        for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], key_rsrc(pg_cur[j]), st_off(j), lg);
       };
 
       // head weights (used from the first unit on), then the index queries
@@ -418,7 +411,10 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           if constexpr (FP8 && !PAGED) {
             kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
           } else if constexpr (FP8) {
-            kscale = p.k_scale[phys_page(pgu[0]) * page_rows + (pos < len ? (pos & (page_rows - 1)) : 0)];
+            // this lane's sub-tile 4u + lg sits in slot (4 ub + lg) % NSLOT (u0 is a multiple of NSLOT)
+            const int s0 = (4 * ub) % NSLOT;
+            const int32_t e = lg == 0 ? pg_cur[s0] : lg == 1 ? pg_cur[s0 + 1] : lg == 2 ? pg_cur[s0 + 2] : pg_cur[s0 + 3];
+            kscale = p.k_scale[phys_page(e) * page_rows + (pos < len ? (pos & (page_rows - 1)) : 0)];
           }
           float part[TQ][4];
 #pragma unroll
@@ -448,12 +444,9 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
             }
             // refill this slot with the sub-tile NSLOT ahead (nothing is read
             // past the wave's sub-tiles or the sequence's end)
-            load_key_tile<FP8>(slot[j], key_rsrc(PAGED ? pgu[RU] : 0), st_off(x + NSLOT), lg);
-          }
-          if constexpr (PAGED) {  // next unit: shift the entries, fetch the one RU + 2 ahead
-#pragma unroll
-            for (int k = 0; k < RU + 1; ++k) pgu[k] = pgu[k + 1];
-            pgu[RU + 1] = page_entry(u0 + ub + RU + 2);
+            if constexpr (PAGED) pg_cur[j] = pg_next[j];
+            load_key_tile<FP8>(slot[j], key_rsrc(pg_cur[j]), st_off(x + NSLOT), lg);
+            if constexpr (PAGED) pg_next[j] = page_entry(x + 2 * NSLOT);
           }
           if (live) {
             // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
