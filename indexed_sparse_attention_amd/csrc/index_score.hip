@@ -534,13 +534,15 @@ static int env_int(const char* name, int dflt) {
   return (e && *e) ? atoi(e) : dflt;
 }
 
-// Launch shape: DSA_SCORE_VARIANT selects the bf16 key-prefetch depth and
-// occupancy (0, the default: rings of 4 sub-tiles, two workgroups per CU, so
-// two waves per SIMD interleave their loads and MFMAs; 1: rings of 8
-// sub-tiles, one workgroup per CU), DSA_SCORE_WGS_PER_CU overrides the
-// workgroups per CU and DSA_SCORE_WGS the total.  (Measured at the 128K
-// decode shape: variant 0 at 2/CU streams the keys about 4 % faster than
-// variant 1 at 1/CU.)
+// Launch shape: DSA_SCORE_VARIANT selects the bf16 key-prefetch depth,
+// tokens per segment and occupancy (0, the default: one token, rings of 4
+// sub-tiles, two workgroups per CU, so two waves per SIMD interleave their
+// loads and MFMAs; two tokens and one workgroup per CU when there are
+// several query tokens.  1: rings of 8 sub-tiles at one per CU; 2: 8 waves;
+// 3 / 4: two / four tokens), DSA_SCORE_WGS_PER_CU overrides the workgroups
+// per CU and DSA_SCORE_WGS the total.  (Measured at the 128K decode shape:
+// variant 0 at 2/CU streams the keys about 4 % faster than variant 1 at
+// 1/CU.)
 hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream, hipEvent_t ev_start,
                         hipEvent_t ev_stop) {
   if (allow_mfma && score_mfma_supported(p)) {
@@ -553,7 +555,17 @@ hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipS
       switch (variant) {
         case 1: launch_mfma<1, 8, false, 1>(p, grid, stream, ev_start, ev_stop); break;
         case 2: launch_mfma<1, 4, false, 1, 512>(p, grid, stream, ev_start, ev_stop); break;
-        default: launch_mfma<1, 4, false, 2>(p, grid, stream, ev_start, ev_stop); break;
+        case 3: launch_mfma<2, 4, false, 1>(p, grid, stream, ev_start, ev_stop); break;
+        case 4: launch_mfma<4, 4, false, 1>(p, grid, stream, ev_start, ev_stop); break;
+        default:
+          // several query tokens: two per segment, so each key tile feeds twice
+          // the MFMAs (12 % faster at 4096 tokens over 64K keys; four tokens
+          // need one workgroup per CU and were slower)
+          if (p.T >= 2)
+            launch_mfma<2, 4, false, 1>(p, num_cus, stream, ev_start, ev_stop);
+          else
+            launch_mfma<1, 4, false, 2>(p, grid, stream, ev_start, ev_stop);
+          break;
       }
     } else if (p.T == 1) {
       launch_mfma<1, 8, true>(p, grid, stream, ev_start, ev_stop);
