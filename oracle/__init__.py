@@ -10,6 +10,7 @@ Functions take a ``synth.Workload`` (or any object with the same fields)
 and return fp64 numpy arrays:
 
   index_scores(w)          -> scores [B,T,Lmax] (NaN where not visible)
+  mx_quantize(v)           -> (E8M0 byte, E4M3 element values) of one group
   topk(w, scores)          -> (idx [B,T,K] ascending, -1 padded; count [B,T])
   sparse_mla(w, idx)       -> (out [B,T,H,Dv], lse [B,T,H])
   forward(w)               -> dict with all of the above
@@ -79,6 +80,10 @@ def _load():
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_quantize.argtypes = [ctypes.c_double]
         lib.oracle_e4m3_quantize.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_mx_quantize.argtypes = [P, ctypes.c_int, P, P]
+        lib.oracle_mx_quantize.restype = None
         _lib = lib
     return _lib
 
@@ -113,6 +118,24 @@ def e4m3_value(code: int) -> float:
 
 def e4m3_quantize(x: float) -> float:
     return _load().oracle_e4m3_quantize(x)
+
+
+def e8m0_value(e: int) -> float:
+    return _load().oracle_e8m0_value(e)
+
+
+def mx_quantize(values) -> tuple:
+    """MX quantisation of one group of at most 32 values to E4M3 elements.
+
+    Returns (E8M0 scale byte, element values as float64); the group's
+    dequantised values are ``elements * 2**(byte - 127)``.
+    """
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64).ravel())
+    assert 1 <= v.size <= 32
+    e = np.zeros(1, np.uint8)
+    out = np.zeros(v.size, np.float64)
+    _load().oracle_mx_quantize(_p(v), v.size, _p(e), _p(out))
+    return int(e[0]), out
 
 
 def index_scores(w, want=None) -> np.ndarray:

@@ -29,13 +29,20 @@
  * token t sees positions 0 .. len - T + t (causal).
  *
  * Input encodings (decoded here with our own bit-field decoders):
- *   dtype 0 = IEEE f32, 1 = bf16, 2 = OCP FP8 E4M3 (bias 7, no inf, max 448).
- * FP8 index keys and latent rows carry one power-of-two scale per row
- * ("Inference Acceleration ..." §4.1/§4.2 describe group scales; one scale per
- * row is the case where every group of a row shares its scale).  With FP8
- * index keys the index query is quantised to E4M3 (round to nearest even,
- * saturating at +-448) before the dot product, as that page's §4.1 quantises
- * both index Q and K.
+ *   dtype 0 = IEEE f32, 1 = bf16, 2 = OCP FP8 E4M3 (bias 7, no inf, max 448),
+ *   3 = MXFP8: E4M3 elements with one E8M0 scale byte per 32 consecutive
+ *       elements of a row (index keys),
+ *   4 = E4M3 elements with one fp32 scale per 128 consecutive elements of a
+ *       row (latent rows).
+ * dtype 2 carries one scale per row ("Inference Acceleration ..." §4.1/§4.2
+ * describe group scales; one scale per row is the case where every group of a
+ * row shares its scale); with such index keys the index query is quantised to
+ * E4M3 (round to nearest even, saturating at +-448) before the dot product, as
+ * that page's §4.1 quantises both index Q and K.  dtype 3 and 4 are the
+ * pages' own granularities: groups of 32 for index Q and K (§4.1 there, and
+ * "Layered Quantization" on the page "Long-Context LLM Inference
+ * Optimization", which names MXFP8), tiles of 128 per token for the main
+ * cache (§4.2 there).
  */
 #include <math.h>
 #include <omp.h>
@@ -92,12 +99,54 @@ double oracle_e4m3_quantize(double x) {
   return x < 0 ? -best : best;
 }
 
+/* E8M0 (the MX scale format): an unsigned biased exponent, value 2^(e-127);
+ * 0xFF is NaN. */
+double oracle_e8m0_value(uint8_t e) { return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127); }
+
+/*
+ * MX quantisation of one group of n <= 32 values to E4M3 elements and a
+ * shared E8M0 scale, following the conversion the OCP Microscaling (MX)
+ * Formats Specification v1.0 gives: the shared exponent is floor(log2 of the
+ * group's largest magnitude) minus the exponent of the element format's
+ * largest power of two (8 for E4M3, whose largest normal is 1.75 * 2^8), kept
+ * within E8M0's range; each element is the nearest E4M3 value of v / 2^shared,
+ * saturating.  An all-zero group gets the smallest scale and zero elements.
+ * Outputs the scale byte and the element values (E4M3 values, not codes).
+ * Values must be finite.
+ */
+void oracle_mx_quantize(const double* v, int n, uint8_t* scale, double* elem) {
+  double amax = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  int shared = -127;
+  if (amax > 0.0) {
+    int ex;
+    frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    shared = (ex - 1) - 8;
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+  }
+  *scale = (uint8_t)(shared + 127);
+  for (int i = 0; i < n; ++i) elem[i] = oracle_e4m3_quantize(ldexp(v[i], -shared));
+}
+
+/* Element value of a stored input (dtypes 3 and 4 store E4M3 codes). */
 static double load(const void* p, int dtype, int64_t i) {
   switch (dtype) {
     case 0: return (double)((const float*)p)[i];
     case 1: return oracle_bf16_value(((const uint16_t*)p)[i]);
     default: return oracle_e4m3_value(((const uint8_t*)p)[i]);
   }
+}
+
+/* Decoded value of column i of row r of a latent cache with Dqk columns:
+ * the element times its scale (per row for dtype 2, per 128-column tile for
+ * dtype 4, none otherwise). */
+static double kv_value(const void* kv, int dtype, const float* kv_scale, int64_t r, int Dqk, int i) {
+  double v = load(kv, dtype, r * Dqk + i);
+  if (dtype == 2) return v * (double)kv_scale[r];
+  if (dtype == 4) return v * (double)kv_scale[r * ((Dqk + 127) / 128) + i / 128];
+  return v;
 }
 
 static int64_t visible(const oracle_dims* d, const int32_t* seq_lens, int b, int t) {
@@ -109,16 +158,20 @@ static int64_t visible(const oracle_dims* d, const int32_t* seq_lens, int b, int
 /* ---------------- 1. indexer scores ---------------- */
 /*
  * scores: [B, T, Lmax] fp64; entries s >= vis are set to NaN (not visible).
- * k_scale: [B, Lmax] (one power-of-two per key row) or NULL.
+ * k_scale: NULL for f32/bf16 keys; fp32 [B, Lmax] (one scale per key row) for
+ * dtype 2; E8M0 bytes [B, Lmax, ceil(Di/32)] for dtype 3 (MXFP8), with which
+ * each index query head is MX-quantised per group of 32 (oracle_mx_quantize)
+ * and the dot product is that of the two dequantised vectors.
  * Only queries with want[b*T+t] != 0 are computed (want == NULL: all).
  */
 int oracle_index_scores(const oracle_dims* d, const void* q_idx, const float* head_w,
-                        const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                        const void* k_idx, const void* k_scale, const int32_t* seq_lens,
                         const uint8_t* want, double* scores) {
   const int B = d->batch, T = d->q_len, Hi = d->idx_heads, Di = d->idx_dim;
   const int64_t L = d->max_seq_len;
-  const int fp8_keys = (d->idx_key_dtype == 2);
+  const int kd = d->idx_key_dtype, G = (Di + 31) / 32;
   double* qd = (double*)malloc(sizeof(double) * Hi * Di);
+  double* grp = (double*)malloc(sizeof(double) * 32);
   for (int b = 0; b < B; ++b) {
     for (int t = 0; t < T; ++t) {
       int64_t bt = (int64_t)b * T + t;
@@ -128,17 +181,28 @@ int oracle_index_scores(const oracle_dims* d, const void* q_idx, const float* he
       for (int h = 0; h < Hi; ++h)
         for (int i = 0; i < Di; ++i) {
           double v = load(q_idx, d->q_idx_dtype, (bt * Hi + h) * Di + i);
-          qd[h * Di + i] = fp8_keys ? oracle_e4m3_quantize(v) : v;
+          qd[h * Di + i] = kd == 2 ? oracle_e4m3_quantize(v) : v;
         }
+      if (kd == 3) /* dynamic MX quantisation of the query, group by group */
+        for (int h = 0; h < Hi; ++h)
+          for (int g = 0; g < G; ++g) {
+            const int n = (Di - 32 * g) < 32 ? (Di - 32 * g) : 32;
+            uint8_t e;
+            oracle_mx_quantize(qd + h * Di + 32 * g, n, &e, grp);
+            for (int i = 0; i < n; ++i) qd[h * Di + 32 * g + i] = grp[i] * oracle_e8m0_value(e);
+          }
 #pragma omp parallel
       {
         double* k = (double*)malloc(sizeof(double) * Di);
 #pragma omp for schedule(static)
         for (int64_t s = 0; s < L; ++s) {
           if (s >= vis) { out[s] = NAN; continue; }
-          const int64_t krow = ((int64_t)b * L + s) * Di;
-          double scale = k_scale ? (double)k_scale[(int64_t)b * L + s] : 1.0;
-          for (int i = 0; i < Di; ++i) k[i] = load(k_idx, d->idx_key_dtype, krow + i);
+          const int64_t r = (int64_t)b * L + s, krow = r * Di;
+          double scale = kd == 2 ? (double)((const float*)k_scale)[r] : 1.0;
+          for (int i = 0; i < Di; ++i) {
+            k[i] = load(k_idx, kd, krow + i);
+            if (kd == 3) k[i] *= oracle_e8m0_value(((const uint8_t*)k_scale)[r * G + i / 32]);
+          }
           double S = 0.0;
           for (int h = 0; h < Hi; ++h) {
             double dot = 0.0;
@@ -153,6 +217,7 @@ int oracle_index_scores(const oracle_dims* d, const void* q_idx, const float* he
     }
   }
   free(qd);
+  free(grp);
   return 0;
 }
 
@@ -213,7 +278,8 @@ int oracle_topk(const oracle_dims* d, const double* scores, const int32_t* seq_l
 
 /* ---------------- 3. sparse attention over the selected rows ---------------- */
 /*
- * q: [B,T,H,Dqk]; kv: [B,Lmax,Dqk] (+ kv_scale [B,Lmax] or NULL);
+ * q: [B,T,H,Dqk]; kv: [B,Lmax,Dqk] (+ kv_scale: [B,Lmax] for dtype 2,
+ * [B,Lmax,ceil(Dqk/128)] for dtype 4, else NULL);
  * idx: [B,T,K]; entries outside [0, len_b) are not selected rows.
  * out: [B,T,H,Dv] fp64; lse: [B,T,H] fp64 (natural log of the softmax
  * normaliser of the scaled logits) or NULL.  No selected row: out = 0,
@@ -242,11 +308,10 @@ int oracle_sparse_mla(const oracle_dims* d, const void* q, const void* kv, const
         for (int i = 0; i < Dqk; ++i) qv[i] = load(q, d->q_dtype, (bt * H + h) * Dqk + i);
         for (int j = 0; j < K; ++j)
           if (sel[j] >= 0 && sel[j] < len) rows[n++] = (int64_t)b * L + sel[j];
-        /* logits z_j = scale * q . c_j (the row decoded and multiplied by its scale) */
+        /* logits z_j = scale * q . c_j (the row decoded: elements times their scales) */
         for (int j = 0; j < n; ++j) {
-          double sc = kv_scale ? (double)kv_scale[rows[j]] : 1.0;
           double dot = 0.0;
-          for (int i = 0; i < Dqk; ++i) dot += qv[i] * (load(kv, d->kv_dtype, rows[j] * Dqk + i) * sc);
+          for (int i = 0; i < Dqk; ++i) dot += qv[i] * kv_value(kv, d->kv_dtype, kv_scale, rows[j], Dqk, i);
           z[j] = d->softmax_scale * dot;
         }
         for (int v = 0; v < Dv; ++v) o[v] = 0.0;
@@ -261,8 +326,7 @@ int oracle_sparse_mla(const oracle_dims* d, const void* q, const void* kv, const
           /* weighted sum of the value part (first Dv columns) of each row */
           for (int j = 0; j < n; ++j) {
             double p = z[j] / Z;
-            double sc = kv_scale ? (double)kv_scale[rows[j]] : 1.0;
-            for (int v = 0; v < Dv; ++v) c[v] = load(kv, d->kv_dtype, rows[j] * Dqk + v) * sc;
+            for (int v = 0; v < Dv; ++v) c[v] = kv_value(kv, d->kv_dtype, kv_scale, rows[j], Dqk, v);
             for (int v = 0; v < Dv; ++v) o[v] += p * c[v];
           }
           if (lse) lse[bt * H + h] = m + log(Z);
@@ -292,10 +356,9 @@ int oracle_attention_weights(const oracle_dims* d, const void* q, const void* kv
     p_out[j] = -INFINITY;
     if (sel[j] < 0 || sel[j] >= len) continue;
     int64_t r = (int64_t)b * L + sel[j];
-    double sc = kv_scale ? (double)kv_scale[r] : 1.0;
     double dot = 0.0;
     for (int i = 0; i < Dqk; ++i)
-      dot += load(q, d->q_dtype, (bt * H + h) * Dqk + i) * (load(kv, d->kv_dtype, r * Dqk + i) * sc);
+      dot += load(q, d->q_dtype, (bt * H + h) * Dqk + i) * kv_value(kv, d->kv_dtype, kv_scale, r, Dqk, i);
     p_out[j] = d->softmax_scale * dot;
     if (p_out[j] > m) m = p_out[j];
   }

@@ -16,6 +16,9 @@ scaled as listed:
   prefill64k B=1, T=4096, L=65536 (61440 cached + 4096 new), causal, as decode8k
   fp8_1m    B=4,  T=2,    L=1048576,    e4m3 index keys and latent cache with one
             power-of-two scale per token in {2^-2..2^2}; bf16 queries
+  mx128k    as decode128k, with MXFP8 index keys (e4m3 integers, one E8M0 scale
+            byte 2^-2..2^2 per 32 dims) and an e4m3 latent cache with one
+            power-of-two scale 2^-2..2^2 per 128-column tile of each row
 
 Index inputs are integers so every score is an exactly representable integer.
 """
@@ -34,9 +37,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
-F32, BF16, E4M3 = 0, 1, 2
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", E4M3: "e4m3"}
-_NP = {F32: np.float32, BF16: np.uint16, E4M3: np.uint8}
+F32, BF16, E4M3, MXE4M3, E4M3T128 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", E4M3: "e4m3", MXE4M3: "mxfp8", E4M3T128: "e4m3-t128"}
+_NP = {F32: np.float32, BF16: np.uint16, E4M3: np.uint8, MXE4M3: np.uint8, E4M3T128: np.uint8}
+MX_GROUP, KV_TILE = 32, 128
 
 # tensor ids of the stream keys
 T_QIDX, T_KIDX, T_W, T_Q, T_KV, T_LENS, T_KSCALE, T_KVSCALE = 1, 2, 3, 4, 5, 6, 7, 8
@@ -64,11 +68,13 @@ def _load():
         lib.synth_fill_i32.argtypes = [P, I64, U64, U64, I64, I64]
         lib.synth_fill_pow2_scale.argtypes = [P, I64, U64, U64, I, I]
         lib.synth_fill_normal_e4m3_scaled.argtypes = [P, P, I64, I64, U64, U64]
+        lib.synth_fill_normal_e4m3_tiled.argtypes = [P, P, I64, I64, I64, U64, U64]
         lib.synth_raw.argtypes = [P, I64, U64, U64]
         lib.synth_splitmix64_from_state.argtypes = [U64, I64, P]
         lib.synth_splitmix64_from_state.restype = None
         for f in (lib.synth_fill_int, lib.synth_fill_normal, lib.synth_fill_i32,
-                  lib.synth_fill_pow2_scale, lib.synth_fill_normal_e4m3_scaled, lib.synth_raw):
+                  lib.synth_fill_pow2_scale, lib.synth_fill_normal_e4m3_scaled,
+                  lib.synth_fill_normal_e4m3_tiled, lib.synth_raw):
             f.restype = None
         _lib = lib
     return _lib
@@ -127,6 +133,22 @@ def normals_e4m3(shape, scale: np.ndarray, seed: int, tensor_id: int) -> np.ndar
     return out
 
 
+def normals_e4m3_tiled(shape, scale: np.ndarray, tile: int, seed: int, tensor_id: int) -> np.ndarray:
+    """e4m3 codes of N(0,1)/scale[row, tile]; scale has shape [rows, ceil(row_len/tile)]."""
+    out = np.empty(shape, np.uint8)
+    row_len = shape[-1]
+    n_rows = out.size // row_len
+    assert scale.size == n_rows * -(-row_len // tile) and scale.dtype == np.float32
+    _load().synth_fill_normal_e4m3_tiled(_ptr(out), _ptr(np.ascontiguousarray(scale)),
+                                         n_rows, row_len, tile, seed, tensor_id)
+    return out
+
+
+def e8m0_scales(shape, elo: int, ehi: int, seed: int, tensor_id: int) -> np.ndarray:
+    """E8M0 scale bytes 127 + e with e uniform on [elo, ehi] (scale 2^e)."""
+    return (i32(shape, elo, ehi, seed, tensor_id) + 127).astype(np.uint8)
+
+
 @dataclasses.dataclass
 class Workload:
     """One seeded DSA problem instance (host arrays, C-contiguous)."""
@@ -150,10 +172,10 @@ class Workload:
     q_idx: np.ndarray             # [B,T,Hi,Di]
     head_w: np.ndarray            # [B,T,Hi] float32
     k_idx: np.ndarray             # [B,Lmax,Di]
-    k_scale: Optional[np.ndarray]  # [B,Lmax] float32 or None
+    k_scale: Optional[np.ndarray]  # [B,Lmax] float32 (e4m3), [B,Lmax,Di/32] uint8 E8M0 (mxfp8) or None
     q: np.ndarray                 # [B,T,H,Dqk]
     kv: np.ndarray                # [B,Lmax,Dqk]
-    kv_scale: Optional[np.ndarray]  # [B,Lmax] float32 or None
+    kv_scale: Optional[np.ndarray]  # [B,Lmax] float32 (e4m3), [B,Lmax,ceil(Dqk/128)] (e4m3-t128) or None
     seed: int
 
     def vis(self, b: int, t: int) -> int:
@@ -190,6 +212,11 @@ WORKLOADS = {
                    w_int=(1, 8), heads=128, qk_dim=576, v_dim=512, top_k=2048,
                    idx_dtype=BF16, q_dtype=BF16, kv_dtype=E4M3, out_dtype=BF16, fp8=True,
                    scale_exp=(-2, 2)),
+    "mx128k": dict(number=6, batch=8, q_len=1, max_seq_len=131072,
+                   len_range=(98304, 131072), idx_heads=64, idx_dim=128, idx_int=(-4, 4),
+                   w_int=(1, 8), heads=128, qk_dim=576, v_dim=512, top_k=2048,
+                   idx_dtype=BF16, q_dtype=BF16, kv_dtype=E4M3T128, out_dtype=BF16, fp8="mx",
+                   scale_exp=(-2, 2)),
 }
 
 
@@ -217,7 +244,14 @@ def make(name: str, seed: Optional[int] = None, **overrides) -> Workload:
     fp8 = r["fp8"]
     q_idx = ints((B, T, Hi, Di), r["idx_dtype"], ilo, ihi, seed, T_QIDX)
     head_w = ints((B, T, Hi), F32, r["w_int"][0], r["w_int"][1], seed, T_W)
-    if fp8:
+    if fp8 == "mx":
+        elo, ehi = r["scale_exp"]
+        k_idx = ints((B, L, Di), E4M3, ilo, ihi, seed, T_KIDX)
+        k_scale = e8m0_scales((B, L, -(-Di // MX_GROUP)), elo, ehi, seed, T_KSCALE)
+        kv_scale = pow2_scales((B, L, -(-Dqk // KV_TILE)), elo, ehi, seed, T_KVSCALE)
+        kv = normals_e4m3_tiled((B, L, Dqk), kv_scale, KV_TILE, seed, T_KV)
+        key_dtype = MXE4M3
+    elif fp8:
         elo, ehi = r["scale_exp"]
         k_idx = ints((B, L, Di), E4M3, ilo, ihi, seed, T_KIDX)
         k_scale = pow2_scales((B, L), elo, ehi, seed, T_KSCALE)

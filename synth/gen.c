@@ -99,7 +99,8 @@ static uint8_t e4m3_encode_rne_sat(double x) {
 }
 
 /* ---------------------------------------------------------------------- */
-/* Exported fillers.  dtype: 0 = f32, 1 = bf16, 2 = e4m3.                  */
+/* Exported fillers.  dtype: 0 = f32, 1 = bf16, 2 = e4m3 (and 3, 4: e4m3 */
+/* codes of the scaled formats, whose scales are filled separately).      */
 /* ---------------------------------------------------------------------- */
 
 static void store(void* out, int dtype, int64_t i, double v) {
@@ -156,6 +157,24 @@ void synth_fill_normal_e4m3_scaled(uint8_t* codes, const float* scale, int64_t n
     for (int64_t j = 0; j < row_len; ++j) {
       int64_t i = r * row_len + j;
       codes[i] = e4m3_encode_rne_sat(draw_normal(h, (uint64_t)i) * inv);
+    }
+  }
+}
+
+/*
+ * As above with one scale per tile of `tile` consecutive values of a row:
+ * value j of row r is divided by scale[r * ceil(row_len / tile) + j / tile].
+ */
+void synth_fill_normal_e4m3_tiled(uint8_t* codes, const float* scale, int64_t n_rows,
+                                  int64_t row_len, int64_t tile, uint64_t seed, uint64_t tensor_id) {
+  uint64_t h = stream_base(seed, tensor_id);
+  const int64_t nt = (row_len + tile - 1) / tile;
+  e4m3_table();
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int64_t j = 0; j < row_len; ++j) {
+      int64_t i = r * row_len + j;
+      codes[i] = e4m3_encode_rne_sat(draw_normal(h, (uint64_t)i) / (double)scale[r * nt + j / tile]);
     }
   }
 }

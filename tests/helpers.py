@@ -34,7 +34,8 @@ def problem(q_idx, head_w, k_idx, q=None, kv=None, seq_lens=None, top_k=4, k_sca
         kv_dtype=kv_dtype, out_dtype=synth.F32,
         seq_lens=np.ascontiguousarray(seq_lens, dtype=np.int32), q_idx=q_idx,
         head_w=np.ascontiguousarray(head_w, dtype=np.float32), k_idx=k_idx,
-        k_scale=None if k_scale is None else np.ascontiguousarray(k_scale, dtype=np.float32),
+        k_scale=None if k_scale is None else np.ascontiguousarray(
+            k_scale, dtype=np.uint8 if idx_key_dtype == synth.MXE4M3 else np.float32),
         q=q, kv=kv,
         kv_scale=None if kv_scale is None else np.ascontiguousarray(kv_scale, dtype=np.float32),
         seed=0)

@@ -349,3 +349,158 @@ def test_attention_fp8_cache_with_row_scales_equals_decoded_f32():
     a, _ = oracle.sparse_mla(mk(codes, synth.E4M3, scale), idx)
     b, _ = oracle.sparse_mla(mk(vals.astype(np.float32), synth.F32, None), idx)
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ MXFP8 index keys
+# The pages quantise index Q and K in groups of 32 with one scale each
+# ("Inference Acceleration for New Large Model Architectures" §4.1) in the MXFP8
+# format ("Long-Context LLM Inference Optimization", Layered Quantization).  The
+# quantiser follows the OCP MX v1.0 conversion (shared exponent floor(log2 amax)
+# minus 8, saturating E4M3 elements).
+
+def test_e8m0_decoder_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([oracle.e8m0_value(int(c)) for c in codes])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+
+
+def test_mx_quantize_closed_forms():
+    e, el = oracle.mx_quantize(np.ones(32))
+    assert e == 127 - 8 and np.all(el == 256.0)          # 1 = 256 * 2^-8
+    e, el = oracle.mx_quantize([1.875, 1.0, -0.5])
+    assert e == 119 and list(el) == [448.0, 256.0, -128.0]  # 480 saturates to 448
+    e, el = oracle.mx_quantize([0.0] * 8)
+    assert e == 0 and np.all(el == 0.0)
+    e, el = oracle.mx_quantize([2.0 ** 10, 3.0])            # amax a power of two -> 256
+    assert e == 127 + 10 - 8 and list(el) == [256.0, 0.75]
+    e, el = oracle.mx_quantize([2.0 ** -130])              # shared exponent clamps at -127
+    assert e == 0 and list(el) == [0.125]
+    e, el = oracle.mx_quantize([2.0 ** 140, -2.0 ** 139])  # and at +127: elements saturate
+    assert e == 254 and list(el) == [448.0, -448.0]
+
+
+def test_mx_quantize_error_bound_and_top_binade():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        v = rng.normal(size=32) * 2.0 ** rng.integers(-20, 20)
+        if trial % 7 == 0:
+            v[rng.integers(0, 32)] *= 1000.0  # an outlier in the group
+        e, el = oracle.mx_quantize(v)
+        X = 2.0 ** (e - 127)
+        deq = el * X
+        # the largest magnitude lands in E4M3's top binade [256, 512) before saturation
+        assert 256.0 <= np.max(np.abs(v)) / X < 512.0
+        for x, d, q in zip(v, deq, el):
+            if abs(x) / X > 448.0:
+                assert q == math.copysign(448.0, x)
+            else:  # half an ulp: 2^-4 relative for normals, 2^-10 * X for subnormals
+                assert abs(d - x) <= max(abs(x) * 2.0 ** -4, X * 2.0 ** -10) * (1 + 1e-12)
+
+
+def _mx_problem(q_idx, head_w, codes, scale_bytes, seq_lens=None):
+    return problem(q_idx, head_w, codes, k_scale=scale_bytes, idx_key_dtype=synth.MXE4M3,
+                   q_idx_dtype=synth.F32, seq_lens=seq_lens)
+
+
+def test_mx_scores_equal_exact_dot_products_of_decoded_keys():
+    # Queries whose groups quantise exactly (integers up to 4, plus an outlier
+    # group: each group has its own scale so the small groups stay exact):
+    # the score is the plain definition over the decoded keys.
+    rng = np.random.default_rng(5)
+    B, T, Hi, Di, L = 2, 2, 3, 96, 11
+    qi = rng.integers(-4, 5, (B, T, Hi, Di)).astype(np.float32)
+    qi[0, 0, 1, :32] *= 64.0  # group 0 of one head much larger than its other groups
+    codes = rng.integers(0, 0x7F, (B, L, Di)).astype(np.uint8) | (rng.integers(0, 2, (B, L, Di)) << 7).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    sb = rng.integers(120, 135, (B, L, Di // 32)).astype(np.uint8)
+    wh = rng.integers(1, 6, (B, T, Hi)).astype(np.float32)
+    got = oracle.index_scores(_mx_problem(qi, wh, codes, sb))
+    kdec = np.array([[[oracle.e4m3_value(int(c)) * oracle.e8m0_value(int(sb[b, s, i // 32]))
+                       for i, c in enumerate(codes[b, s])] for s in range(L)] for b in range(B)])
+    for b in range(B):
+        for t in range(T):
+            vis = L - T + 1 + t
+            dots = qi[b, t].astype(np.float64) @ kdec[b, :vis].T  # [Hi, vis]
+            want = (wh[b, t][:, None] * np.maximum(dots, 0.0)).sum(0)
+            assert np.array_equal(got[b, t, :vis], want)
+            assert np.all(np.isnan(got[b, t, vis:]))
+
+
+def test_mx_scores_reduce_to_row_scaled_fp8_when_group_scales_agree():
+    rng = np.random.default_rng(6)
+    B, T, Hi, Di, L = 1, 1, 4, 64, 9
+    qi = rng.integers(-4, 5, (B, T, Hi, Di)).astype(np.float32)
+    codes = (rng.integers(0, 9, (B, L, Di)) * 8 + 0x30).astype(np.uint8)  # values 0.5 .. 16
+    codes |= (rng.integers(0, 2, (B, L, Di)) << 7).astype(np.uint8)
+    ex = rng.integers(-3, 4, (B, L))
+    wh = np.ones((B, T, Hi), np.float32)
+    mx = oracle.index_scores(_mx_problem(qi, wh, codes, np.repeat((ex + 127)[..., None], 2, -1)))
+    row = oracle.index_scores(problem(qi, wh, codes, k_scale=2.0 ** ex, idx_key_dtype=synth.E4M3))
+    assert np.array_equal(mx, row, equal_nan=True)
+
+
+def test_mx_scores_scale_equivariance_and_group_locality():
+    rng = np.random.default_rng(8)
+    B, T, Hi, Di, L = 1, 1, 2, 128, 7
+    qi = rng.normal(size=(B, T, Hi, Di)).astype(np.float32)  # quantisation rounds here
+    codes = rng.integers(0, 0x7E, (B, L, Di)).astype(np.uint8)
+    sb = rng.integers(124, 131, (B, L, 4)).astype(np.uint8)
+    wh = np.array([[[1.0, 2.0]]], np.float32)
+    base = oracle.index_scores(_mx_problem(qi, wh, codes, sb))
+    # doubling the query doubles every group's scale and leaves the elements
+    assert np.array_equal(oracle.index_scores(_mx_problem(2 * qi, wh, codes, sb)), 2 * base, equal_nan=True)
+    # one more in every scale byte of row 3 doubles that row's score only
+    sb2 = sb.copy()
+    sb2[0, 3] += 1
+    s2 = oracle.index_scores(_mx_problem(qi, wh, codes, sb2))
+    assert s2[0, 0, 3] == 2 * base[0, 0, 3]
+    assert np.array_equal(np.delete(s2, 3, axis=2), np.delete(base, 3, axis=2), equal_nan=True)
+    # zeroing the key elements of group 2 of row 1 equals dropping that group's products
+    c3 = codes.copy()
+    c3[0, 1, 64:96] = 0
+    s3 = oracle.index_scores(_mx_problem(qi, wh, c3, sb))
+    qdeq = np.zeros((Hi, Di))
+    for h in range(Hi):
+        for g in range(4):
+            e, el = oracle.mx_quantize(qi[0, 0, h, 32 * g:32 * g + 32].astype(np.float64))
+            qdeq[h, 32 * g:32 * g + 32] = el * 2.0 ** (e - 127)
+    kdec = np.array([oracle.e4m3_value(int(c)) for c in c3[0, 1]]) * \
+        np.repeat([2.0 ** (int(x) - 127) for x in sb[0, 1]], 32)
+    assert math.isclose(s3[0, 0, 1], float((wh[0, 0] * np.maximum(qdeq @ kdec, 0)).sum()), rel_tol=1e-12)
+
+
+# ------------------------------------------------------------------ FP8 cache, 128-column tiles
+# One scale per token and 128-element tile of the main cache ("Inference
+# Acceleration for New Large Model Architectures" §4.2).
+
+def test_attention_tile_scales_single_row_reproduces_decoded_row():
+    B, T, H, Dqk, Dv, L, K = 1, 1, 2, 300, 260, 4, 3  # tiles of 128, 128, 44 columns
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 0x7E, (B, L, Dqk)).astype(np.uint8) | (rng.integers(0, 2, (B, L, Dqk)) << 7).astype(np.uint8)
+    scale = np.array([[[0.5, 4.0, 0.25]] * L], np.float32) * (1 + np.arange(L))[None, :, None].astype(np.float32)
+    q = rng.normal(size=(B, T, H, Dqk)).astype(np.float32)
+    w = problem(np.zeros((B, T, 1, 1), np.float32), np.ones((B, T, 1), np.float32),
+                np.zeros((B, L, 1), np.float32), q=q, kv=codes, top_k=K, v_dim=Dv,
+                kv_dtype=synth.E4M3T128, kv_scale=scale, softmax_scale=0.125)
+    out, lse = oracle.sparse_mla(w, np.array([[[2, -1, -1]]], np.int32))
+    row = torch.from_numpy(codes[0, 2]).view(torch.float8_e4m3fn).double().numpy() * \
+        np.repeat(scale[0, 2], [128, 128, 44])
+    assert np.array_equal(out[0, 0], np.stack([row[:Dv]] * H))
+    np.testing.assert_allclose(lse[0, 0], 0.125 * (q[0, 0].astype(np.float64) @ row), rtol=1e-13)
+
+
+def test_attention_tile_scales_reduce_to_row_scales():
+    B, T, H, Dqk, Dv, L, K = 1, 2, 3, 256 + 64, 256, 10, 4
+    rng = np.random.default_rng(10)
+    codes = rng.integers(0, 0x7E, (B, L, Dqk)).astype(np.uint8)
+    rs = (2.0 ** rng.integers(-2, 3, (B, L))).astype(np.float32)
+    q = rng.normal(size=(B, T, H, Dqk)).astype(np.float32)
+    idx = np.array([[[1, 3, 7, 9], [0, 2, 5, -1]]], np.int32)
+    mk = lambda kvd, sc: problem(np.zeros((B, T, 1, 1), np.float32), np.ones((B, T, 1), np.float32),
+                                 np.zeros((B, L, 1), np.float32), q=q, kv=codes, top_k=K, v_dim=Dv,
+                                 kv_dtype=kvd, kv_scale=sc)
+    a = oracle.sparse_mla(mk(synth.E4M3T128, np.repeat(rs[..., None], 3, -1)), idx)
+    b = oracle.sparse_mla(mk(synth.E4M3, rs), idx)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

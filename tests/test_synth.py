@@ -62,7 +62,10 @@ def test_recipes_shapes_small():
         assert w.kv.shape == (2, L, w.qk_dim)
         assert w.head_w.shape == (2, T, w.idx_heads)
         assert np.all((w.seq_lens >= L // 2) & (w.seq_lens <= L))
-        assert (w.k_scale is not None) == (name == "fp8_1m")
+        assert (w.k_scale is not None) == (name in ("fp8_1m", "mx128k"))
+        if name == "mx128k":  # one E8M0 byte per 32 dims, one scale per 128-column tile
+            assert w.k_scale.shape == (2, L, w.idx_dim // 32) and w.k_scale.dtype == np.uint8
+            assert w.kv_scale.shape == (2, L, -(-w.qk_dim // 128))
         assert abs(w.softmax_scale - w.qk_dim ** -0.5) < 1e-15
 
 
