@@ -154,11 +154,12 @@ def algorithmic_bytes(w):
     """Bytes the path must move per step: index keys once per sequence, the
     selected latent rows, queries, weights, outputs and index lists."""
     import numpy as np
-    kb = {0: 4, 1: 2, 2: 1}[w.idx_key_dtype]
-    cb = {0: 4, 1: 2, 2: 1}[w.kv_dtype]
+    kb = {0: 4, 1: 2, 2: 1, 3: 1}[w.idx_key_dtype]
+    cb = {0: 4, 1: 2, 2: 1, 4: 1}[w.kv_dtype]
     ob = {0: 4, 1: 2}[w.out_dtype]
-    ks = 4 if w.k_scale is not None else 0
-    vs = 4 if w.kv_scale is not None else 0
+    # scale bytes per row: fp32 per row, E8M0 bytes per 32 dims, fp32 per 128-column tile
+    ks = 0 if w.k_scale is None else w.k_scale.itemsize * int(np.prod(w.k_scale.shape[2:], dtype=np.int64))
+    vs = 0 if w.kv_scale is None else w.kv_scale.itemsize * int(np.prod(w.kv_scale.shape[2:], dtype=np.int64))
     qb = {0: 4, 1: 2}[w.q_dtype]
     lens = np.minimum(w.seq_lens.astype(np.int64), w.max_seq_len)
     keys = int(lens.sum()) * (w.idx_dim * kb + ks)
@@ -213,7 +214,8 @@ def main():
     k_copies = [k0] + [k0.clone() for _ in range(R - 1)]
     kv_copies = [kv0] + [kv0.clone() for _ in range(R - 1)]
     out_dtype = torch.float32 if w.out_dtype == synth.F32 else torch.bfloat16
-    prob = dsa.forward_problem(q_idx, k0, q, kv0, seq_lens, w.top_k, w.v_dim, w.softmax_scale, out_dtype)
+    prob = dsa.forward_problem(q_idx, k0, q, kv0, seq_lens, w.top_k, w.v_dim, w.softmax_scale, out_dtype,
+                               k_scale, kv_scale)
     ws = torch.zeros(dsa.forward_workspace_size(prob), dtype=torch.uint8, device=dev)  # counters start at zero
     B, T, H = w.batch, w.q_len, w.heads
     outs = {"out": torch.empty((B, T, H, w.v_dim), dtype=out_dtype, device=dev),
@@ -244,7 +246,8 @@ def main():
 
         k_copies = [pool(k, (w.idx_dim,)) for k in k_copies]
         kv_copies = [pool(kv, (w.qk_dim,)) for kv in kv_copies]
-        k_scale, kv_scale = pool(k_scale, ()), pool(kv_scale, ())
+        k_scale = pool(k_scale, tuple(w.k_scale.shape[2:])) if k_scale is not None else None
+        kv_scale = pool(kv_scale, tuple(w.kv_scale.shape[2:])) if kv_scale is not None else None
         torch.cuda.synchronize()
 
     def step(r, stage_events=None):
@@ -362,7 +365,8 @@ def main():
     line = {
         "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {synth.F32: "f32", synth.BF16: "bf16"}.get(w.idx_key_dtype, "fp8-e4m3/bf16"),
+        "vs_baseline": None, "dtype": {synth.F32: "f32", synth.BF16: "bf16",
+                                       synth.MXE4M3: "mxfp8-e4m3/bf16"}.get(w.idx_key_dtype, "fp8-e4m3/bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_len": T, "max_seq_len": w.max_seq_len,
                    "mean_len": float(np.mean(w.seq_lens)), "top_k": w.top_k,

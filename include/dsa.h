@@ -75,9 +75,21 @@ typedef enum dsa_status {
 } dsa_status;
 
 typedef enum dsa_dtype {
-  DSA_F32 = 0,      /* IEEE binary32 */
-  DSA_BF16 = 1,     /* bfloat16 (upper half of binary32) */
-  DSA_FP8_E4M3 = 2  /* OCP FP8 E4M3: bias 7, no infinities, max 448, 0x7F/0xFF NaN */
+  DSA_F32 = 0,       /* IEEE binary32 */
+  DSA_BF16 = 1,      /* bfloat16 (upper half of binary32) */
+  DSA_FP8_E4M3 = 2,  /* OCP FP8 E4M3: bias 7, no infinities, max 448, 0x7F/0xFF NaN;
+                        one fp32 scale per row */
+  /* Index keys only: OCP MXFP8, E4M3 elements with one E8M0 scale byte
+   * (value 2^(e-127); 0xFF, NaN, must not occur) per 32 consecutive elements
+   * of a row, the last group of a row shorter when idx_dim % 32 != 0: the
+   * group-wise index quantisation of "Inference Acceleration for New Large
+   * Model Architectures" §4.1 in the format that "Long-Context LLM Inference
+   * Optimization" (Layered Quantization) names. */
+  DSA_MXFP8_E4M3 = 3,
+  /* Latent cache only: E4M3 elements with one fp32 scale per 128 consecutive
+   * elements of a row (ceil(qk_dim / 128) scales per row), the per-token,
+   * per-tile cache quantisation of "Inference Acceleration ..." §4.2. */
+  DSA_FP8_E4M3_T128 = 4
 } dsa_dtype;
 
 /*
@@ -88,7 +100,8 @@ typedef enum dsa_dtype {
  * heads of idx_dim each score every visible position s as
  *     S[s] = sum_h head_w[h] * max(0, q_idx[h,:] . k_idx[s,:] * k_scale[s])
  * (the ReLU-weighted head aggregation is this library's reading of "score,
- * then head-weight"; k_scale is 1 unless the keys are FP8).
+ * then head-weight"; k_scale is 1 unless the keys are FP8_E4M3; MXFP8_E4M3
+ * keys scale each group of 32 dims instead, as dsa_index_score states).
  *
  * Sparse MLA attention ("Optimization and Deployment Practices for
  * Next-Generation Sparse Attention LLMs" §1-§2): one latent row of qk_dim
@@ -109,13 +122,15 @@ typedef struct dsa_problem {
   int32_t top_k;        /* K >= 1 */
   float softmax_scale;  /* finite, > 0 (usually 1/sqrt(qk_dim)) */
   int32_t q_idx_dtype;  /* DSA_F32 | DSA_BF16 */
-  int32_t idx_key_dtype;/* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3 (then k_scale required) */
+  int32_t idx_key_dtype;/* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3 | DSA_MXFP8_E4M3 (the last two
+                           with k_scale) */
   int32_t q_dtype;      /* DSA_F32 | DSA_BF16 */
-  int32_t kv_dtype;     /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3 (then kv_scale required) */
+  int32_t kv_dtype;     /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3 | DSA_FP8_E4M3_T128 (the last
+                           two with kv_scale) */
   int32_t out_dtype;    /* DSA_F32 | DSA_BF16 */
 } dsa_problem;
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 #define DSA_FORWARD_STAGES 3 /* indexer scores, Top-K, sparse attention */
 
 int dsa_abi_version(void);
@@ -125,13 +140,23 @@ const char* dsa_last_error(void);
 
 /*
  * Indexer scores (step 1).
- *   q_idx    [B,T,Hi,Di]  q_idx_dtype.  With FP8 keys the index query is
- *                         quantised to E4M3 (nearest, ties to even, saturating
- *                         at +-448) before the products, as the pages quantise
- *                         index Q and K alike ("Inference Acceleration ..." §4.1).
+ *   q_idx    [B,T,Hi,Di]  q_idx_dtype (finite).  With FP8 keys the index query
+ *                         is quantised to E4M3 (nearest, ties to even,
+ *                         saturating at +-448) before the products, as the
+ *                         pages quantise index Q and K alike ("Inference
+ *                         Acceleration ..." §4.1).  With MXFP8 keys it is
+ *                         quantised to MXFP8 on the fly, each head's groups of
+ *                         32 on their own: shared exponent E = floor(log2 of
+ *                         the group's largest magnitude) - 8, kept in
+ *                         [-127, 127] (-127 for an all-zero group), elements
+ *                         the nearest E4M3 values of x / 2^E, saturating (the
+ *                         OCP MX v1.0 conversion); the score then uses the
+ *                         dequantised query and keys.
  *   head_w   [B,T,Hi]     fp32 head weights.
- *   k_idx    [B,Lmax,Di]  idx_key_dtype index keys.
- *   k_scale  [B,Lmax]     fp32 positive per-row scale when keys are FP8, else NULL.
+ *   k_idx    [B,Lmax,Di]  idx_key_dtype index keys (E4M3 codes for both FP8 forms).
+ *   k_scale  FP8_E4M3:    fp32 [B,Lmax], a positive scale per row (4-byte aligned);
+ *            MXFP8_E4M3:  uint8 [B,Lmax,ceil(Di/32)] E8M0 group scales;
+ *            otherwise NULL.
  *   seq_lens [B]          int32 filled rows per sequence.
  *   scores   [B,T,Lmax]   fp32 output; entries s >= vis are left unspecified
  *                         (they may be overwritten).
@@ -139,7 +164,7 @@ const char* dsa_last_error(void);
  * be 16-byte aligned.
  */
 dsa_status dsa_index_score(const dsa_problem* p, const void* q_idx, const float* head_w,
-                           const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                           const void* k_idx, const void* k_scale, const int32_t* seq_lens,
                            float* scores, struct ihipStream_t* stream);
 
 /* Workspace bytes dsa_topk needs for problem p (0 if p is invalid). */
@@ -180,10 +205,13 @@ size_t dsa_sparse_mla_workspace_size(const dsa_problem* p);
  * Sparse MLA attention over selected rows (step 3).
  *   q        [B,T,H,Dqk]  q_dtype queries (already absorbed into the latent space).
  *   kv       [B,Lmax,Dqk] kv_dtype latent cache rows.
- *   kv_scale [B,Lmax]     fp32 positive per-row scale when kv is FP8, else NULL.
- *                         A power of two (the per-token scales of the format)
- *                         expands a row to bf16 exactly; any other value is
- *                         applied in fp32 and the product rounded to bf16.
+ *   kv_scale FP8_E4M3:       fp32 [B,Lmax], a positive scale per row;
+ *            FP8_E4M3_T128:  fp32 [B,Lmax,ceil(Dqk/128)], a positive scale per
+ *                            128-column tile of each row;
+ *            otherwise NULL.
+ *                         A power-of-two scale expands its elements to bf16
+ *                         exactly; any other value is applied in fp32 and the
+ *                         product rounded to bf16.
  *   topk_idx [B,T,K]      int32 rows to attend over; entries outside [0, len_b)
  *                         are ignored, so -1 padding is allowed.
  *   out      [B,T,H,Dv]   out_dtype output.  No valid entry: out = 0.
@@ -219,7 +247,7 @@ size_t dsa_forward_workspace_size(const dsa_problem* p);
  *                so they time the kernel alone.
  */
 dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
-                       const void* k_idx, const float* k_scale, const void* q, const void* kv,
+                       const void* k_idx, const void* k_scale, const void* q, const void* kv,
                        const float* kv_scale, const int32_t* seq_lens, float* scores,
                        int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
                        size_t ws_bytes, struct ihipStream_t* stream,
@@ -246,9 +274,11 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
  *
  * The _paged entry points take, in place of k_idx / k_scale / kv / kv_scale,
  *   k_pages   [num_pages, page_size, idx_dim]     (idx_key_dtype)
- *   k_scales  [num_pages, page_size] fp32 when the keys are FP8, else NULL
+ *   k_scales  [num_pages, page_size] fp32 (FP8_E4M3 keys),
+ *             [num_pages, page_size, idx_dim/32] E8M0 (MXFP8_E4M3), else NULL
  *   kv_pages  [num_pages, page_size, qk_dim]      (kv_dtype)
- *   kv_scales [num_pages, page_size] fp32 when the cache is FP8, else NULL
+ *   kv_scales [num_pages, page_size] fp32 (FP8_E4M3 cache),
+ *             [num_pages, page_size, ceil(qk_dim/128)] fp32 (FP8_E4M3_T128), else NULL
  * and are otherwise the calls above (same workspaces, outputs and timing
  * events; topk_idx stays in logical positions).  They need the matrix-core
  * kernels (64 x 128 indexer, 576/512 MLA, bf16 or FP8 caches): other problems
@@ -262,14 +292,14 @@ typedef struct dsa_paging {
 } dsa_paging;
 
 dsa_status dsa_index_score_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
-                                 const float* head_w, const void* k_pages, const float* k_scales,
+                                 const float* head_w, const void* k_pages, const void* k_scales,
                                  const int32_t* seq_lens, float* scores, struct ihipStream_t* stream);
 dsa_status dsa_sparse_mla_decode_paged(const dsa_problem* p, const dsa_paging* pg, const void* q,
                                        const void* kv_pages, const float* kv_scales,
                                        const int32_t* topk_idx, const int32_t* seq_lens, void* out,
                                        float* lse, void* ws, size_t ws_bytes, struct ihipStream_t* stream);
 dsa_status dsa_forward_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
-                             const float* head_w, const void* k_pages, const float* k_scales,
+                             const float* head_w, const void* k_pages, const void* k_scales,
                              const void* q, const void* kv_pages, const float* kv_scales,
                              const int32_t* seq_lens, float* scores, int32_t* topk_idx,
                              int32_t* topk_count, void* out, float* lse, void* ws, size_t ws_bytes,

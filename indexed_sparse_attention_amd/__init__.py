@@ -26,7 +26,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
-DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_MXFP8_E4M3, DSA_FP8_E4M3_T128 = 0, 1, 2, 3, 4
 FORWARD_STAGES = 3
 _STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
            3: "DSA_ERR_WORKSPACE_TOO_SMALL", 4: "DSA_ERR_HIP"}
@@ -121,6 +121,23 @@ def dtype_code(t: torch.Tensor) -> int:
     raise DsaError(1, f"unsupported tensor dtype {t.dtype}")
 
 
+def key_dtype_code(k: torch.Tensor, k_scale: Optional[torch.Tensor]) -> int:
+    """Index-key format: E4M3 codes with uint8 (E8M0) scales are MXFP8."""
+    c = dtype_code(k)
+    if c == DSA_FP8_E4M3 and k_scale is not None and k_scale.dtype in (torch.uint8, torch.float8_e8m0fnu):
+        return DSA_MXFP8_E4M3
+    return c
+
+
+def kv_dtype_code(kv: torch.Tensor, kv_scale: Optional[torch.Tensor]) -> int:
+    """Latent-cache format: E4M3 codes with one more scale dimension than
+    rows (one scale per 128-column tile) are FP8_E4M3_T128."""
+    c = dtype_code(kv)
+    if c == DSA_FP8_E4M3 and kv_scale is not None and kv_scale.dim() == kv.dim():
+        return DSA_FP8_E4M3_T128
+    return c
+
+
 def _torch_dtype(code: int) -> torch.dtype:
     return {DSA_F32: torch.float32, DSA_BF16: torch.bfloat16}[code]
 
@@ -188,19 +205,19 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Option
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
-def _index_problem(q_idx, k_idx, seq_lens, top_k=1) -> dict:
+def _index_problem(q_idx, k_idx, seq_lens, top_k=1, k_scale=None) -> dict:
     B, T, Hi, Di = q_idx.shape
     assert k_idx.dim() == 3 and k_idx.shape[0] == B and k_idx.shape[2] == Di, "k_idx must be [B,Lmax,Di]"
     assert seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]"
     return dict(batch=B, q_len=T, max_seq_len=k_idx.shape[1], idx_heads=Hi, idx_dim=Di,
-                top_k=top_k, q_idx_dtype=dtype_code(q_idx), idx_key_dtype=dtype_code(k_idx))
+                top_k=top_k, q_idx_dtype=dtype_code(q_idx), idx_key_dtype=key_dtype_code(k_idx, k_scale))
 
 
 def dsa_index_score(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor,
                     seq_lens: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
                     scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     lib = load_library()
-    d = _index_problem(q_idx, k_idx, seq_lens)
+    d = _index_problem(q_idx, k_idx, seq_lens, k_scale=k_scale)
     p = make_problem(**d)
     if scores is None:
         scores = torch.empty((d["batch"], d["q_len"], d["max_seq_len"]), dtype=torch.float32,
@@ -238,7 +255,7 @@ def dsa_sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, topk_idx: torch.Ten
         out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     p = make_problem(batch=B, q_len=T, max_seq_len=kv.shape[1], heads=H, qk_dim=Dqk, v_dim=v_dim,
                      top_k=K, softmax_scale=softmax_scale, q_dtype=dtype_code(q),
-                     kv_dtype=dtype_code(kv), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
+                     kv_dtype=kv_dtype_code(kv, kv_scale), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
     out = torch.empty((B, T, H, v_dim), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if return_lse else None
     nbytes = lib.dsa_sparse_mla_workspace_size(ctypes.byref(p))
@@ -250,14 +267,14 @@ def dsa_sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, topk_idx: torch.Ten
 
 
 def forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale=None,
-                    out_dtype: Optional[torch.dtype] = None) -> Problem:
-    d = _index_problem(q_idx, k_idx, seq_lens, top_k)
+                    out_dtype: Optional[torch.dtype] = None, k_scale=None, kv_scale=None) -> Problem:
+    d = _index_problem(q_idx, k_idx, seq_lens, top_k, k_scale)
     B, T, H, Dqk = q.shape
     assert (B, T) == (d["batch"], d["q_len"]) and kv.shape == (B, d["max_seq_len"], Dqk)
     if out_dtype is None:
         out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     d.update(heads=H, qk_dim=Dqk, v_dim=v_dim, softmax_scale=softmax_scale, q_dtype=dtype_code(q),
-             kv_dtype=dtype_code(kv), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
+             kv_dtype=kv_dtype_code(kv, kv_scale), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
     return make_problem(**d)
 
 
@@ -305,8 +322,9 @@ def dsa_forward_paged(q_idx: torch.Tensor, head_w: torch.Tensor, k_pages: torch.
         out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     p = make_problem(batch=B, q_len=T, max_seq_len=max_seq_len, idx_heads=Hi, idx_dim=Di, heads=H,
                      qk_dim=Dqk, v_dim=v_dim, top_k=top_k, softmax_scale=softmax_scale,
-                     q_idx_dtype=dtype_code(q_idx), idx_key_dtype=dtype_code(k_pages), q_dtype=dtype_code(q),
-                     kv_dtype=dtype_code(kv_pages), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
+                     q_idx_dtype=dtype_code(q_idx), idx_key_dtype=key_dtype_code(k_pages, k_scales),
+                     q_dtype=dtype_code(q), kv_dtype=kv_dtype_code(kv_pages, kv_scales),
+                     out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
     pg = make_paging(block_table, page_size, num_pages)
     o = _forward_outputs(p, q.device, top_k, v_dim, return_scores, return_lse, out)
     ws = _workspace(lib.dsa_forward_workspace_size(ctypes.byref(p)), q.device, workspace)
@@ -328,7 +346,7 @@ def dsa_forward(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor, 
     """Whole path.  ``out`` may hold preallocated 'out', 'lse', 'topk_idx',
     'topk_count', 'scores' tensors (reused as given)."""
     lib = load_library()
-    p = forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale, out_dtype)
+    p = forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale, out_dtype, k_scale, kv_scale)
     dev = q.device
     B, T, H = p.batch, p.q_len, p.heads
     o = dict(out or {})

@@ -10,6 +10,9 @@ constexpr int kWave = 64;
 
 // Number formats (values of dsa_dtype).
 constexpr int kF32 = 0, kBF16 = 1, kE4M3 = 2;
+// E4M3 elements with scales kept beside them: one E8M0 byte per 32 elements
+// of a row (MXFP8, index keys), one fp32 per 128 elements (latent rows)
+constexpr int kMXE4M3 = 3, kE4M3T128 = 4;
 
 // Top-K histogram: the top 12 bits of the order-preserving score key.
 constexpr int kHistBits = 12;

@@ -72,9 +72,10 @@ dsa_status validate_problem(const dsa_problem* p) {
     return fail(DSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   auto in = [](int32_t d, int lo, int hi) { return d >= lo && d <= hi; };
   if (!in(p->q_idx_dtype, DSA_F32, DSA_BF16)) return fail(DSA_ERR_INVALID_ARG, "q_idx_dtype must be F32 or BF16");
-  if (!in(p->idx_key_dtype, DSA_F32, DSA_FP8_E4M3)) return fail(DSA_ERR_INVALID_ARG, "idx_key_dtype invalid");
+  if (!in(p->idx_key_dtype, DSA_F32, DSA_MXFP8_E4M3)) return fail(DSA_ERR_INVALID_ARG, "idx_key_dtype invalid");
   if (!in(p->q_dtype, DSA_F32, DSA_BF16)) return fail(DSA_ERR_INVALID_ARG, "q_dtype must be F32 or BF16");
-  if (!in(p->kv_dtype, DSA_F32, DSA_FP8_E4M3)) return fail(DSA_ERR_INVALID_ARG, "kv_dtype invalid");
+  if (!in(p->kv_dtype, DSA_F32, DSA_FP8_E4M3) && p->kv_dtype != DSA_FP8_E4M3_T128)
+    return fail(DSA_ERR_INVALID_ARG, "kv_dtype invalid");
   if (!in(p->out_dtype, DSA_F32, DSA_BF16)) return fail(DSA_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
   // sizes must fit the int64 offsets the kernels use
   const double bt = (double)p->batch * p->q_len;
@@ -130,7 +131,8 @@ struct MlaLayout {
 bool mla_uses_mfma(const dsa_problem* p) {
   return !force_generic() && p->qk_dim == 576 && p->v_dim == 512 && p->heads % 64 == 0 &&
          (int64_t)p->top_k <= 64 * (int64_t)dsa::mla_max_rows_per_split() &&
-         p->q_dtype == DSA_BF16 && (p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_FP8_E4M3);
+         p->q_dtype == DSA_BF16 &&
+         (p->kv_dtype == DSA_BF16 || p->kv_dtype == DSA_FP8_E4M3 || p->kv_dtype == DSA_FP8_E4M3_T128);
 }
 
 MlaLayout mla_layout(const dsa_problem* p) {
@@ -207,15 +209,17 @@ dsa_status hip_check(hipError_t e, const char* what) {
   } while (0)
 
 dsa_status check_index_inputs(const dsa_problem* p, const void* q_idx, const float* head_w,
-                              const void* k_idx, const float* k_scale, const int32_t* seq_lens) {
+                              const void* k_idx, const void* k_scale, const int32_t* seq_lens) {
   REQUIRE(q_idx && aligned(q_idx, 16), "q_idx must be non-NULL and 16-byte aligned");
   REQUIRE(head_w && aligned(head_w, 4), "head_w must be non-NULL and 4-byte aligned");
   REQUIRE(k_idx && aligned(k_idx, 16), "k_idx must be non-NULL and 16-byte aligned");
   REQUIRE(seq_lens && aligned(seq_lens, 4), "seq_lens must be non-NULL and 4-byte aligned");
   if (p->idx_key_dtype == DSA_FP8_E4M3)
     REQUIRE(k_scale && aligned(k_scale, 4), "k_scale is required (4-byte aligned) for FP8 index keys");
+  else if (p->idx_key_dtype == DSA_MXFP8_E4M3)
+    REQUIRE(k_scale, "k_scale (E8M0 group scales) is required for MXFP8 index keys");
   else
-    REQUIRE(!k_scale, "k_scale must be NULL unless idx_key_dtype is FP8_E4M3");
+    REQUIRE(!k_scale, "k_scale must be NULL unless the index keys are FP8_E4M3 or MXFP8_E4M3");
   return DSA_OK;
 }
 
@@ -226,10 +230,10 @@ dsa_status check_mla_inputs(const dsa_problem* p, const void* q, const void* kv,
   REQUIRE(seq_lens && aligned(seq_lens, 4), "seq_lens must be non-NULL and 4-byte aligned");
   REQUIRE(out && aligned(out, 16), "out must be non-NULL and 16-byte aligned");
   REQUIRE(!lse || aligned(lse, 4), "lse must be 4-byte aligned");
-  if (p->kv_dtype == DSA_FP8_E4M3)
+  if (p->kv_dtype == DSA_FP8_E4M3 || p->kv_dtype == DSA_FP8_E4M3_T128)
     REQUIRE(kv_scale && aligned(kv_scale, 4), "kv_scale is required (4-byte aligned) for an FP8 cache");
   else
-    REQUIRE(!kv_scale, "kv_scale must be NULL unless kv_dtype is FP8_E4M3");
+    REQUIRE(!kv_scale, "kv_scale must be NULL unless kv_dtype is FP8_E4M3 or FP8_E4M3_T128");
   if (!mla_uses_mfma(p)) {
     REQUIRE(p->qk_dim <= 2048, "qk_dim > 2048 is not supported by the portable attention kernel");
     if (p->v_dim > 1024) return fail(DSA_ERR_UNSUPPORTED, "v_dim > 1024 is not supported by the portable attention kernel");
@@ -238,7 +242,7 @@ dsa_status check_mla_inputs(const dsa_problem* p, const void* q, const void* kv,
 }
 
 dsa::ScoreParams score_params(const dsa_problem* p, const void* q_idx, const float* head_w,
-                              const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                              const void* k_idx, const void* k_scale, const int32_t* seq_lens,
                               float* scores, uint32_t* hist) {
   dsa::ScoreParams s;
   s.q_idx = q_idx;
@@ -396,7 +400,7 @@ const char* dsa_status_string(dsa_status s) {
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
 static dsa_status index_score_impl(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
-                                   const float* head_w, const void* k_idx, const float* k_scale,
+                                   const float* head_w, const void* k_idx, const void* k_scale,
                                    const int32_t* seq_lens, float* scores, hipStream_t stream) {
   dsa_status st = validate_problem(p);
   if (st != DSA_OK) return st;
@@ -411,13 +415,13 @@ static dsa_status index_score_impl(const dsa_problem* p, const dsa_paging* pg, c
 }
 
 dsa_status dsa_index_score(const dsa_problem* p, const void* q_idx, const float* head_w,
-                           const void* k_idx, const float* k_scale, const int32_t* seq_lens,
+                           const void* k_idx, const void* k_scale, const int32_t* seq_lens,
                            float* scores, struct ihipStream_t* stream) {
   return index_score_impl(p, nullptr, q_idx, head_w, k_idx, k_scale, seq_lens, scores, stream);
 }
 
 dsa_status dsa_index_score_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
-                                 const float* head_w, const void* k_pages, const float* k_scales,
+                                 const float* head_w, const void* k_pages, const void* k_scales,
                                  const int32_t* seq_lens, float* scores, struct ihipStream_t* stream) {
   if (!pg) return fail(DSA_ERR_INVALID_ARG, "pg must be non-NULL");
   return index_score_impl(p, pg, q_idx, head_w, k_pages, k_scales, seq_lens, scores, stream);
@@ -511,7 +515,7 @@ size_t dsa_forward_workspace_size(const dsa_problem* p) {
 }
 
 static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
-                               const float* head_w, const void* k_idx, const float* k_scale, const void* q,
+                               const float* head_w, const void* k_idx, const void* k_scale, const void* q,
                                const void* kv, const float* kv_scale, const int32_t* seq_lens, float* scores,
                                int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
                                size_t ws_bytes, hipStream_t stream, struct ihipEvent_t* const* stage_events) {
@@ -575,7 +579,7 @@ static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const
 }
 
 dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
-                       const void* k_idx, const float* k_scale, const void* q, const void* kv,
+                       const void* k_idx, const void* k_scale, const void* q, const void* kv,
                        const float* kv_scale, const int32_t* seq_lens, float* scores,
                        int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
                        size_t ws_bytes, struct ihipStream_t* stream,
@@ -585,7 +589,7 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
 }
 
 dsa_status dsa_forward_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
-                             const float* head_w, const void* k_pages, const float* k_scales,
+                             const float* head_w, const void* k_pages, const void* k_scales,
                              const void* q, const void* kv_pages, const float* kv_scales,
                              const int32_t* seq_lens, float* scores, int32_t* topk_idx,
                              int32_t* topk_count, void* out, float* lse, void* ws, size_t ws_bytes,

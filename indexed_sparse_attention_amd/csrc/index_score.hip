@@ -34,8 +34,37 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
   if (s >= vis) return;
   const bool fp8 = (p.k_dtype == kE4M3);
   const int64_t krow = ((int64_t)b * p.Lmax + s) * p.Di;
-  const float scale = p.k_scale ? p.k_scale[(int64_t)b * p.Lmax + s] : 1.0f;
   float S = 0.0f;
+  if (p.k_dtype == kMXE4M3) {
+    // MXFP8: the query is quantised group by group (32 dims, the last group
+    // may be shorter) with a shared power-of-two scale 2^E, E = floor(log2
+    // amax) - 8 (the largest magnitude lands in E4M3's top binade; OCP MX
+    // v1.0 conversion), and each group's products carry both groups' scales.
+    const int G = (p.Di + 31) / 32;
+    const uint8_t* ks = (const uint8_t*)p.k_scale + ((int64_t)b * p.Lmax + s) * G;
+    for (int h = 0; h < p.Hi; ++h) {
+      const int64_t qrow = ((int64_t)bt * p.Hi + h) * p.Di;
+      float d = 0.0f;
+      for (int g = 0; g < G; ++g) {
+        const int i0 = 32 * g, n = min(32, p.Di - i0);
+        float amax = 0.0f;
+        for (int i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(load_elem(p.q_idx, p.q_dtype, qrow + i0 + i)));
+        const int ef = (int)(__float_as_uint(amax) >> 23);  // biased exponent (amax >= 0)
+        const int E = ef == 0 ? -127 : max(ef - 127 - 8, -127);
+        const float inv = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E
+        float gd = 0.0f;
+        for (int i = 0; i < n; ++i)
+          gd = fmaf(e4m3_quantize(load_elem(p.q_idx, p.q_dtype, qrow + i0 + i) * inv),
+                    load_elem(p.k_idx, kE4M3, krow + i0 + i), gd);
+        d += ldexpf(gd, E + (int)ks[g] - 127);
+      }
+      S = fmaf(p.head_w[(int64_t)bt * p.Hi + h], fmaxf(d, 0.0f), S);
+    }
+    p.scores[(int64_t)bt * p.Lmax + s] = S;
+    if (p.hist) atomicAdd(&p.hist[(int64_t)bt * kHistBins + (score_key(S) >> kHistShift)], 1u);
+    return;
+  }
+  const float scale = p.k_scale ? ((const float*)p.k_scale)[(int64_t)b * p.Lmax + s] : 1.0f;
   for (int h = 0; h < p.Hi; ++h) {
     const int64_t qrow = ((int64_t)bt * p.Hi + h) * p.Di;
     float d = 0.0f;
@@ -72,22 +101,36 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
 // the 4 lane groups leaves lane l with the full score of column l%16 of the
 // unit's sub-tile l/16.
 //
-// Operand k-ordering: MFMA A and B share one (lane group, element) -> k
-// assignment, so any fixed permutation of the 128 dims gives the same dot
-// product; lane group j of k-step ks carries dims 32 ks + 8 j .. +8 (bf16) or
-// dims 32 j .. +32 (e4m3, single k-step of 128).
+// Operand k-ordering: bf16 operands A and B share one (lane group, element)
+// -> k assignment, so any fixed permutation of the 128 dims gives the same
+// dot product; lane group j of k-step ks carries dims 32 ks + 8 j .. +8.  The
+// e4m3 product (one k-step of 128) applies its scales per 32 consecutive k,
+// so there the operands follow the hardware's own order: lane group j holds k
+// 16 j .. +16 in its first 16 bytes and 64 + 16 j .. +16 in the next 16, and
+// lane l's scale operand applies to row (A) / column (B) l%16 of the group of
+// k = 32 (l/16) .. +32 (both checked on the device against an exact sum).
+//
+// Key formats: bf16; e4m3 with one scale per row (applied to the score,
+// the operands' scales are 1); MXFP8, e4m3 with an E8M0 scale per 32 dims,
+// whose index query is quantised the same way while it is staged, both
+// scales going into the scaled e4m3 MFMA.
 // ---------------------------------------------------------------------------
 constexpr int kHi = 64, kDi = 128;
+constexpr int kKeyBF16 = 0, kKeyE4M3 = 1, kKeyMX = 2;
+constexpr int kGroups = kDi / 32;  // MX groups per row
 
-template <bool FP8>
-struct KeyTile;
+template <int KF>
+struct KeyTile {  // e4m3: one k-step of 128 dims, 32 bytes
+  i32x8 v;
+};
 template <>
-struct KeyTile<false> {  // bf16: 4 k-steps of 32 dims, 16 bytes each
+struct KeyTile<kKeyBF16> {  // bf16: 4 k-steps of 32 dims, 16 bytes each
   bf16x8 v[4];
 };
 template <>
-struct KeyTile<true> {  // e4m3: one k-step of 128 dims, 32 bytes
+struct KeyTile<kKeyMX> {  // MXFP8: the codes and this lane's group scale (E8M0)
   i32x8 v;
+  int sc;
 };
 
 // Key rows are read through a buffer resource over the sequence's filled rows
@@ -99,37 +142,46 @@ struct KeyTile<true> {  // e4m3: one k-step of 128 dims, 32 bytes
 constexpr uint32_t kNoRow = 0x80000000u;  // offset of a read that must not happen
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
-template <bool FP8>
-__device__ __forceinline__ void load_key_tile(KeyTile<FP8>& kt, __amdgpu_buffer_rsrc_t rows, uint32_t row_off,
-                                              int lg) {
-  if constexpr (!FP8) {  // 128 bf16 = 16 x 16 B
+// scales: (MXFP8) a buffer resource over the rows' E8M0 bytes, kGroups per
+// row, in the same row order as `rows` (a row past the bound reads scale 0).
+template <int KF>
+__device__ __forceinline__ void load_key_tile(KeyTile<KF>& kt, __amdgpu_buffer_rsrc_t rows,
+                                              __amdgpu_buffer_rsrc_t scales, uint32_t row_off, int lg) {
+  if constexpr (KF == kKeyBF16) {  // 128 bf16 = 16 x 16 B
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       kt.v[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 16 * (ks * 4 + lg), 0, 0));
-  } else {  // 128 bytes = 8 x 16 B
-    const i32x4 a = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 32 * lg, 0, 0));
-    const i32x4 c = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 32 * lg + 16, 0, 0));
+  } else {  // 128 bytes = 8 x 16 B: dims 16 lg .. +16 and 64 + 16 lg .. +16
+    const i32x4 a = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 16 * lg, 0, 0));
+    const i32x4 c = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, row_off + 64 + 16 * lg, 0, 0));
     kt.v = i32x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+    if constexpr (KF == kKeyMX)  // scale of group lg of this row
+      kt.sc = __builtin_amdgcn_raw_buffer_load_b8(scales, row_off / kDi * kGroups + lg, 0, 0);
   }
 }
 
-template <int TQ, bool FP8>
-struct QRegs;
+template <int TQ, int KF>
+struct QRegs {
+  i32x8 a[TQ][4];  // [token][head tile], 32 e4m3 codes
+};
 template <int TQ>
-struct QRegs<TQ, false> {
+struct QRegs<TQ, kKeyBF16> {
   bf16x8 a[TQ][4][4];  // [token][head tile][k-step]
 };
 template <int TQ>
-struct QRegs<TQ, true> {
+struct QRegs<TQ, kKeyMX> {
   i32x8 a[TQ][4];  // [token][head tile], 32 e4m3 codes
+  int sc[TQ][4];   // [token][head tile]: E8M0 scale of this lane's head row and group
 };
 
-template <int TQ, int NSLOT, bool FP8, int MINB, int NT, bool PAGED>
+template <int TQ, int NSLOT, int KF, int MINB, int NT, bool PAGED>
 __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
+  constexpr bool FP8 = KF != kKeyBF16, MX = KF == kKeyMX;
   constexpr int kScoreThreads = NT, kScoreWaves = NT / kWave;
   // LDS: [TQ] index queries in operand order (bf16: 64 x 128 x 2 B; e4m3: 64 x 128 B),
   // then [TQ][kHistBins] histogram counters when p.hist.
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ uint8_t s_qsc[MX ? TQ * kHi * kGroups : 4];  // (MXFP8) query group scales [TQ][head][group]
   constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
   uint8_t* lds_q = (uint8_t*)lds;
   uint32_t* lds_hist = lds + TQ * kQBytes / 4;
@@ -261,6 +313,10 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
       const __amdgpu_buffer_rsrc_t krows = __builtin_amdgcn_make_buffer_rsrc(
           (void*)((const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes), (short)0, len * kRowBytes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t kscales =
+          MX ? __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.k_scale + (int64_t)b * p.Lmax * kGroups),
+                                                 (short)0, len * kGroups, kBufferFlags)
+             : krows;
       const int last_row = len - 1;
       auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
 
@@ -289,6 +345,15 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                                                    (short)0, (int)(page_rows * kRowBytes), kBufferFlags);
         }
       };
+      auto scale_rsrc = [&](int32_t entry) -> __amdgpu_buffer_rsrc_t {  // (MXFP8) the scales of key_rsrc's rows
+        if constexpr (!PAGED || !MX) {
+          return kscales;
+        } else {
+          const int64_t pp = phys_page(__builtin_amdgcn_readfirstlane(entry));
+          return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.k_scale + pp * page_rows * kGroups),
+                                                   (short)0, (int)(page_rows * kGroups), kBufferFlags);
+        }
+      };
       auto st_off = [&](int x) -> uint32_t {  // offset of the key row this lane loads for sub-tile x
         const int64_t pos = sub_pos(x) + lc;
         const int64_t r = PAGED ? (pos & (page_rows - 1)) : pos;
@@ -305,7 +370,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       // iteration wait for all loads in flight.
       constexpr int RB = 8;
       static_assert((4 * RB) % NSLOT == 0 && NSLOT % 4 == 0, "ring must tile the batch");
-      KeyTile<FP8> slot[NSLOT];
+      KeyTile<KF> slot[NSLOT];
       auto fill_ring = [&]() {
         if constexpr (PAGED) {
 #pragma unroll
@@ -314,7 +379,8 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           for (int j = 0; j < NSLOT; ++j) pg_next[j] = page_entry(j + NSLOT);
         }
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j) load_key_tile<FP8>(slot[j], key_rsrc(pg_cur[j]), st_off(j), lg);
+        for (int j = 0; j < NSLOT; ++j)
+          load_key_tile<KF>(slot[j], key_rsrc(pg_cur[j]), scale_rsrc(pg_cur[j]), st_off(j), lg);
       };
 
       // head weights (used from the first unit on), then the index queries
@@ -367,11 +433,30 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                            bf16_bits_to_f32((uint32_t)v[1] & 0xFFFFu), bf16_bits_to_f32((uint32_t)v[1] >> 16)};
             }
           }
+          // MXFP8: word tid + 256 k is word tid%8 of group (tid + 256 k)/8, so the
+          // 8 words of a group sit in 8 neighbouring lanes: their largest
+          // magnitude sets the group's shared exponent E = floor(log2 amax) - 8
+          // (within E8M0's range) and the codes are of x / 2^E (OCP MX v1.0)
+          float inv[kWords];
+#pragma unroll
+          for (int k = 0; k < kWords; ++k) {
+            inv[k] = 1.0f;
+            if constexpr (MX) {
+              float m = fmaxf(fmaxf(fabsf(x[k][0]), fabsf(x[k][1])), fmaxf(fabsf(x[k][2]), fabsf(x[k][3])));
+              m = fmaxf(m, __shfl_xor(m, 1, kWave));
+              m = fmaxf(m, __shfl_xor(m, 2, kWave));
+              m = fmaxf(m, __shfl_xor(m, 4, kWave));
+              const int ef = (int)(__float_as_uint(m) >> 23);  // biased exponent (m >= 0)
+              const int E = ef == 0 ? -127 : max(ef - 127 - 8, -127);
+              inv[k] = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E
+              if ((tid & 7) == 0) s_qsc[tq * kHi * kGroups + (tid + k * kScoreThreads) / 8] = (uint8_t)(E + 127);
+            }
+          }
 #pragma unroll
           for (int k = 0; k < kWords; ++k) {
             uint32_t word = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) word |= e4m3_code_exact(e4m3_quantize(x[k][e])) << (8 * e);
+            for (int e = 0; e < 4; ++e) word |= e4m3_code_exact(e4m3_quantize(x[k][e] * inv[k])) << (8 * e);
             ((uint32_t*)(lds_q + tq * kQBytes))[tid + k * kScoreThreads] = word;
           }
         }
@@ -380,7 +465,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         __syncthreads();
       else
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      QRegs<TQ, FP8> q;
+      QRegs<TQ, KF> q;
 #pragma unroll
       for (int tq = 0; tq < TQ; ++tq) {
 #pragma unroll
@@ -389,10 +474,11 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           if constexpr (!FP8) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) q.a[tq][ht][ks] = ((const bf16x8*)qrow)[ks * 4 + lg];
-          } else {
+          } else {  // dims 16 lg .. +16 and 64 + 16 lg .. +16
             const i32x4* r = (const i32x4*)qrow;
-            const i32x4 x0 = r[2 * lg], x1 = r[2 * lg + 1];
+            const i32x4 x0 = r[lg], x1 = r[4 + lg];
             q.a[tq][ht] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            if constexpr (MX) q.sc[tq][ht] = s_qsc[(tq * kHi + ht * 16 + lc) * kGroups + lg];
           }
         }
       }
@@ -408,13 +494,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           // after the reduce-scatter lane l holds position lc of its sub-tile 4u + lg
           const int64_t pos = sub_pos(4 * (u0 + ub) + lg) + lc;
           float kscale = 1.0f;
-          if constexpr (FP8 && !PAGED) {
-            kscale = p.k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
-          } else if constexpr (FP8) {
+          const float* k_scale = (const float*)p.k_scale;
+          if constexpr (KF == kKeyE4M3 && !PAGED) {
+            kscale = k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
+          } else if constexpr (KF == kKeyE4M3) {
             // this lane's sub-tile 4u + lg sits in slot (4 ub + lg) % NSLOT (u0 is a multiple of NSLOT)
             const int s0 = (4 * ub) % NSLOT;
             const int32_t e = lg == 0 ? pg_cur[s0] : lg == 1 ? pg_cur[s0 + 1] : lg == 2 ? pg_cur[s0 + 2] : pg_cur[s0 + 3];
-            kscale = p.k_scale[phys_page(e) * page_rows + (pos < len ? (pos & (page_rows - 1)) : 0)];
+            kscale = k_scale[phys_page(e) * page_rows + (pos < len ? (pos & (page_rows - 1)) : 0)];
           }
           float part[TQ][4];
 #pragma unroll
@@ -432,9 +519,12 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
                       a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[tq][ht][ks], slot[j].v[ks], a, 0, 0, 0);
-                  } else {
+                  } else if constexpr (!MX) {  // unit operand scales (E8M0 127 = 1)
                     a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[tq][ht], slot[j].v, a, 0, 0, 0,
                                                                          127, 0, 127);
+                  } else {
+                    a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[tq][ht], slot[j].v, a, 0, 0, 0,
+                                                                         q.sc[tq][ht], 0, slot[j].sc);
                   }
 #pragma unroll
                   for (int e = 0; e < 4; ++e) sacc = fmaf(w[tq][ht][e], fmaxf(a[e], 0.0f), sacc);
@@ -445,7 +535,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
             // refill this slot with the sub-tile NSLOT ahead (nothing is read
             // past the wave's sub-tiles or the sequence's end)
             if constexpr (PAGED) pg_cur[j] = pg_next[j];
-            load_key_tile<FP8>(slot[j], key_rsrc(pg_cur[j]), st_off(x + NSLOT), lg);
+            load_key_tile<KF>(slot[j], key_rsrc(pg_cur[j]), scale_rsrc(pg_cur[j]), st_off(x + NSLOT), lg);
             if constexpr (PAGED) pg_next[j] = page_entry(x + 2 * NSLOT);
           }
           if (live) {
@@ -457,7 +547,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
               const float r1 = (upper ? part[tq][3] : part[tq][1]) +
                                __shfl_xor(upper ? part[tq][1] : part[tq][3], 32, kWave);
               float sc = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16, kWave);
-              if constexpr (FP8) sc *= kscale;
+              if constexpr (KF == kKeyE4M3) sc *= kscale;
               sbuf[tq][ub] = sc;
               if (p.hist && t0 + tq < p.T && pos < (int64_t)len - p.T + 1 + t0 + tq)
                 atomicAdd(&lds_hist[tq * kHistBins + (score_key(sc) >> kHistShift)], 1u);
@@ -506,27 +596,27 @@ bool score_mfma_supported(const ScoreParams& p) {
   const int64_t row_bytes = p.k_dtype == kBF16 ? 2 * kDi : kDi;
   if (!p.block_table && (int64_t)p.Lmax * row_bytes >= (int64_t)kNoRow) return false;  // (paged: one page at a time)
   if (p.k_dtype == kBF16) return p.q_dtype == kBF16;
-  return p.k_dtype == kE4M3;
+  return p.k_dtype == kE4M3 || p.k_dtype == kMXE4M3;
 }
 
-template <int TQ, int NSLOT, bool FP8, int MINB, int NT, bool PAGED>
+template <int TQ, int NSLOT, int KF, int MINB, int NT, bool PAGED>
 static void launch_mfma_k(const ScoreParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop) {
-  constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
+  constexpr int kQBytes = KF != kKeyBF16 ? kHi * kDi : kHi * kDi * 2;
   const size_t lds = TQ * kQBytes + (p.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
   if (ev_start || ev_stop)  // events taken by the dispatch itself at the kernel's start and end
-    hipExtLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT, PAGED>), dim3(grid), dim3(NT), lds, stream,
+    hipExtLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, KF, MINB, NT, PAGED>), dim3(grid), dim3(NT), lds, stream,
                           ev_start, ev_stop, 0, p);
   else
-    hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, FP8, MINB, NT, PAGED>), dim3(grid), dim3(NT), lds, stream, p);
+    hipLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, KF, MINB, NT, PAGED>), dim3(grid), dim3(NT), lds, stream, p);
 }
 
-template <int TQ, int NSLOT, bool FP8, int MINB = 2, int NT = 256>
+template <int TQ, int NSLOT, int KF, int MINB = 2, int NT = 256>
 static void launch_mfma(const ScoreParams& p, int grid, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (p.block_table)
-    launch_mfma_k<TQ, NSLOT, FP8, MINB, NT, true>(p, grid, stream, ev_start, ev_stop);
+    launch_mfma_k<TQ, NSLOT, KF, MINB, NT, true>(p, grid, stream, ev_start, ev_stop);
   else
-    launch_mfma_k<TQ, NSLOT, FP8, MINB, NT, false>(p, grid, stream, ev_start, ev_stop);
+    launch_mfma_k<TQ, NSLOT, KF, MINB, NT, false>(p, grid, stream, ev_start, ev_stop);
 }
 
 static int env_int(const char* name, int dflt) {
@@ -553,24 +643,32 @@ hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipS
     if (env_int("DSA_SCORE_WGS", 0) > 0) grid = env_int("DSA_SCORE_WGS", 0);
     if (p.k_dtype == kBF16) {
       switch (variant) {
-        case 1: launch_mfma<1, 8, false, 1>(p, grid, stream, ev_start, ev_stop); break;
-        case 2: launch_mfma<1, 4, false, 1, 512>(p, grid, stream, ev_start, ev_stop); break;
-        case 3: launch_mfma<2, 4, false, 1>(p, grid, stream, ev_start, ev_stop); break;
-        case 4: launch_mfma<4, 4, false, 1>(p, grid, stream, ev_start, ev_stop); break;
+        case 1: launch_mfma<1, 8, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
+        case 2: launch_mfma<1, 4, kKeyBF16, 1, 512>(p, grid, stream, ev_start, ev_stop); break;
+        case 3: launch_mfma<2, 4, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
+        case 4: launch_mfma<4, 4, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
         default:
           // several query tokens: two per segment, so each key tile feeds twice
           // the MFMAs (12 % faster at 4096 tokens over 64K keys; four tokens
           // need one workgroup per CU and were slower)
           if (p.T >= 2)
-            launch_mfma<2, 4, false, 1>(p, num_cus, stream, ev_start, ev_stop);
+            launch_mfma<2, 4, kKeyBF16, 1>(p, num_cus, stream, ev_start, ev_stop);
           else
-            launch_mfma<1, 4, false, 2>(p, grid, stream, ev_start, ev_stop);
+            launch_mfma<1, 4, kKeyBF16, 2>(p, grid, stream, ev_start, ev_stop);
           break;
       }
-    } else if (p.T == 1) {
-      launch_mfma<1, 8, true>(p, grid, stream, ev_start, ev_stop);
+    } else if (p.k_dtype == kE4M3) {
+      if (p.T == 1)
+        launch_mfma<1, 8, kKeyE4M3>(p, grid, stream, ev_start, ev_stop);
+      else
+        launch_mfma<2, 4, kKeyE4M3>(p, grid, stream, ev_start, ev_stop);
     } else {
-      launch_mfma<2, 4, true>(p, grid, stream, ev_start, ev_stop);
+      // (two tokens with their group scales need more than half the
+      // registers: one workgroup per CU)
+      if (p.T == 1)
+        launch_mfma<1, 8, kKeyMX>(p, grid, stream, ev_start, ev_stop);
+      else
+        launch_mfma<2, 4, kKeyMX, 1>(p, num_cus, stream, ev_start, ev_stop);
     }
   } else {
     dim3 grid((unsigned)((p.Lmax + 255) / 256), (unsigned)(p.B * p.T));

@@ -10,7 +10,7 @@ struct ScoreParams {
   const void* q_idx;        // [B,T,Hi,Di] q_dtype
   const float* head_w;      // [B,T,Hi]
   const void* k_idx;        // [B,Lmax,Di] k_dtype
-  const float* k_scale;     // [B,Lmax] or null
+  const void* k_scale;      // fp32 [B,Lmax] (e4m3), E8M0 bytes [B,Lmax,Di/32] (mxfp8) or null
   const int32_t* seq_lens;  // [B]
   float* scores;            // [B,T,Lmax]
   uint32_t* hist;           // [B*T, 4096] (zeroed) or null
@@ -45,7 +45,7 @@ struct TopkParams {
 struct MlaParams {
   const void* q;            // [B,T,H,Dqk]
   const void* kv;           // [B,Lmax,Dqk]
-  const float* kv_scale;    // [B,Lmax] or null
+  const float* kv_scale;    // [B,Lmax] (e4m3), [B,Lmax,ceil(Dqk/128)] (e4m3, 128-column tiles) or null
   const int32_t* topk_idx;  // [B,T,K]
   const int32_t* seq_lens;  // [B]
   void* out;                // [B,T,H,Dv]

@@ -33,6 +33,13 @@ __device__ __forceinline__ float mla_load(const void* p, int dtype, int64_t i) {
   return e4m3_to_f32(((const uint8_t*)p)[i]);
 }
 
+// Scale of column i of cache row `row` (1 for f32/bf16 caches).
+__device__ __forceinline__ float kv_col_scale(const MlaParams& p, int64_t row, int i) {
+  if (p.kv_dtype == kE4M3) return p.kv_scale[row];
+  if (p.kv_dtype == kE4M3T128) return p.kv_scale[row * ((p.Dqk + 127) / 128) + i / 128];
+  return 1.0f;
+}
+
 __device__ __forceinline__ void store_out(void* out, int dtype, int64_t i, float v) {
   if (dtype == kF32) ((float*)out)[i] = v;
   else ((uint16_t*)out)[i] = (uint16_t)f32_to_bf16_bits(v);
@@ -66,9 +73,9 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
       int64_t row = -1;
       if (r >= 0 && r < len) {
         row = (int64_t)b * p.Lmax + r;
-        const float sc = p.kv_scale ? p.kv_scale[row] : 1.0f;
         float d = 0.0f;
-        for (int i = 0; i < p.Dqk; ++i) d = fmaf(s_q[i], mla_load(p.kv, p.kv_dtype, row * p.Dqk + i) * sc, d);
+        for (int i = 0; i < p.Dqk; ++i)
+          d = fmaf(s_q[i], mla_load(p.kv, p.kv_dtype, row * p.Dqk + i) * kv_col_scale(p, row, i), d);
         z = d * p.scale;
       }
       s_z[j] = z;
@@ -93,11 +100,11 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
       if (s_row[j] < 0) continue;
       const float pj = expf(s_z[j] - m_new);
       lsum += pj;
-      const float sc = p.kv_scale ? p.kv_scale[s_row[j]] : 1.0f;
 #pragma unroll
       for (int k = 0; k < kGenMaxDvPerThread; ++k) {
         const int d = tid + k * kGenThreads;
-        if (d < p.Dv) o[k] = fmaf(pj, mla_load(p.kv, p.kv_dtype, s_row[j] * p.Dqk + d) * sc, o[k]);
+        if (d < p.Dv)
+          o[k] = fmaf(pj, mla_load(p.kv, p.kv_dtype, s_row[j] * p.Dqk + d) * kv_col_scale(p, s_row[j], d), o[k]);
       }
     }
     m = m_new;
@@ -379,42 +386,54 @@ struct TileCopy {
 };
 
 // e4m3 cache: expands, in place, the rows this wave copied: lane l takes row
-// 16w + l/4 (whose scale it holds) and raw chunks m = l%4 + 4k, k < 9.  The
-// wave's copies must have landed (vmcnt(0)).  Code x power-of-two scale is
-// exact in bf16.
-__device__ __forceinline__ void fp8_decode(uint8_t* buf, float scale, int wave, int l) {
+// 16w + l/4 (whose scales it holds: one per row, or one per 128-column tile)
+// and raw chunks m = l%4 + 4k, k < 9, i.e. columns 16 m .. +16, which lie in
+// tile m / 8 = k / 2 for every lane.  The wave's copies must have landed
+// (vmcnt(0)).  Code x power-of-two scale is exact in bf16.
+template <int NSC>
+__device__ __forceinline__ void fp8_decode(uint8_t* buf, const float (&sc)[NSC], int wave, int l) {
+  constexpr int kSteps = kDqk / 64;                    // k = 0 .. 8
+  constexpr int kPerScale = NSC == 1 ? kSteps : 2;     // k-steps under one scale (a tile: 2)
   const int r = 16 * wave + (l >> 2);
-  const uint32_t sb = __float_as_uint(scale);
-  const bool pow2 = (sb & 0x807FFFFFu) == 0 && (sb >> 23) != 0;  // a positive normal power of two
-  const float hw_scale = pow2 ? scale : 1.0f;
+  // one pass per scale, so each scale is a fixed register (selecting it by k
+  // would become an indexed scratch load)
+#pragma unroll
+  for (int i = 0; i < NSC; ++i) {
+    const float scale = sc[i];
+    const uint32_t sb = __float_as_uint(scale);
+    const bool pow2 = (sb & 0x807FFFFFu) == 0 && (sb >> 23) != 0;  // a positive normal power of two
+    const float hw_scale = pow2 ? scale : 1.0f;
 #pragma unroll 1
-  for (int k = 0; k < kDqk / 64; ++k) {
-    const int m = (l & 3) + 4 * k;
-    uint8_t* d0 = buf + chunk_off(r, 2 * m);
-    const i32x4 v = *(const i32x4*)d0;
-    // codes 4q .. 4q+3 -> bf16 pairs with the hardware's scaled OCP e4m3
-    // conversion, exact for a power-of-two scale (checked against the
-    // format's definition for all 256 codes and the scales 2^-2 .. 2^2).  The
-    // instruction takes only the scale's exponent, so a row whose scale is
-    // not a power of two is converted unscaled and multiplied in fp32.
-    uint32_t w[8];
+    for (int k = i * kPerScale; k < min((i + 1) * kPerScale, kSteps); ++k) {
+      const int m = (l & 3) + 4 * k;
+      uint8_t* d0 = buf + chunk_off(r, 2 * m);
+      const i32x4 v = *(const i32x4*)d0;
+      // codes 4q .. 4q+3 -> bf16 pairs with the hardware's scaled OCP e4m3
+      // conversion, exact for a power-of-two scale (checked against the
+      // format's definition for all 256 codes and the scales 2^-2 .. 2^2).
+      // The instruction takes only the scale's exponent, so a scale that is
+      // not a power of two is converted unscaled and multiplied in fp32.
+      uint32_t w[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[q], hw_scale, false));
-      w[2 * q + 1] =
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[q], hw_scale, true));
-    }
-    if (!pow2) {
+      for (int q = 0; q < 4; ++q) {
+        w[2 * q] =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[q], hw_scale, false));
+        w[2 * q + 1] =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[q], hw_scale, true));
+      }
+      if (!pow2) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        w[j] = pack_bf16x2(__uint_as_float(w[j] << 16) * scale, __uint_as_float(w[j] & 0xFFFF0000u) * scale);
+        for (int j = 0; j < 8; ++j)
+          w[j] = pack_bf16x2(__uint_as_float(w[j] << 16) * scale, __uint_as_float(w[j] & 0xFFFF0000u) * scale);
+      }
+      *(i32x4*)d0 = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *(i32x4*)(buf + chunk_off(r, 2 * m + 1)) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
     }
-    *(i32x4*)d0 = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    *(i32x4*)(buf + chunk_off(r, 2 * m + 1)) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
   }
 }
 
-template <bool FP8>
+// NSC: scales per cache row (e4m3: 1 per row, or one per 128-column tile)
+template <bool FP8, int NSC = 1>
 __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_mfma_kernel(MlaParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
@@ -477,16 +496,20 @@ void mla_mfma_kernel(MlaParams p) {
 #pragma unroll
   for (int k = 0; k < kPer; ++k) s_idx[tid + k * kMlaThreads] = iv[k];  // -1 past the list
   for (int i = kIdxCap + tid; i < n_pad; i += kMlaThreads) s_idx[i] = -1;
-  float kscale = 0.0f;  // e4m3: scale of row 16 wave + l/4 of the tile being copied
+  float kscale[NSC] = {};  // e4m3: scales of row 16 wave + l/4 of the tile being copied
+  auto load_kscale = [&](int64_t row) {
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) kscale[i] = p.kv_scale[row * NSC + i];
+  };
   if (paged) {  // the first tile's rows come back from LDS
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int32_t pos0[2] = {s_idx[my_row], s_idx[my_row + 8]};
     tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
-    if constexpr (FP8) kscale = p.kv_scale[max(s_idx[16 * wave + (l >> 2)], 0)];
+    if constexpr (FP8) load_kscale(max(s_idx[16 * wave + (l >> 2)], 0));
   } else {
     const int32_t pos0[2] = {resolve(my_row), resolve(my_row + 8)};
     tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
-    if constexpr (FP8) kscale = p.kv_scale[seq_row0 + max(resolve(16 * wave + (l >> 2)), 0)];
+    if constexpr (FP8) load_kscale(seq_row0 + max(resolve(16 * wave + (l >> 2)), 0));
   }
 
   // query heads h0 + lc, dims 32 ks + 8 lg .. +8  (operand B of QK^T)
@@ -777,7 +800,7 @@ void mla_mfma_kernel(MlaParams p) {
     for (int t = 0; t < n_tiles; ++t) {
       __syncthreads();
       tile_dma<true>(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l);
-      kscale = p.kv_scale[seq_row0 + max(s_idx[(t + 1) * kTile + srow], 0)];
+      load_kscale(seq_row0 + max(s_idx[(t + 1) * kTile + srow], 0));
       pos[0] = s_idx[(t + 2) * kTile + my_row];
       pos[1] = s_idx[(t + 2) * kTile + my_row + 8];
       compute(sh.rows[cur], t * kTile, [](int) {});
@@ -916,7 +939,7 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(MlaParams p) {
 
 bool mla_mfma_supported(const MlaParams& p) {
   return p.Dqk == kDqk && p.Dv == kDv && p.H % kHeadsPerWG == 0 && p.q_dtype == kBF16 &&
-         (p.kv_dtype == kBF16 || p.kv_dtype == kE4M3);
+         (p.kv_dtype == kBF16 || p.kv_dtype == kE4M3 || p.kv_dtype == kE4M3T128);
 }
 
 hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream) {
@@ -929,11 +952,17 @@ hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream) {
                               (int)lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kMlaThreads), lds, stream, p);
-    } else {
+    } else if (p.kv_dtype == kE4M3) {
       e = hipFuncSetAttribute((const void*)mla_mfma_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(mla_mfma_kernel<true>, grid, dim3(kMlaThreads), lds, stream, p);
+    } else {  // one scale per 128-column tile: ceil(576 / 128) per row
+      constexpr int kTiles = (kDqk + 127) / 128;
+      e = hipFuncSetAttribute((const void*)mla_mfma_kernel<true, kTiles>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((mla_mfma_kernel<true, kTiles>), grid, dim3(kMlaThreads), lds, stream, p);
     }
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;

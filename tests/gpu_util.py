@@ -71,7 +71,7 @@ def check_attention(w, out, lse, ref_out, ref_lse, want=None):
     g = out[sel].astype(np.float64)
     r = ref_out[sel]
     err = np.abs(g - r)
-    if w.kv_dtype == synth.E4M3:
+    if w.kv_dtype in (synth.E4M3, synth.E4M3T128):
         ok = err <= FP8_ABS
         bar = f"abs {FP8_ABS}"
     else:

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = dsa.load_library()
-    assert lib.dsa_abi_version() == 3
+    assert lib.dsa_abi_version() == 4
     assert lib.dsa_status_string(0) == b"DSA_OK"
     assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
 
@@ -57,7 +57,8 @@ BAD_PROBLEMS = [
     dict(idx_heads=0), dict(idx_dim=0), dict(heads=0), dict(qk_dim=0), dict(v_dim=0),
     dict(v_dim=577), dict(top_k=0), dict(softmax_scale=0.0), dict(softmax_scale=-1.0),
     dict(softmax_scale=float("inf")), dict(softmax_scale=float("nan")), dict(q_idx_dtype=2),
-    dict(idx_key_dtype=3), dict(q_dtype=2), dict(kv_dtype=-1), dict(out_dtype=2),
+    dict(idx_key_dtype=4), dict(idx_key_dtype=5), dict(q_dtype=2), dict(kv_dtype=-1), dict(kv_dtype=3),
+    dict(kv_dtype=5), dict(out_dtype=2),
 ]
 
 FAKE = 0x10000  # a 16-byte aligned non-NULL address: never dereferenced, calls fail validation first
@@ -104,6 +105,16 @@ def test_pointer_checks():
     assert b"k_scale" in lib.dsa_last_error()
     pk8 = good_problem(kv_dtype=2)
     assert lib.dsa_sparse_mla_decode(ctypes.byref(pk8), f, f, None, f, f, f, f, f, 1 << 40, None) == 1
+    assert b"kv_scale" in lib.dsa_last_error()
+    # MXFP8 keys need their E8M0 group scales (any alignment); 128-column
+    # tile scales of an FP8 cache are fp32 like the per-row ones
+    pmx = good_problem(idx_key_dtype=3)
+    assert lib.dsa_index_score(ctypes.byref(pmx), f, f, f, None, f, f, None) == 1
+    assert b"k_scale" in lib.dsa_last_error()
+    pt = good_problem(kv_dtype=4)
+    assert lib.dsa_sparse_mla_decode(ctypes.byref(pt), f, f, None, f, f, f, f, f, 1 << 40, None) == 1
+    assert b"kv_scale" in lib.dsa_last_error()
+    assert lib.dsa_sparse_mla_decode(ctypes.byref(pt), f, f, f + 2, f, f, f, f, f, 1 << 40, None) == 1
     assert b"kv_scale" in lib.dsa_last_error()
 
 

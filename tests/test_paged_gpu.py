@@ -54,8 +54,10 @@ def paginate(w, page_size, seed, spare=7):
 
     Di, Dqk = w.idx_dim, w.qk_dim
     return dict(table=table, num_pages=num_pages, page_size=page_size,
-                k_pages=pool(w.k_idx, (Di,)), k_scales=pool(w.k_scale, ()),
-                kv_pages=pool(w.kv, (Dqk,)), kv_scales=pool(w.kv_scale, ()))
+                k_pages=pool(w.k_idx, (Di,)),
+                k_scales=None if w.k_scale is None else pool(w.k_scale, w.k_scale.shape[2:]),
+                kv_pages=pool(w.kv, (Dqk,)),
+                kv_scales=None if w.kv_scale is None else pool(w.kv_scale, w.kv_scale.shape[2:]))
 
 
 def run_paged(w, pgd, dev="cuda:0"):
