@@ -33,7 +33,7 @@ def _samples(w):
     return want
 
 
-@pytest.mark.parametrize("name", ["decode8k", "decode128k", "prefill64k", "fp8_1m"])
+@pytest.mark.parametrize("name", ["decode8k", "decode128k", "prefill64k", "fp8_1m", "mx128k"])
 def test_full_size_workload(name):
     w = synth.make(name)
     print(f"\n[full] {name} B={w.batch} T={w.q_len} Lmax={w.max_seq_len} K={w.top_k}", flush=True)
