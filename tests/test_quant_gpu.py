@@ -127,3 +127,13 @@ def test_tile_scales_not_powers_of_two():
     factor = rng.uniform(0.55, 0.95, size=w.kv_scale.shape).astype(np.float32)
     w.kv_scale[:] = np.where(rng.random(w.kv_scale.shape) < 0.5, w.kv_scale, w.kv_scale * factor)
     _full_check(w)
+
+
+def test_partial_last_group_and_tile_on_portable_kernels():
+    # idx_dim 80 = groups of 32, 32 and 16; qk_dim 300 = tiles of 128, 128 and
+    # 44 (the scale shapes use ceil(dim / 32) and ceil(dim / 128)); these
+    # dims run on the portable kernels
+    w = _case(batch=2, q_len=2, max_seq_len=700, len_range=(400, 700), top_k=50, idx_heads=4, idx_dim=80,
+              heads=4, qk_dim=300, v_dim=260)
+    assert w.k_scale.shape[-1] == 3 and w.kv_scale.shape[-1] == 3
+    _full_check(w)
