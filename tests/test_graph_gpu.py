@@ -16,13 +16,14 @@ if not torch.cuda.is_available():
 @pytest.mark.parametrize("name,kw", [
     ("decode128k", dict(batch=3, max_seq_len=16384, len_range=(9000, 16384))),
     ("fp8_1m", dict(batch=2, max_seq_len=12000, len_range=(8000, 12000), top_k=1024)),
+    ("mx128k", dict(batch=2, q_len=2, max_seq_len=12000, len_range=(8000, 12000), top_k=1024)),
 ])
 def test_graph_replays_match_eager(name, kw):
     w = synth.make(name, **kw)
     d = G.to_device(w)
     out_dtype = G.out_torch_dtype(w)
     prob = dsa.forward_problem(d["q_idx"], d["k_idx"], d["q"], d["kv"], d["seq_lens"], w.top_k, w.v_dim,
-                               w.softmax_scale, out_dtype)
+                               w.softmax_scale, out_dtype, d["k_scale"], d["kv_scale"])
     ws = torch.zeros(dsa.forward_workspace_size(prob), dtype=torch.uint8, device="cuda")
     B, T, H = w.batch, w.q_len, w.heads
     outs = {"out": torch.empty((B, T, H, w.v_dim), dtype=out_dtype, device="cuda"),
