@@ -78,7 +78,10 @@ def _check_scores_close(w, got, ref):
     G_ = w.idx_dim // 32
     kdec = np.abs(np.array([oracle.e4m3_value(c) for c in range(256)])[w.k_idx]) * \
         np.repeat(2.0 ** (w.k_scale.astype(np.float64) - 127), 32, axis=-1)  # [B, L, Di]
-    qv = np.abs((w.q_idx.astype(np.uint32) << 16).view(np.float32).astype(np.float64))  # [B, T, Hi, Di]
+    if w.q_idx_dtype == synth.F32:
+        qv = np.abs(w.q_idx.astype(np.float64))
+    else:
+        qv = np.abs((w.q_idx.astype(np.uint32) << 16).view(np.float32).astype(np.float64))  # [B, T, Hi, Di]
     for b in range(w.batch):
         for t in range(w.q_len):
             vis = max(w.vis(b, t), 0)
@@ -137,3 +140,18 @@ def test_partial_last_group_and_tile_on_portable_kernels():
               heads=4, qk_dim=300, v_dim=260)
     assert w.k_scale.shape[-1] == 3 and w.kv_scale.shape[-1] == 3
     _full_check(w)
+
+
+def test_mx_fp32_queries_on_the_matrix_core_path():
+    # fp32 index queries (values bf16 cannot hold) quantised by the staging
+    # code of the scaled-MFMA kernel, one and two tokens
+    for T in (1, 2):
+        w = _case(batch=2, q_len=T, max_seq_len=2500, len_range=(1500, 2500), top_k=128)
+        rng = np.random.default_rng(21 + T)
+        x = rng.normal(size=w.q_idx.shape) * 2.0 ** rng.integers(-5, 6, w.q_idx.shape[:-1] + (1,))
+        w.q_idx = np.ascontiguousarray(x.astype(np.float32))
+        w.q_idx_dtype = synth.F32
+        d = G.to_device(w)
+        s = dsa.dsa_index_score(d["q_idx"], d["head_w"], d["k_idx"], d["seq_lens"], k_scale=d["k_scale"])
+        torch.cuda.synchronize()
+        _check_scores_close(w, s.cpu().numpy(), oracle.index_scores(w))
