@@ -48,6 +48,10 @@ CASES = {
     # causal multi-token chunk
     "prefill_chunk": dict(name="prefill64k", q_len=16, max_seq_len=4096, len_range=(4096, 4096),
                           top_k=512),
+    # a fresh prompt: every row is a new token (T = L), so token t sees t + 1
+    # positions and the first K - 1 tokens have fewer than K to select from
+    "prefill_fresh_prompt": dict(name="prefill64k", q_len=512, max_seq_len=512, len_range=(512, 512),
+                                 top_k=128),
     # fp8 index keys + fp8 latent cache, two draft tokens
     "fp8_drafts": dict(name="fp8_1m", batch=2, max_seq_len=16384, len_range=(9000, 16384), top_k=1024),
 }
