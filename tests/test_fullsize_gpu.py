@@ -71,3 +71,50 @@ def test_full_size_workload(name):
     out = r["out"].float().cpu().numpy()
     err = G.check_attention(w, out, r["lse"].cpu().numpy(), ref_out, ref_lse, want)
     print(f"[ok] {name}: {want.sum()} sampled queries exact, max abs attention err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name,page_size", [("decode128k", 64), ("mx128k", 256)])
+def test_full_size_paged_equals_contiguous(name, page_size):
+    # the paged launch at full size: the caches scattered over a pool of
+    # pages in a seeded random order (built on the device), every output equal
+    # to the contiguous path's bit for bit, sampled queries against the oracle
+    w = synth.make(name)
+    print(f"\n[full paged] {name} B={w.batch} Lmax={w.max_seq_len} page={page_size}", flush=True)
+    d = G.to_device(w)
+    B, L = w.batch, w.max_seq_len
+    max_pages = (L + page_size - 1) // page_size
+    num_pages = B * max_pages + 5
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    perm = torch.randperm(num_pages, generator=gen)[:B * max_pages]
+    table = perm.view(B, max_pages).to(torch.int32).cuda()
+
+    def pool(x):
+        if x is None:
+            return None
+        row = tuple(x.shape[2:])
+        pad = max_pages * page_size - L
+        if pad:
+            x = torch.cat([x, torch.zeros((B, pad) + row, dtype=x.dtype, device=x.device)], dim=1)
+        out = torch.zeros((num_pages, page_size) + row, dtype=x.dtype, device=x.device)
+        out[perm.cuda().long()] = x.reshape((B * max_pages, page_size) + row)
+        return out
+
+    kw = dict(out_dtype=G.out_torch_dtype(w), return_scores=True)
+    cont = dsa.dsa_forward(d["q_idx"], d["head_w"], d["k_idx"], d["q"], d["kv"], d["seq_lens"], w.top_k, w.v_dim,
+                           w.softmax_scale, k_scale=d["k_scale"], kv_scale=d["kv_scale"], **kw)
+    paged = dsa.dsa_forward_paged(d["q_idx"], d["head_w"], pool(d["k_idx"]), d["q"], pool(d["kv"]), d["seq_lens"],
+                                  table, w.top_k, w.v_dim, L, w.softmax_scale, k_scales=pool(d["k_scale"]),
+                                  kv_scales=pool(d["kv_scale"]), **kw)
+    torch.cuda.synchronize()
+    for k in ("topk_idx", "topk_count", "out", "lse"):
+        assert torch.equal(paged[k], cont[k]), f"paged {k} differs from the contiguous path"
+    for b in range(B):
+        vis = w.vis(b, w.q_len - 1)
+        assert torch.equal(paged["scores"][b, :, :vis - w.q_len + 1], cont["scores"][b, :, :vis - w.q_len + 1])
+    want = _samples(w)
+    ref_scores = oracle.index_scores(w, want)
+    scores = paged["scores"].cpu().numpy()
+    G.check_scores(w, scores, ref_scores, want)
+    ref_idx, ref_cnt = oracle.topk(w, ref_scores, want)
+    G.check_topk(w, paged["topk_idx"].cpu().numpy(), paged["topk_count"].cpu().numpy(), ref_idx, ref_cnt, want)
+    print(f"[ok] {name} paged: equal to contiguous, {want.sum()} sampled queries exact", flush=True)
