@@ -118,3 +118,24 @@ def test_full_size_paged_equals_contiguous(name, page_size):
     ref_idx, ref_cnt = oracle.topk(w, ref_scores, want)
     G.check_topk(w, paged["topk_idx"].cpu().numpy(), paged["topk_count"].cpu().numpy(), ref_idx, ref_cnt, want)
     print(f"[ok] {name} paged: equal to contiguous, {want.sum()} sampled queries exact", flush=True)
+
+
+def test_index_and_topk_at_the_largest_contiguous_length():
+    # the matrix-core indexer addresses a sequence's key rows with 32-bit byte
+    # offsets: bf16 rows allow Lmax * 256 < 2^31, so 8,388,544 positions is
+    # the largest length it takes; scores and the Top-K of the one query
+    # against the oracle
+    L = (2 ** 31 // 256) - 64
+    w = synth.make("decode128k", batch=1, max_seq_len=L, len_range=(L - 5, L - 5), heads=1, qk_dim=8, v_dim=8)
+    print(f"\n[max] Lmax={L} len={int(w.seq_lens[0])}", flush=True)
+    d = G.to_device(w)
+    p = dsa.make_problem(batch=1, q_len=1, max_seq_len=L, idx_heads=64, idx_dim=128, top_k=w.top_k)
+    assert "score=mfma" in dsa.kernel_choice(p)
+    scores = dsa.dsa_index_score(d["q_idx"], d["head_w"], d["k_idx"], d["seq_lens"])
+    idx, cnt = dsa.dsa_topk(scores, d["seq_lens"], w.top_k)
+    torch.cuda.synchronize()
+    ref = oracle.index_scores(w)
+    G.check_scores(w, scores.cpu().numpy(), ref)
+    ref_idx, ref_cnt = oracle.topk(w, ref)
+    G.check_topk(w, idx.cpu().numpy(), cnt.cpu().numpy(), ref_idx, ref_cnt)
+    print("[ok] largest length: scores exact, Top-K equal", flush=True)
