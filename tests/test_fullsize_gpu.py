@@ -120,18 +120,21 @@ def test_full_size_paged_equals_contiguous(name, page_size):
     print(f"[ok] {name} paged: equal to contiguous, {want.sum()} sampled queries exact", flush=True)
 
 
-def test_index_and_topk_at_the_largest_contiguous_length():
+@pytest.mark.parametrize("name,row_bytes", [("decode128k", 256), ("mx128k", 128)])
+def test_index_and_topk_at_the_largest_contiguous_length(name, row_bytes):
     # the matrix-core indexer addresses a sequence's key rows with 32-bit byte
-    # offsets: bf16 rows allow Lmax * 256 < 2^31, so 8,388,544 positions is
-    # the largest length it takes; scores and the Top-K of the one query
-    # against the oracle
-    L = (2 ** 31 // 256) - 64
-    w = synth.make("decode128k", batch=1, max_seq_len=L, len_range=(L - 5, L - 5), heads=1, qk_dim=8, v_dim=8)
-    print(f"\n[max] Lmax={L} len={int(w.seq_lens[0])}", flush=True)
+    # offsets: Lmax * row bytes < 2^31, so 8,388,544 bf16 or 16,777,152 MXFP8
+    # positions is the largest length it takes (for MXFP8 a skipped ring read
+    # then lands just past the scale buffer's bound); scores and the Top-K of
+    # the one query against the oracle
+    L = (2 ** 31 // row_bytes) - 64
+    w = synth.make(name, batch=1, max_seq_len=L, len_range=(L - 5, L - 5), heads=1, qk_dim=8, v_dim=8)
+    print(f"\n[max] {name} Lmax={L} len={int(w.seq_lens[0])}", flush=True)
     d = G.to_device(w)
-    p = dsa.make_problem(batch=1, q_len=1, max_seq_len=L, idx_heads=64, idx_dim=128, top_k=w.top_k)
+    p = dsa.make_problem(batch=1, q_len=1, max_seq_len=L, idx_heads=64, idx_dim=128, top_k=w.top_k,
+                         idx_key_dtype=w.idx_key_dtype)
     assert "score=mfma" in dsa.kernel_choice(p)
-    scores = dsa.dsa_index_score(d["q_idx"], d["head_w"], d["k_idx"], d["seq_lens"])
+    scores = dsa.dsa_index_score(d["q_idx"], d["head_w"], d["k_idx"], d["seq_lens"], k_scale=d["k_scale"])
     idx, cnt = dsa.dsa_topk(scores, d["seq_lens"], w.top_k)
     torch.cuda.synchronize()
     ref = oracle.index_scores(w)
