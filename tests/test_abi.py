@@ -225,3 +225,24 @@ def test_paging_needs_the_matrix_core_kernels():
     assert lib.dsa_index_score_paged(ctypes.byref(tiny), ctypes.byref(pg), f, f, f, None, f, f, None) == 2
     assert lib.dsa_sparse_mla_decode_paged(ctypes.byref(tiny), ctypes.byref(pg), f, f, None, f, f, f, f, f,
                                            1 << 40, None) == 2
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no CPU fallback: without libdsa.so every entry point raises DsaError
+    import subprocess
+    import sys
+    code = (
+        "import torch, indexed_sparse_attention_amd as dsa\n"
+        f"dsa.LIB_PATH = {str(tmp_path / 'absent.so')!r}\n"
+        "orig = dsa.load_library\n"
+        "dsa.load_library = lambda path=dsa.LIB_PATH: orig(path)\n"
+        "t = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)\n"
+        "try:\n"
+        "    dsa.dsa_index_score(t, torch.zeros(1, 1, 64), torch.zeros(1, 8, 128, dtype=torch.bfloat16),\n"
+        "                        torch.zeros(1, dtype=torch.int32))\n"
+        "except dsa.DsaError as e:\n"
+        "    print('raised', e)\n"
+        "else:\n"
+        "    raise SystemExit('no error')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0 and "raised" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
