@@ -158,6 +158,63 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _bad(msg: str):
+    raise DsaError(1, msg)
+
+
+_FLOAT_IN = (torch.float32, torch.bfloat16)
+_OUT_CODE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
+_CODE_IN = (torch.float32, torch.bfloat16, torch.float8_e4m3fn, torch.uint8)
+_E8M0 = (torch.uint8, torch.float8_e8m0fnu)
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape: tuple, dtypes: tuple, device=None) -> None:
+    """The C ABI sees raw pointers only, so this layer checks every tensor's
+    shape, dtype and device against the problem before a call: a tensor of
+    the wrong size would otherwise be read or written out of bounds.  (Kept
+    to a few attribute reads per tensor: it runs on every call.)"""
+    if (t.__class__ is torch.Tensor or isinstance(t, torch.Tensor)) and t.shape == shape and \
+            t.dtype in dtypes and (device is None or t.device == device):
+        return
+    if t is None:
+        _bad(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        _bad(f"{name} must be a torch.Tensor")
+    want = tuple(int(x) for x in shape)
+    if tuple(t.shape) != want:
+        _bad(f"{name} must have shape {want}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        _bad(f"{name} must have dtype in {[str(d) for d in dtypes]}, got {t.dtype}")
+    _bad(f"{name} is on {t.device}, expected {device}")
+
+
+def _expect_none(t, name: str, why: str) -> None:
+    if t is not None:
+        _bad(f"{name} must be None {why}")
+
+
+def _key_scale_check(k_scale, key_code: int, rows: tuple, idx_dim: int, device, name="k_scale") -> None:
+    if key_code == DSA_FP8_E4M3:
+        _expect(k_scale, name, rows, (torch.float32,), device)
+    elif key_code == DSA_MXFP8_E4M3:
+        _expect(k_scale, name, rows + (-(-idx_dim // 32),), _E8M0, device)
+    else:
+        _expect_none(k_scale, name, "unless the index keys are E4M3 codes")
+
+
+def _kv_scale_check(kv_scale, kv_code: int, rows: tuple, qk_dim: int, device, name="kv_scale") -> None:
+    if kv_code == DSA_FP8_E4M3:
+        _expect(kv_scale, name, rows, (torch.float32,), device)
+    elif kv_code == DSA_FP8_E4M3_T128:
+        _expect(kv_scale, name, rows + (-(-qk_dim // 128),), (torch.float32,), device)
+    else:
+        _expect_none(kv_scale, name, "unless the latent cache holds E4M3 codes")
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def make_problem(*, batch, q_len, max_seq_len, idx_heads=1, idx_dim=1, heads=1, qk_dim=1, v_dim=1,
                  top_k=1, softmax_scale=None, q_idx_dtype=DSA_BF16, idx_key_dtype=DSA_BF16,
                  q_dtype=DSA_BF16, kv_dtype=DSA_BF16, out_dtype=DSA_BF16) -> Problem:
@@ -197,31 +254,47 @@ def kernel_choice(p: Problem) -> str:
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
-    if nbytes == 0:
-        return workspace
     if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+            _bad(f"workspace must be a tensor on {device}")
         return workspace
+    if nbytes == 0:
+        return None
     # zeroed: the leading counter region must be zero on the first call
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
-def _index_problem(q_idx, k_idx, seq_lens, top_k=1, k_scale=None) -> dict:
+def _index_problem(q_idx, head_w, k_idx, seq_lens, top_k=1, k_scale=None, skip_head_w=False) -> dict:
+    """Problem fields of the indexer, with every indexer tensor checked
+    (head_w may be left out, as None, only where skip_head_w says so)."""
+    if not isinstance(q_idx, torch.Tensor) or q_idx.dim() != 4:
+        _bad("q_idx must be a [B,T,Hi,Di] tensor")
     B, T, Hi, Di = q_idx.shape
-    assert k_idx.dim() == 3 and k_idx.shape[0] == B and k_idx.shape[2] == Di, "k_idx must be [B,Lmax,Di]"
-    assert seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]"
-    return dict(batch=B, q_len=T, max_seq_len=k_idx.shape[1], idx_heads=Hi, idx_dim=Di,
-                top_k=top_k, q_idx_dtype=dtype_code(q_idx), idx_key_dtype=key_dtype_code(k_idx, k_scale))
+    dev = q_idx.device
+    _expect(q_idx, "q_idx", (B, T, Hi, Di), _FLOAT_IN, dev)
+    if not isinstance(k_idx, torch.Tensor) or k_idx.dim() != 3:
+        _bad("k_idx must be a [B,Lmax,Di] tensor")
+    L = k_idx.shape[1]
+    _expect(k_idx, "k_idx", (B, L, Di), _CODE_IN, dev)
+    if head_w is not None or not skip_head_w:
+        _expect(head_w, "head_w", (B, T, Hi), (torch.float32,), dev)
+    _expect(seq_lens, "seq_lens", (B,), (torch.int32,), dev)
+    key = key_dtype_code(k_idx, k_scale)
+    _key_scale_check(k_scale, key, (B, L), Di, dev)
+    return dict(batch=B, q_len=T, max_seq_len=L, idx_heads=Hi, idx_dim=Di, top_k=top_k,
+                q_idx_dtype=dtype_code(q_idx), idx_key_dtype=key)
 
 
 def dsa_index_score(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor,
                     seq_lens: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
                     scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     lib = load_library()
-    d = _index_problem(q_idx, k_idx, seq_lens, k_scale=k_scale)
+    d = _index_problem(q_idx, head_w, k_idx, seq_lens, k_scale=k_scale)
     p = make_problem(**d)
+    shape = (d["batch"], d["q_len"], d["max_seq_len"])
     if scores is None:
-        scores = torch.empty((d["batch"], d["q_len"], d["max_seq_len"]), dtype=torch.float32,
-                             device=q_idx.device)
+        scores = torch.empty(shape, dtype=torch.float32, device=q_idx.device)
+    _expect(scores, "scores", shape, (torch.float32,), q_idx.device)
     _check(lib.dsa_index_score(ctypes.byref(p), _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _ptr(k_scale),
                                _ptr(seq_lens), _ptr(scores), _stream(stream)))
     return scores
@@ -230,15 +303,42 @@ def dsa_index_score(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tens
 def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
              workspace: Optional[torch.Tensor] = None, stream=None):
     lib = load_library()
+    if not isinstance(scores, torch.Tensor) or scores.dim() != 3:
+        _bad("scores must be a [B,T,Lmax] tensor")
     B, T, L = scores.shape
+    dev = scores.device
+    _expect(scores, "scores", (B, T, L), (torch.float32,), dev)
+    _expect(seq_lens, "seq_lens", (B,), (torch.int32,), dev)
     p = make_problem(batch=B, q_len=T, max_seq_len=L, top_k=top_k)
-    idx = torch.empty((B, T, top_k), dtype=torch.int32, device=scores.device)
-    cnt = torch.empty((B, T), dtype=torch.int32, device=scores.device)
+    idx = torch.empty((B, T, top_k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, T), dtype=torch.int32, device=dev)
     nbytes = lib.dsa_topk_workspace_size(ctypes.byref(p))
-    ws = _workspace(nbytes, scores.device, workspace)
+    ws = _workspace(nbytes, dev, workspace)
     _check(lib.dsa_topk(ctypes.byref(p), _ptr(scores), _ptr(seq_lens), _ptr(idx), _ptr(cnt), _ptr(ws),
-                        nbytes if workspace is None else ws.numel(), _stream(stream)))
+                        _nbytes(ws), _stream(stream)))
     return idx, cnt
+
+
+def _mla_checks(q, kv, seq_lens, kv_scale, v_dim, topk_idx=None, top_k=None, kv_rows=None):
+    """Checks the attention tensors; returns (B, T, H, Dqk, kv_code)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        _bad("q must be a [B,T,H,Dqk] tensor")
+    B, T, H, Dqk = q.shape
+    dev = q.device
+    _expect(q, "q", (B, T, H, Dqk), _FLOAT_IN, dev)
+    if kv_rows is None:
+        if not isinstance(kv, torch.Tensor) or kv.dim() != 3:
+            _bad("kv must be a [B,Lmax,Dqk] tensor")
+        kv_rows = (B, kv.shape[1])
+    _expect(kv, "kv", kv_rows + (Dqk,), _CODE_IN, dev)
+    _expect(seq_lens, "seq_lens", (B,), (torch.int32,), dev)
+    if not 1 <= v_dim <= Dqk:
+        _bad(f"v_dim must be in [1, {Dqk}], got {v_dim}")
+    code = kv_dtype_code(kv, kv_scale)
+    _kv_scale_check(kv_scale, code, kv_rows, Dqk, dev)
+    if topk_idx is not None:
+        _expect(topk_idx, "topk_idx", (B, T, top_k), (torch.int32,), dev)
+    return B, T, H, Dqk, code
 
 
 def dsa_sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, topk_idx: torch.Tensor,
@@ -247,58 +347,79 @@ def dsa_sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, topk_idx: torch.Ten
                           return_lse: bool = True, workspace: Optional[torch.Tensor] = None,
                           stream=None):
     lib = load_library()
-    B, T, H, Dqk = q.shape
-    assert kv.dim() == 3 and kv.shape[0] == B and kv.shape[2] == Dqk, "kv must be [B,Lmax,Dqk]"
+    if not isinstance(topk_idx, torch.Tensor) or topk_idx.dim() != 3:
+        _bad("topk_idx must be a [B,T,K] tensor")
     K = topk_idx.shape[-1]
-    assert topk_idx.shape == (B, T, K) and topk_idx.dtype == torch.int32
+    B, T, H, Dqk, kv_code = _mla_checks(q, kv, seq_lens, kv_scale, v_dim, topk_idx, K)
     if out_dtype is None:
         out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out_dtype not in _FLOAT_IN:
+        _bad(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     p = make_problem(batch=B, q_len=T, max_seq_len=kv.shape[1], heads=H, qk_dim=Dqk, v_dim=v_dim,
                      top_k=K, softmax_scale=softmax_scale, q_dtype=dtype_code(q),
-                     kv_dtype=kv_dtype_code(kv, kv_scale), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
+                     kv_dtype=kv_code, out_dtype=_OUT_CODE[out_dtype])
     out = torch.empty((B, T, H, v_dim), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if return_lse else None
     nbytes = lib.dsa_sparse_mla_workspace_size(ctypes.byref(p))
     ws = _workspace(nbytes, q.device, workspace)
     _check(lib.dsa_sparse_mla_decode(ctypes.byref(p), _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(topk_idx),
-                                     _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(stream)))
+                                     _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                     _stream(stream)))
     return out, lse
 
 
 def forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale=None,
-                    out_dtype: Optional[torch.dtype] = None, k_scale=None, kv_scale=None) -> Problem:
-    d = _index_problem(q_idx, k_idx, seq_lens, top_k, k_scale)
-    B, T, H, Dqk = q.shape
-    assert (B, T) == (d["batch"], d["q_len"]) and kv.shape == (B, d["max_seq_len"], Dqk)
+                    out_dtype: Optional[torch.dtype] = None, k_scale=None, kv_scale=None,
+                    head_w=None) -> Problem:
+    """dsa_problem of a dsa_forward call (head_w, when given, is checked too)."""
+    d = _index_problem(q_idx, head_w, k_idx, seq_lens, top_k, k_scale, skip_head_w=True)
+    B, T, H, Dqk, kv_code = _mla_checks(q, kv, seq_lens, kv_scale, v_dim,
+                                        kv_rows=(d["batch"], d["max_seq_len"]))
+    if (B, T) != (d["batch"], d["q_len"]):
+        _bad(f"q is [{B},{T},...] but q_idx is [{d['batch']},{d['q_len']},...]")
     if out_dtype is None:
         out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out_dtype not in _FLOAT_IN:
+        _bad(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     d.update(heads=H, qk_dim=Dqk, v_dim=v_dim, softmax_scale=softmax_scale, q_dtype=dtype_code(q),
-             kv_dtype=kv_dtype_code(kv, kv_scale), out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
+             kv_dtype=kv_code, out_dtype=_OUT_CODE[out_dtype])
     return make_problem(**d)
+
+
+_OUT_KEYS = ("out", "lse", "topk_idx", "topk_count", "scores")
 
 
 def _forward_outputs(p: Problem, dev, top_k: int, v_dim: int, return_scores: bool, return_lse: bool,
                      out: Optional[dict]) -> dict:
-    B, T, H = p.batch, p.q_len, p.heads
+    """Outputs of a forward call: caller-supplied tensors (checked against the
+    problem) or new ones."""
+    B, T, H, L = p.batch, p.q_len, p.heads, p.max_seq_len
+    spec = {"out": ((B, T, H, v_dim), (_torch_dtype(p.out_dtype),)),
+            "lse": ((B, T, H), (torch.float32,)),
+            "topk_idx": ((B, T, top_k), (torch.int32,)),
+            "topk_count": ((B, T), (torch.int32,)),
+            "scores": ((B, T, L), (torch.float32,))}
     o = dict(out or {})
-    if "out" not in o:
-        o["out"] = torch.empty((B, T, H, v_dim), dtype=_torch_dtype(p.out_dtype), device=dev)
-    if return_lse and "lse" not in o:
-        o["lse"] = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    if "topk_idx" not in o:
-        o["topk_idx"] = torch.empty((B, T, top_k), dtype=torch.int32, device=dev)
-    if "topk_count" not in o:
-        o["topk_count"] = torch.empty((B, T), dtype=torch.int32, device=dev)
-    if return_scores and "scores" not in o:
-        o["scores"] = torch.empty((B, T, p.max_seq_len), dtype=torch.float32, device=dev)
-    return o
+    for k in o:
+        if k not in _OUT_KEYS:
+            _bad(f"unknown output {k!r} (expected one of {_OUT_KEYS})")
+        if o[k] is not None:
+            _expect(o[k], k, spec[k][0], spec[k][1], dev)
+    for k in ("out", "topk_idx", "topk_count"):
+        if o.get(k) is None:
+            o[k] = torch.empty(spec[k][0], dtype=spec[k][1][0], device=dev)
+    if return_lse and o.get("lse") is None:
+        o["lse"] = torch.empty(spec["lse"][0], dtype=torch.float32, device=dev)
+    if return_scores and o.get("scores") is None:
+        o["scores"] = torch.empty(spec["scores"][0], dtype=torch.float32, device=dev)
+    return {k: v for k, v in o.items() if v is not None}
 
 
 def _events(stage_events):
     if stage_events is None:
         return None
-    assert len(stage_events) == FORWARD_STAGES + 1
+    if len(stage_events) != FORWARD_STAGES + 1:
+        _bad(f"stage_events must hold {FORWARD_STAGES + 1} events")
     return (ctypes.c_void_p * (FORWARD_STAGES + 1))(*[e.cuda_event for e in stage_events])
 
 
@@ -311,27 +432,47 @@ def dsa_forward_paged(q_idx: torch.Tensor, head_w: torch.Tensor, k_pages: torch.
                       workspace: Optional[torch.Tensor] = None, stage_events: Optional[Sequence] = None,
                       stream=None) -> dict:
     """Whole path over paged caches: k_pages [num_pages, page_size, Di],
-    kv_pages [num_pages, page_size, Dqk] (scales [num_pages, page_size]),
-    block_table int32 [batch, max_pages] shared by both caches."""
+    kv_pages [num_pages, page_size, Dqk] (scales [num_pages, page_size] or
+    [num_pages, page_size, groups]), block_table int32 [batch, max_pages]
+    shared by both caches."""
     lib = load_library()
-    num_pages, page_size, Di = k_pages.shape
-    assert kv_pages.shape[:2] == (num_pages, page_size)
-    B, T, Hi, _ = q_idx.shape
-    _, _, H, Dqk = q.shape
+    if not isinstance(q_idx, torch.Tensor) or q_idx.dim() != 4:
+        _bad("q_idx must be a [B,T,Hi,Di] tensor")
+    B, T, Hi, Di = q_idx.shape
+    dev = q_idx.device
+    _expect(q_idx, "q_idx", (B, T, Hi, Di), _FLOAT_IN, dev)
+    _expect(head_w, "head_w", (B, T, Hi), (torch.float32,), dev)
+    _expect(seq_lens, "seq_lens", (B,), (torch.int32,), dev)
+    if not isinstance(k_pages, torch.Tensor) or k_pages.dim() != 3:
+        _bad("k_pages must be a [num_pages, page_size, Di] tensor")
+    num_pages, page_size = k_pages.shape[:2]
+    _expect(k_pages, "k_pages", (num_pages, page_size, Di), _CODE_IN, dev)
+    key = key_dtype_code(k_pages, k_scales)
+    _key_scale_check(k_scales, key, (num_pages, page_size), Di, dev, "k_scales")
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2:
+        _bad("block_table must be an int32 [batch, max_pages] tensor")
+    _expect(block_table, "block_table", (B, block_table.shape[1]), (torch.int32,), dev)
+    if block_table.shape[1] * page_size < max_seq_len:
+        _bad(f"block_table covers {block_table.shape[1] * page_size} rows < max_seq_len {max_seq_len}")
+    _, _, H, Dqk, kv_code = _mla_checks(q, kv_pages, seq_lens, kv_scales, v_dim,
+                                        kv_rows=(num_pages, page_size))
+    if tuple(q.shape[:2]) != (B, T):
+        _bad(f"q is [{q.shape[0]},{q.shape[1]},...] but q_idx is [{B},{T},...]")
     if out_dtype is None:
         out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out_dtype not in _FLOAT_IN:
+        _bad(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     p = make_problem(batch=B, q_len=T, max_seq_len=max_seq_len, idx_heads=Hi, idx_dim=Di, heads=H,
                      qk_dim=Dqk, v_dim=v_dim, top_k=top_k, softmax_scale=softmax_scale,
-                     q_idx_dtype=dtype_code(q_idx), idx_key_dtype=key_dtype_code(k_pages, k_scales),
-                     q_dtype=dtype_code(q), kv_dtype=kv_dtype_code(kv_pages, kv_scales),
-                     out_dtype=dtype_code(torch.empty(0, dtype=out_dtype)))
-    pg = make_paging(block_table, page_size, num_pages)
-    o = _forward_outputs(p, q.device, top_k, v_dim, return_scores, return_lse, out)
-    ws = _workspace(lib.dsa_forward_workspace_size(ctypes.byref(p)), q.device, workspace)
+                     q_idx_dtype=dtype_code(q_idx), idx_key_dtype=key, q_dtype=dtype_code(q),
+                     kv_dtype=kv_code, out_dtype=_OUT_CODE[out_dtype])
+    pg = Paging(_ptr(block_table), page_size, block_table.shape[1], num_pages)
+    o = _forward_outputs(p, dev, top_k, v_dim, return_scores, return_lse, out)
+    ws = _workspace(lib.dsa_forward_workspace_size(ctypes.byref(p)), dev, workspace)
     _check(lib.dsa_forward_paged(ctypes.byref(p), ctypes.byref(pg), _ptr(q_idx), _ptr(head_w), _ptr(k_pages),
                                  _ptr(k_scales), _ptr(q), _ptr(kv_pages), _ptr(kv_scales), _ptr(seq_lens),
                                  _ptr(o.get("scores")), _ptr(o["topk_idx"]), _ptr(o["topk_count"]),
-                                 _ptr(o["out"]), _ptr(o.get("lse")), _ptr(ws), ws.numel(), _stream(stream),
+                                 _ptr(o["out"]), _ptr(o.get("lse")), _ptr(ws), _nbytes(ws), _stream(stream),
                                  _events(stage_events)))
     return o
 
@@ -344,30 +485,17 @@ def dsa_forward(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor, 
                 out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
                 stage_events: Optional[Sequence] = None, stream=None) -> dict:
     """Whole path.  ``out`` may hold preallocated 'out', 'lse', 'topk_idx',
-    'topk_count', 'scores' tensors (reused as given)."""
+    'topk_count', 'scores' tensors (checked against the problem, reused as
+    given)."""
     lib = load_library()
-    p = forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale, out_dtype, k_scale, kv_scale)
+    p = forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale, out_dtype, k_scale,
+                        kv_scale, head_w=head_w)
     dev = q.device
-    B, T, H = p.batch, p.q_len, p.heads
-    o = dict(out or {})
-    if "out" not in o:
-        o["out"] = torch.empty((B, T, H, v_dim), dtype=_torch_dtype(p.out_dtype), device=dev)
-    if return_lse and "lse" not in o:
-        o["lse"] = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    if "topk_idx" not in o:
-        o["topk_idx"] = torch.empty((B, T, top_k), dtype=torch.int32, device=dev)
-    if "topk_count" not in o:
-        o["topk_count"] = torch.empty((B, T), dtype=torch.int32, device=dev)
-    if return_scores and "scores" not in o:
-        o["scores"] = torch.empty((B, T, p.max_seq_len), dtype=torch.float32, device=dev)
+    o = _forward_outputs(p, dev, top_k, v_dim, return_scores, return_lse, out)
     nbytes = lib.dsa_forward_workspace_size(ctypes.byref(p))
     ws = _workspace(nbytes, dev, workspace)
-    ev = None
-    if stage_events is not None:
-        assert len(stage_events) == FORWARD_STAGES + 1
-        ev = (ctypes.c_void_p * (FORWARD_STAGES + 1))(*[e.cuda_event for e in stage_events])
     _check(lib.dsa_forward(ctypes.byref(p), _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _ptr(k_scale),
                            _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(seq_lens), _ptr(o.get("scores")),
                            _ptr(o["topk_idx"]), _ptr(o["topk_count"]), _ptr(o["out"]),
-                           _ptr(o.get("lse")), _ptr(ws), ws.numel(), _stream(stream), ev))
+                           _ptr(o.get("lse")), _ptr(ws), _nbytes(ws), _stream(stream), _events(stage_events)))
     return o

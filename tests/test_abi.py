@@ -246,3 +246,120 @@ def test_missing_library_fails_loudly(tmp_path):
         "    raise SystemExit('no error')\n")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 0 and "raised" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
+
+
+# ---------------------------------------------------------------- the binding's tensor checks
+# The C ABI takes raw pointers, so the Python layer is what compares every
+# tensor with the problem; a wrong shape or dtype must raise DsaError before
+# any pointer reaches the library.  CPU tensors suffice: the checks run first.
+def _cpu_forward_args(B=2, T=1, L=256, Hi=64, Di=128, H=128, Dqk=576, fp8=None):
+    import torch
+    a = dict(q_idx=torch.zeros(B, T, Hi, Di, dtype=torch.bfloat16),
+             head_w=torch.zeros(B, T, Hi), k_idx=torch.zeros(B, L, Di, dtype=torch.bfloat16),
+             q=torch.zeros(B, T, H, Dqk, dtype=torch.bfloat16), kv=torch.zeros(B, L, Dqk, dtype=torch.bfloat16),
+             seq_lens=torch.full((B,), L, dtype=torch.int32), top_k=64, v_dim=512)
+    if fp8 == "row":
+        a.update(k_idx=torch.zeros(B, L, Di, dtype=torch.uint8), k_scale=torch.ones(B, L),
+                 kv=torch.zeros(B, L, Dqk, dtype=torch.uint8), kv_scale=torch.ones(B, L))
+    elif fp8 == "mx":
+        a.update(k_idx=torch.zeros(B, L, Di, dtype=torch.uint8), k_scale=torch.full((B, L, Di // 32), 127, dtype=torch.uint8),
+                 kv=torch.zeros(B, L, Dqk, dtype=torch.uint8), kv_scale=torch.ones(B, L, 5))
+    return a
+
+
+def _expect_dsa_error(fn, *args, match, **kw):
+    with pytest.raises(dsa.DsaError) as e:
+        fn(*args, **kw)
+    assert e.value.status == 1 and match in str(e.value), str(e.value)
+
+
+@pytest.mark.parametrize("field,bad,match", [
+    ("head_w", ("shape", (2, 1, 63)), "head_w"),
+    ("head_w", ("dtype", "bfloat16"), "head_w"),
+    ("seq_lens", ("shape", (3,)), "seq_lens"),
+    ("seq_lens", ("dtype", "int64"), "seq_lens"),
+    ("k_idx", ("shape", (2, 256, 64)), "k_idx"),
+    ("k_idx", ("shape", (3, 256, 128)), "k_idx"),
+    ("q", ("shape", (2, 2, 128, 576)), "q"),
+    ("kv", ("shape", (2, 255, 576)), "kv"),
+    ("kv", ("shape", (2, 256, 512)), "kv"),
+])
+def test_binding_checks_forward_inputs(field, bad, match):
+    import torch
+    a = _cpu_forward_args()
+    kind, v = bad
+    if kind == "shape":
+        a[field] = torch.zeros(v, dtype=a[field].dtype)
+    else:
+        a[field] = a[field].to(getattr(torch, v))
+    _expect_dsa_error(dsa.dsa_forward, **a, match=match)
+
+
+@pytest.mark.parametrize("fp8,field,shape,match", [
+    ("row", "k_scale", (2, 255), "k_scale"),
+    ("row", "kv_scale", (2, 256, 2), "kv_scale"),
+    ("mx", "k_scale", (2, 256, 3), "k_scale"),
+    ("mx", "kv_scale", (2, 256, 4), "kv_scale"),
+])
+def test_binding_checks_scale_layouts(fp8, field, shape, match):
+    import torch
+    a = _cpu_forward_args(fp8=fp8)
+    a[field] = torch.zeros(shape, dtype=a[field].dtype)
+    _expect_dsa_error(dsa.dsa_forward, **a, match=match)
+    if field == "k_scale":
+        _expect_dsa_error(dsa.dsa_index_score, a["q_idx"], a["head_w"], a["k_idx"], a["seq_lens"],
+                          k_scale=a[field], match=match)
+    else:
+        idx = torch.zeros(2, 1, 64, dtype=torch.int32)
+        _expect_dsa_error(dsa.dsa_sparse_mla_decode, a["q"], a["kv"], idx, a["seq_lens"], 512,
+                          kv_scale=a[field], match=match)
+
+
+@pytest.mark.parametrize("key,shape,dtype,match", [
+    ("out", (2, 1, 128, 511), "bfloat16", "out"),
+    ("out", (2, 1, 128, 512), "float32", "out"),       # a bf16 problem with an fp32 buffer
+    ("lse", (2, 1, 127), "float32", "lse"),
+    ("topk_idx", (2, 1, 63), "int32", "topk_idx"),
+    ("topk_idx", (2, 1, 64), "int64", "topk_idx"),
+    ("topk_count", (2,), "int32", "topk_count"),
+    ("scores", (2, 1, 255), "float32", "scores"),
+    ("bogus", (1,), "float32", "bogus"),
+])
+def test_binding_checks_preallocated_outputs(key, shape, dtype, match):
+    import torch
+    a = _cpu_forward_args()
+    _expect_dsa_error(dsa.dsa_forward, **a, out={key: torch.zeros(shape, dtype=getattr(torch, dtype))}, match=match)
+
+
+def test_binding_checks_the_other_entry_points():
+    import torch
+    a = _cpu_forward_args()
+    _expect_dsa_error(dsa.dsa_index_score, a["q_idx"], a["head_w"], a["k_idx"], a["seq_lens"],
+                      scores=torch.zeros(2, 1, 100), match="scores")
+    _expect_dsa_error(dsa.dsa_topk, torch.zeros(2, 1, 256, dtype=torch.bfloat16), a["seq_lens"], 64, match="scores")
+    _expect_dsa_error(dsa.dsa_topk, torch.zeros(2, 1, 256), torch.zeros(3, dtype=torch.int32), 64, match="seq_lens")
+    _expect_dsa_error(dsa.dsa_sparse_mla_decode, a["q"], a["kv"], torch.zeros(2, 2, 64, dtype=torch.int32),
+                      a["seq_lens"], 512, match="topk_idx")
+    _expect_dsa_error(dsa.dsa_sparse_mla_decode, a["q"], a["kv"], torch.zeros(2, 1, 64, dtype=torch.int32),
+                      a["seq_lens"], 577, match="v_dim")
+
+
+def test_binding_checks_paged_inputs():
+    import torch
+    a = _cpu_forward_args()
+    pages = dict(k_pages=torch.zeros(10, 64, 128, dtype=torch.bfloat16),
+                 kv_pages=torch.zeros(10, 64, 576, dtype=torch.bfloat16),
+                 block_table=torch.zeros(2, 4, dtype=torch.int32))
+    base = dict(q_idx=a["q_idx"], head_w=a["head_w"], q=a["q"], seq_lens=a["seq_lens"], top_k=64, v_dim=512,
+                max_seq_len=256)
+    bad = [
+        (dict(block_table=torch.zeros(3, 4, dtype=torch.int32)), "block_table"),
+        (dict(block_table=torch.zeros(2, 3, dtype=torch.int32)), "max_seq_len"),
+        (dict(k_pages=torch.zeros(10, 64, 64, dtype=torch.bfloat16)), "k_pages"),
+        (dict(kv_pages=torch.zeros(10, 64, 512, dtype=torch.bfloat16)), "kv"),
+        (dict(kv_pages=torch.zeros(9, 64, 576, dtype=torch.bfloat16)), "kv"),
+    ]
+    for change, match in bad:
+        kw = dict(base, **pages)
+        kw.update(change)
+        _expect_dsa_error(dsa.dsa_forward_paged, match=match, **kw)

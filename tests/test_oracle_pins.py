@@ -126,6 +126,32 @@ def test_scores_relu_identities_against_matmul(T):
             assert np.all(np.isnan(sp[b, t, vis:]))  # causal: not visible
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_scores_int64_brute_force(T):
+    # Small integer inputs make every score an integer, so plain Python
+    # integer arithmetic (no floating point anywhere: products, the ReLU as a
+    # comparison, the weighted head sum) gives the exact value, which the
+    # fp64 oracle must reproduce exactly.  Lengths are ragged and causal.
+    B, Hi, Di, L = 2, 4, 9, 13
+    rng = np.random.default_rng(99 + T)
+    qi = rng.integers(-4, 5, (B, T, Hi, Di))
+    ki = rng.integers(-4, 5, (B, L, Di))
+    wh = rng.integers(1, 9, (B, T, Hi))
+    lens = np.array([L, L - 5], np.int32)
+    got = oracle.index_scores(problem(qi.astype(np.float32), wh.astype(np.float32), ki.astype(np.float32),
+                                      seq_lens=lens))
+    for b in range(B):
+        for t in range(T):
+            vis = int(lens[b]) - T + 1 + t
+            for s in range(vis):
+                want = 0
+                for h in range(Hi):
+                    dot = sum(int(qi[b, t, h, i]) * int(ki[b, s, i]) for i in range(Di))
+                    want += int(wh[b, t, h]) * (dot if dot > 0 else 0)
+                assert got[b, t, s] == want, (b, t, s, got[b, t, s], want)
+            assert np.all(np.isnan(got[b, t, vis:]))
+
+
 def test_scores_bf16_inputs_equal_f32_inputs():
     qi = RNG.integers(-4, 5, (1, 2, 3, 8)).astype(np.float32)
     ki = RNG.integers(-4, 5, (1, 6, 8)).astype(np.float32)

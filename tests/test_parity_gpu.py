@@ -54,6 +54,13 @@ CASES = {
                                  top_k=128),
     # fp8 index keys + fp8 latent cache, two draft tokens
     "fp8_drafts": dict(name="fp8_1m", batch=2, max_seq_len=16384, len_range=(9000, 16384), top_k=1024),
+    # an odd token count: the two-token score kernels (bf16 and per-row e4m3
+    # keys) then run a last token pair whose second token does not exist
+    # (its loads are clamped, its stores and histogram updates skipped)
+    "prefill_chunk_odd": dict(name="prefill64k", q_len=3, max_seq_len=5000, len_range=(3000, 5000),
+                              batch=2, top_k=700),
+    "fp8_drafts_odd": dict(name="fp8_1m", batch=2, q_len=3, max_seq_len=9000, len_range=(5000, 9000),
+                           top_k=600),
 }
 
 
@@ -74,6 +81,20 @@ def test_topk_modes_match_oracle(mode):
         _full_check(_case("fp8_1m", batch=2, max_seq_len=20000, len_range=(12000, 20000), top_k=1500))
     finally:
         del os.environ["DSA_TOPK_MODE"]
+
+
+@pytest.mark.parametrize("name", ["decode8k", "fp8_1m", "mx128k"])
+def test_two_tokens_with_fewer_rows_than_tokens(name):
+    # q_len 2 with len_b = 0 (no token sees anything), 1 (the first token
+    # sees nothing, the second one position), 2, and a long ragged row, on
+    # the two-token score kernels of bf16, per-row e4m3 and MXFP8 keys
+    w = _case(name, batch=4, q_len=2, max_seq_len=3000, len_range=(2, 3000), top_k=256)
+    w.seq_lens[:] = [0, 1, 2, 2999]
+    got, _ = _full_check(w)
+    assert got["topk_count"].tolist() == [[0, 0], [0, 1], [1, 2], [256, 256]]
+    assert np.all(got["topk_idx"][0] == -1) and np.all(got["out"][0] == 0)
+    assert np.all(np.isneginf(got["lse"][0])) and np.isneginf(got["lse"][1, 0]).all()
+    assert got["topk_idx"][1, 1, 0] == 0 and np.all(got["topk_idx"][1, 1, 1:] == -1)
 
 
 def test_entry_points_separately():

@@ -109,6 +109,61 @@ def test_mx_query_quantisation_rounds_like_oracle(generic):
     _check_scores_close(w, s.cpu().numpy(), oracle.index_scores(w))
 
 
+def _one_element_probe(w, seed):
+    """Rounding queries, and keys and head weights that turn each score into
+    one dequantised query element: key row s is +-1 (E4M3 0x38 / 0xB8) in
+    dimension (s // 2) % Di alone, with every E8M0 group scale 1 (byte 127),
+    and each query token weights one head by 1 and the rest by 0.  Then
+    S[s] = max(0, +-q^[h, i]) exactly (every other product and head term is
+    an exact zero), so the scores show every element of the query as the
+    kernel quantised it, bit for bit."""
+    B, T, Hi, Di = w.q_idx.shape
+    w.q_idx[:] = _rounding_queries(w, seed)
+    L = w.max_seq_len
+    s = np.arange(L)
+    k = np.zeros((L, Di), np.uint8)
+    k[s, (s // 2) % Di] = np.where(s % 2 == 0, 0x38, 0xB8)
+    w.k_idx[:] = k[None]
+    w.k_scale[:] = 127
+    heads = [0, 1, 2, 3, 17, 33, 50, 63]  # 0: outlier group, 1: zero group, 2: clamped group
+    w.head_w[:] = 0.0
+    for n, (b, t) in enumerate(np.ndindex(B, T)):
+        w.head_w[b, t, heads[n % len(heads)]] = 1.0
+    return w
+
+
+@pytest.mark.parametrize("generic", [False, True])
+@pytest.mark.parametrize("T", [1, 2])
+def test_mx_query_rounding_exact(T, generic):
+    # both score kernels (one and two tokens per segment) and the portable
+    # kernel must quantise the index query exactly as the oracle does
+    w = _one_element_probe(_case(batch=4, q_len=T, max_seq_len=2 * 128 * 3, len_range=(2 * 128 * 3,) * 2,
+                                 top_k=64), seed=5 + T)
+    d = G.to_device(w)
+    if generic:
+        os.environ["DSA_FORCE_GENERIC"] = "1"
+    try:
+        got = dsa.dsa_index_score(d["q_idx"], d["head_w"], d["k_idx"], d["seq_lens"], k_scale=d["k_scale"])
+        torch.cuda.synchronize()
+    finally:
+        if generic:
+            del os.environ["DSA_FORCE_GENERIC"]
+    ref = oracle.index_scores(w)
+    got = got.cpu().numpy().astype(np.float64)
+    for b in range(w.batch):
+        for t in range(w.q_len):
+            vis = w.vis(b, t)
+            g, r = got[b, t, :vis], ref[b, t, :vis]
+            # the group whose exponent clamps at -127 holds values near 2^-124:
+            # their dequantised elements are fp32 subnormals, which the matrix
+            # core may flush; everywhere else equality is exact
+            tiny = np.abs(r) < 2.0 ** -126
+            bad = np.flatnonzero((g != r) & ~(tiny & (g == 0.0)))
+            assert bad.size == 0, (f"b={b} t={t}: {bad.size} of {vis} scores differ, first s={bad[0]} "
+                                   f"gpu={g[bad[0]]!r} oracle={r[bad[0]]!r}")
+            assert np.count_nonzero(r) > vis // 4  # the probe does see the query's elements
+
+
 def test_mx_paged_matches_oracle_and_contiguous():
     w = _case(batch=3, q_len=2, max_seq_len=7000, len_range=(4000, 7000), top_k=512)
     got = run_paged(w, paginate(w, 64, seed=13))
