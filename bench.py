@@ -306,8 +306,10 @@ def main():
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
+    h0 = time.perf_counter()
     for i in range(args.steps):
         run(i)
+    host_us = (time.perf_counter() - h0) / args.steps * 1e6  # host time to issue one step
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -373,7 +375,7 @@ def main():
                    "indexer": f"{w.idx_heads}x{w.idx_dim}", "mla_heads": H, "qk_dim": w.qk_dim,
                    "v_dim": w.v_dim, "graph": graphs is not None, "rotate": R, "paged": args.paged,
                    "kernels": dsa.kernel_choice(prob)},
-        "hbm_gbps_e2e": e2e_gbps, "hbm_frac_e2e": e2e_gbps / HBM_PEAK_GBPS,
+        "hbm_gbps_e2e": e2e_gbps, "hbm_frac_e2e": e2e_gbps / HBM_PEAK_GBPS, "host_us_per_step": host_us,
         "algorithmic_bytes_per_step": ab["total"],
         "stages_us": {"scores": stage_ms[0] * 1e3, "topk": stage_ms[1] * 1e3, "attention": stage_ms[2] * 1e3},
         "roofline": {"kernel": "score_mfma_kernel", "bound": "hbm", "achieved": score_gbps,

@@ -16,9 +16,10 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers to dense, row-major arrays in the
  *    shapes given per argument.  The caller owns every buffer; the library
- *    allocates nothing, keeps no pointer after a call returns, and never
- *    synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
- *    null stream) and completes asynchronously.
+ *    allocates nothing (its one buffer, the fixed workspace of
+ *    dsa_forward_noalloc, is a static device array), keeps no pointer after a
+ *    call returns, and never synchronises: work is enqueued on `stream` (a
+ *    hipStream_t; NULL is the null stream) and completes asynchronously.
  *  - Validation first: every scalar and pointer argument is checked before any
  *    HIP call.  A non-DSA_OK return enqueues nothing; dsa_last_error() then
  *    describes the problem (thread-local string).
@@ -130,7 +131,7 @@ typedef struct dsa_problem {
   int32_t out_dtype;    /* DSA_F32 | DSA_BF16 */
 } dsa_problem;
 
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 #define DSA_FORWARD_STAGES 3 /* indexer scores, Top-K, sparse attention */
 
 int dsa_abi_version(void);
@@ -252,6 +253,30 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
                        int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
                        size_t ws_bytes, struct ihipStream_t* stream,
                        struct ihipEvent_t* const* stage_events);
+
+/*
+ * dsa_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a device array the library owns, DSA_NOALLOC_WORKSPACE_BYTES
+ * on each GPU it runs on, held until the process ends.  Arguments, outputs
+ * and stage events are those of dsa_forward without ws / ws_bytes.
+ *  - A problem whose dsa_forward_workspace_size exceeds
+ *    DSA_NOALLOC_WORKSPACE_BYTES returns DSA_ERR_WORKSPACE_TOO_SMALL (nothing
+ *    is enqueued); every argument is validated before any HIP call.
+ *  - No hipMalloc, hipFree or allocating library call is made.  The first
+ *    call on a device looks up that device's array address once.
+ *  - The array keeps the last call's contents; each call first clears the
+ *    counters it needs with a fill kernel on `stream`.  Every call on one GPU
+ *    shares that GPU's array, so calls that overlap on one GPU (on two
+ *    streams, or from two threads) race: serialise them.
+ */
+#define DSA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+dsa_status dsa_forward_noalloc(const dsa_problem* p, const void* q_idx, const float* head_w,
+                               const void* k_idx, const void* k_scale, const void* q, const void* kv,
+                               const float* kv_scale, const int32_t* seq_lens, float* scores,
+                               int32_t* topk_idx, int32_t* topk_count, void* out, float* lse,
+                               struct ihipStream_t* stream, struct ihipEvent_t* const* stage_events);
 
 /*
  * Paged caches.  The pages have the fused indexer read the paged key cache

@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
   dsa_topk(scores, seq_lens, top_k, q_len)                             -> (idx, count)
   dsa_sparse_mla_decode(q, kv, topk_idx, seq_lens, v_dim, ...)         -> (out, lse)
   dsa_forward(q_idx, head_w, k_idx, q, kv, seq_lens, top_k, v_dim, ...) -> dict
+  dsa_forward_noalloc(...)  dsa_forward with the library's own device
+                            workspace (for callers that cannot allocate)
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_MXFP8_E4M3, DSA_FP8_E4M3_T128 = 0, 1, 2, 3, 4
 FORWARD_STAGES = 3
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # DSA_NOALLOC_WORKSPACE_BYTES
 _STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
            3: "DSA_ERR_WORKSPACE_TOO_SMALL", 4: "DSA_ERR_HIP"}
 
@@ -95,9 +98,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_index_score_paged.argtypes = [PP, PG, P, P, P, P, P, P, P]
     lib.dsa_sparse_mla_decode_paged.argtypes = [PP, PG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.dsa_forward_paged.argtypes = [PP, PG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
+    lib.dsa_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     for f in (lib.dsa_index_score, lib.dsa_topk, lib.dsa_sparse_mla_decode, lib.dsa_forward,
               lib.dsa_kernel_choice, lib.dsa_index_score_paged, lib.dsa_sparse_mla_decode_paged,
-              lib.dsa_forward_paged):
+              lib.dsa_forward_paged, lib.dsa_forward_noalloc):
         f.restype = ctypes.c_int
     for f in (lib.dsa_topk_workspace_size, lib.dsa_sparse_mla_workspace_size,
               lib.dsa_forward_workspace_size, lib.dsa_workspace_zero_bytes):
@@ -498,4 +502,26 @@ def dsa_forward(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor, 
                            _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(seq_lens), _ptr(o.get("scores")),
                            _ptr(o["topk_idx"]), _ptr(o["topk_count"]), _ptr(o["out"]),
                            _ptr(o.get("lse")), _ptr(ws), _nbytes(ws), _stream(stream), _events(stage_events)))
+    return o
+
+
+def dsa_forward_noalloc(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor, q: torch.Tensor,
+                        kv: torch.Tensor, seq_lens: torch.Tensor, top_k: int, v_dim: int,
+                        softmax_scale: Optional[float] = None, k_scale: Optional[torch.Tensor] = None,
+                        kv_scale: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                        return_scores: bool = False, return_lse: bool = True, out: Optional[dict] = None,
+                        stage_events: Optional[Sequence] = None, stream=None) -> dict:
+    """dsa_forward with the workspace the library keeps on each GPU (no
+    workspace argument, no device allocation by the library).  Every output
+    must be preallocated in ``out`` for a call that may allocate nothing at
+    all; missing outputs are allocated here with torch.  Calls that overlap on
+    one GPU race on that workspace."""
+    lib = load_library()
+    p = forward_problem(q_idx, k_idx, q, kv, seq_lens, top_k, v_dim, softmax_scale, out_dtype, k_scale,
+                        kv_scale, head_w=head_w)
+    o = _forward_outputs(p, q.device, top_k, v_dim, return_scores, return_lse, out)
+    _check(lib.dsa_forward_noalloc(ctypes.byref(p), _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _ptr(k_scale),
+                                   _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(seq_lens), _ptr(o.get("scores")),
+                                   _ptr(o["topk_idx"]), _ptr(o["topk_count"]), _ptr(o["out"]),
+                                   _ptr(o.get("lse")), _stream(stream), _events(stage_events)))
     return o

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "dsa_api.cpp"]
+SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "noalloc_ws.hip", "dsa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -514,11 +514,17 @@ size_t dsa_forward_workspace_size(const dsa_problem* p) {
   return (size_t)fwd_layout(p).bytes;
 }
 
+// kValidate checks every argument but the workspace and enqueues nothing;
+// kRunClearing zeroes the workspace's counters (a fill kernel) before the
+// path runs, for a workspace whose contents are not known.
+enum class FwdMode { kRun, kValidate, kRunClearing };
+
 static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
                                const float* head_w, const void* k_idx, const void* k_scale, const void* q,
                                const void* kv, const float* kv_scale, const int32_t* seq_lens, float* scores,
                                int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
-                               size_t ws_bytes, hipStream_t stream, struct ihipEvent_t* const* stage_events) {
+                               size_t ws_bytes, hipStream_t stream, struct ihipEvent_t* const* stage_events,
+                               FwdMode mode = FwdMode::kRun) {
   dsa_status st = validate_problem(p);
   if (st != DSA_OK) return st;
   if ((st = check_index_inputs(p, q_idx, head_w, k_idx, k_scale, seq_lens)) != DSA_OK) return st;
@@ -531,6 +537,7 @@ static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const
     for (int i = 0; i <= DSA_FORWARD_STAGES; ++i)
       REQUIRE(stage_events[i], "stage_events[%d] is NULL", i);
   const FwdLayout F = fwd_layout(p);
+  if (mode == FwdMode::kValidate) return ok();
   if ((int64_t)ws_bytes < F.bytes)
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_forward needs %lld workspace bytes, got %zu",
                 (long long)F.bytes, ws_bytes);
@@ -538,6 +545,10 @@ static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const
 
   uint8_t* w = (uint8_t*)ws;
   hipStream_t s = stream;
+  if (mode == FwdMode::kRunClearing &&
+      (st = hip_check(dsa::launch_zero_u32((uint32_t*)(w + F.off_topk + F.tk.off_hist), F.tk.zero_bytes / 4, s),
+                      "workspace counters")) != DSA_OK)
+    return st;
   float* sc = scores ? scores : (float*)(w + F.off_scores);
   int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + F.off_idx);
   uint32_t* hist = (uint32_t*)(w + F.off_topk + F.tk.off_hist);
@@ -586,6 +597,28 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
                        struct ihipEvent_t* const* stage_events) {
   return forward_impl(p, nullptr, q_idx, head_w, k_idx, k_scale, q, kv, kv_scale, seq_lens, scores, topk_idx,
                       topk_count, out, lse, ws, ws_bytes, stream, stage_events);
+}
+
+dsa_status dsa_forward_noalloc(const dsa_problem* p, const void* q_idx, const float* head_w,
+                               const void* k_idx, const void* k_scale, const void* q, const void* kv,
+                               const float* kv_scale, const int32_t* seq_lens, float* scores,
+                               int32_t* topk_idx, int32_t* topk_count, void* out, float* lse,
+                               struct ihipStream_t* stream, struct ihipEvent_t* const* stage_events) {
+  // every argument first (no HIP call before this), then the size bound
+  dsa_status st = forward_impl(p, nullptr, q_idx, head_w, k_idx, k_scale, q, kv, kv_scale, seq_lens, scores,
+                               topk_idx, topk_count, out, lse, nullptr, 0, stream, stage_events, FwdMode::kValidate);
+  if (st != DSA_OK) return st;
+  const int64_t need = fwd_layout(p).bytes;
+  if (need > (int64_t)DSA_NOALLOC_WORKSPACE_BYTES)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
+                "dsa_forward_noalloc: this problem needs %lld workspace bytes, more than the %zu the library "
+                "holds per GPU; use dsa_forward with a workspace of dsa_forward_workspace_size(p) bytes",
+                (long long)need, (size_t)DSA_NOALLOC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if ((st = hip_check(dsa::noalloc_workspace(&ws, &ws_bytes), "library workspace lookup")) != DSA_OK) return st;
+  return forward_impl(p, nullptr, q_idx, head_w, k_idx, k_scale, q, kv, kv_scale, seq_lens, scores, topk_idx,
+                      topk_count, out, lse, ws, ws_bytes, stream, stage_events, FwdMode::kRunClearing);
 }
 
 dsa_status dsa_forward_paged(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,

@@ -78,6 +78,10 @@ hipError_t launch_hist(const float* scores, const int32_t* seq_lens, uint32_t* h
                        int64_t Lmax, hipStream_t stream);
 hipError_t launch_select(const TopkParams& p, hipStream_t stream);
 
+// noalloc_ws.hip: the device address (on the current device) and size of
+// the library-owned workspace of dsa_forward_noalloc.
+hipError_t noalloc_workspace(void** ptr, size_t* bytes);
+
 // sparse_mla.hip
 bool mla_mfma_supported(const MlaParams& p);
 int mla_row_tile();

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = dsa.load_library()
-    assert lib.dsa_abi_version() == 4
+    assert lib.dsa_abi_version() == 5
     assert lib.dsa_status_string(0) == b"DSA_OK"
     assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
 
@@ -363,3 +363,21 @@ def test_binding_checks_paged_inputs():
         kw = dict(base, **pages)
         kw.update(change)
         _expect_dsa_error(dsa.dsa_forward_paged, match=match, **kw)
+
+
+def test_noalloc_checks_arguments_and_size_before_any_hip_call():
+    lib = dsa.load_library()
+    f = FAKE
+    # an invalid problem and a NULL pointer: rejected as for dsa_forward
+    p = good_problem(top_k=0)
+    assert lib.dsa_forward_noalloc(ctypes.byref(p), f, f, f, None, f, f, None, f, None, None, None, f, f,
+                                   None, None) == 1
+    p = good_problem()
+    assert lib.dsa_forward_noalloc(ctypes.byref(p), None, f, f, None, f, f, None, f, None, None, None, f, f,
+                                   None, None) == 1
+    # a problem whose workspace exceeds the library's fixed one: a clear error
+    big = good_problem(batch=8, q_len=2, max_seq_len=1 << 20)
+    assert lib.dsa_forward_workspace_size(ctypes.byref(big)) > dsa.NOALLOC_WORKSPACE_BYTES
+    assert lib.dsa_forward_noalloc(ctypes.byref(big), f, f, f, None, f, f, None, f, None, None, None, f, f,
+                                   None, None) == 3
+    assert b"dsa_forward_noalloc" in lib.dsa_last_error() and b"workspace" in lib.dsa_last_error()
