@@ -10,6 +10,8 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <tuple>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "kernels.hpp"
@@ -381,6 +383,26 @@ bool score_uses_mfma(const dsa_problem* p) {
 }
 
 }  // namespace
+
+namespace dsa {
+
+// hipFuncSetAttribute costs a runtime call per launch; it is made once per
+// kernel and device instead.
+hipError_t set_max_dynamic_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::tuple<const void*, int, int>> done;  // (kernel, device, bytes)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(mu);
+  for (const auto& d : done)
+    if (std::get<0>(d) == kernel && std::get<1>(d) == dev && std::get<2>(d) >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(kernel, dev, bytes);
+  return e;
+}
+
+}  // namespace dsa
 
 extern "C" {
 

@@ -65,6 +65,9 @@ struct MlaParams {
   int max_pages, page_shift;
 };
 
+// Raises a kernel's dynamic LDS limit to `bytes` (once per kernel and device).
+hipError_t set_max_dynamic_lds(const void* kernel, int bytes);
+
 // index_score.hip
 bool score_mfma_supported(const ScoreParams& p);
 // With the matrix-core kernel, ev_start / ev_stop (either may be null) are

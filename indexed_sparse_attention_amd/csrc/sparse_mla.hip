@@ -949,19 +949,16 @@ hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream) {
     const size_t lds = sizeof(MlaShared);
     hipError_t e;
     if (p.kv_dtype == kBF16) {
-      e = hipFuncSetAttribute((const void*)mla_mfma_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+      e = set_max_dynamic_lds((const void*)mla_mfma_kernel<false>, (int)lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kMlaThreads), lds, stream, p);
     } else if (p.kv_dtype == kE4M3) {
-      e = hipFuncSetAttribute((const void*)mla_mfma_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+      e = set_max_dynamic_lds((const void*)mla_mfma_kernel<true>, (int)lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(mla_mfma_kernel<true>, grid, dim3(kMlaThreads), lds, stream, p);
     } else {  // one scale per 128-column tile: ceil(576 / 128) per row
       constexpr int kTiles = (kDqk + 127) / 128;
-      e = hipFuncSetAttribute((const void*)mla_mfma_kernel<true, kTiles>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+      e = set_max_dynamic_lds((const void*)mla_mfma_kernel<true, kTiles>, (int)lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((mla_mfma_kernel<true, kTiles>), grid, dim3(kMlaThreads), lds, stream, p);
     }

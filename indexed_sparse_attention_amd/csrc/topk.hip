@@ -513,8 +513,7 @@ hipError_t launch_select(const TopkParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(select_chunk_kernel<false>, grid, dim3(kSelThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)select_emit_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)sizeof(EmitShared));
+  e = set_max_dynamic_lds((const void*)select_emit_kernel, (int)sizeof(EmitShared));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kSelThreads), sizeof(EmitShared), stream, p);
   return hipGetLastError();
