@@ -51,7 +51,22 @@
  *    equals +0.  NaN scores are not supported.
  *  - Attention logits and values are accumulated in fp32 (bf16 matrix-core
  *    products for bf16/fp8 caches), softmax uses the running-max (online)
- *    form, outputs are rounded to nearest even when out_dtype is bf16.
+ *    form, outputs are rounded to nearest even when out_dtype is bf16.  When
+ *    the matrix-core attention splits a query's index list over several
+ *    workgroups (the library's choice, for parallelism), each split's
+ *    normalised output is rounded to bf16 before the fp32 merge, so an fp32
+ *    out_dtype there still carries one bf16 rounding (relative 2^-9) per
+ *    split; the portable kernels keep fp32 throughout.
+ *
+ * Workspaces
+ * ----------
+ *  A call whose scratch would pass 1 GiB (a long prefill chunk, a very large
+ *  batch) runs as a series of launches over tiles of one sequence's query
+ *  tokens, each token seeing exactly what it sees in the whole problem; the
+ *  *_workspace_size functions then return one tile's scratch, which the
+ *  tiles reuse in turn on `stream`.  The results are those of the whole
+ *  call.  (A 4096-token chunk over 64K cached rows needs 653 MiB for
+ *  dsa_forward instead of 5.1 GiB.)
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -245,7 +260,9 @@ size_t dsa_forward_workspace_size(const dsa_problem* p);
  *                stage i (1 = scores, 2 = Top-K, 3 = attention), for per-stage
  *                timing.  With the matrix-core score kernel, events 0 and 1
  *                are taken by that kernel's dispatch at its own start and end,
- *                so they time the kernel alone.
+ *                so they time the kernel alone.  A call that runs in token
+ *                tiles (see Workspaces) records event 0 before its first
+ *                tile and events 1 .. 3 after its last.
  */
 dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
                        const void* k_idx, const void* k_scale, const void* q, const void* kv,

@@ -108,4 +108,13 @@ __device__ __forceinline__ int clamp_len(int32_t len, int64_t lmax) {
   return (int)(l > lmax ? lmax : l);
 }
 
+// Rows a launch treats as filled: seq_lens[b] clamped to [0, Lmax], less
+// `sub` rows (a launch over a tile of a sequence's query tokens that ends
+// `sub` tokens before the last one sees exactly as those tokens do), never
+// below 0.
+__device__ __forceinline__ int filled_rows(int32_t len, int64_t lmax, int sub) {
+  const int l = clamp_len(len, lmax) - sub;
+  return l > 0 ? l : 0;
+}
+
 }  // namespace dsa

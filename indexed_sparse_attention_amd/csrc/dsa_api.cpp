@@ -186,6 +186,71 @@ FwdLayout fwd_layout(const dsa_problem* p) {
   return F;
 }
 
+// ------------------------------------------------------------------ token tiles
+// A call whose workspace would pass 1 GiB runs as a series of launches
+// over tiles of one sequence's query tokens (a long prefill chunk, or a very
+// large batch): tile (b, t0, n) is the problem of sequence b alone with
+// query tokens t0 .. t0+n-1, its pointers offset to them, and `len_sub` =
+// T - t0 - n rows hidden from its score and Top-K kernels, so that every
+// token sees exactly what it sees in the whole problem.  The workspace then
+// holds one tile's scratch, reused tile after tile on the one stream.
+// (DSA_TILE_BUDGET, in bytes, replaces it: tests use it to make small
+// problems run in tiles)
+int64_t tile_budget() {
+  const char* e = getenv("DSA_TILE_BUDGET");
+  if (e && *e) {
+    const long long v = atoll(e);
+    if (v > 0) return (int64_t)v;
+  }
+  return (int64_t)1 << 30;
+}
+
+dsa_problem tile_problem(const dsa_problem* p, int n) {
+  dsa_problem t = *p;
+  t.batch = 1;
+  t.q_len = n;
+  return t;
+}
+
+// query tokens per tile (0: the call runs whole), the largest power of two
+// whose tile scratch fits the budget
+template <class Bytes>
+int tile_tokens(const dsa_problem* p, Bytes bytes) {
+  const int64_t budget = tile_budget();
+  if (bytes(p) <= budget) return 0;
+  int n = 1;
+  while (2 * (int64_t)n <= p->q_len) n *= 2;
+  while (n > 1) {
+    const dsa_problem t = tile_problem(p, n);
+    if (bytes(&t) <= budget) break;
+    n /= 2;
+  }
+  return n;
+}
+
+int64_t elem_bytes(int32_t dtype) { return dtype == DSA_F32 ? 4 : dtype == DSA_BF16 ? 2 : 1; }
+int64_t key_row_bytes(const dsa_problem* p) { return (int64_t)p->idx_dim * elem_bytes(p->idx_key_dtype); }
+int64_t key_scale_row_bytes(const dsa_problem* p) {
+  if (p->idx_key_dtype == DSA_FP8_E4M3) return 4;
+  if (p->idx_key_dtype == DSA_MXFP8_E4M3) return (p->idx_dim + 31) / 32;
+  return 0;
+}
+int64_t kv_row_bytes(const dsa_problem* p) { return (int64_t)p->qk_dim * elem_bytes(p->kv_dtype); }
+int64_t kv_scale_row_bytes(const dsa_problem* p) {
+  if (p->kv_dtype == DSA_FP8_E4M3) return 4;
+  if (p->kv_dtype == DSA_FP8_E4M3_T128) return 4 * (int64_t)((p->qk_dim + 127) / 128);
+  return 0;
+}
+
+template <class T>
+T* advance(T* ptr, int64_t bytes) {
+  return ptr ? (T*)((const uint8_t*)ptr + bytes) : nullptr;
+}
+
+int64_t topk_bytes(const dsa_problem* p) { return topk_layout(p).bytes; }
+int64_t mla_bytes(const dsa_problem* p) { return mla_layout(p).bytes; }
+int64_t fwd_bytes(const dsa_problem* p) { return fwd_layout(p).bytes; }
+
 int num_cus() {
   static std::mutex mu;
   static int cache[64] = {0};
@@ -245,8 +310,9 @@ dsa_status check_mla_inputs(const dsa_problem* p, const void* q, const void* kv,
 
 dsa::ScoreParams score_params(const dsa_problem* p, const void* q_idx, const float* head_w,
                               const void* k_idx, const void* k_scale, const int32_t* seq_lens,
-                              float* scores, uint32_t* hist) {
+                              float* scores, uint32_t* hist, int len_sub = 0) {
   dsa::ScoreParams s;
+  s.len_sub = len_sub;
   s.q_idx = q_idx;
   s.head_w = head_w;
   s.k_idx = k_idx;
@@ -269,8 +335,9 @@ dsa::ScoreParams score_params(const dsa_problem* p, const void* q_idx, const flo
 }
 
 dsa::TopkParams topk_params(const dsa_problem* p, const TopkLayout& L, uint8_t* ws, const float* scores,
-                            const int32_t* seq_lens, int32_t* idx, int32_t* cnt) {
+                            const int32_t* seq_lens, int32_t* idx, int32_t* cnt, int len_sub = 0) {
   dsa::TopkParams t;
+  t.len_sub = len_sub;
   t.scores = scores;
   t.seq_lens = seq_lens;
   t.hist = (uint32_t*)(ws + L.off_hist);
@@ -294,6 +361,7 @@ dsa::MlaParams mla_params(const dsa_problem* p, const MlaLayout& L, uint8_t* ws,
                           const void* kv, const float* kv_scale, const int32_t* idx,
                           const int32_t* seq_lens, void* out, float* lse) {
   dsa::MlaParams m;
+  m.len_sub = 0;  // (the attention's length only bounds the index entries it accepts)
   m.q = q;
   m.kv = kv;
   m.kv_scale = kv_scale;
@@ -449,9 +517,27 @@ dsa_status dsa_index_score_paged(const dsa_problem* p, const dsa_paging* pg, con
   return index_score_impl(p, pg, q_idx, head_w, k_pages, k_scales, seq_lens, scores, stream);
 }
 
+static int64_t topk_ws_bytes(const dsa_problem* p) {
+  const int n = tile_tokens(p, topk_bytes);
+  if (!n) return topk_layout(p).bytes;
+  const dsa_problem t = tile_problem(p, n);
+  return topk_layout(&t).bytes;
+}
+
 size_t dsa_topk_workspace_size(const dsa_problem* p) {
   if (validate_problem(p) != DSA_OK) return 0;
-  return (size_t)topk_layout(p).bytes;
+  return (size_t)topk_ws_bytes(p);
+}
+
+// One launch pair (histogram, select) over problem p.
+static dsa_status topk_run(const dsa_problem* p, const float* scores, const int32_t* seq_lens, int len_sub,
+                           int32_t* topk_idx, int32_t* topk_count, uint8_t* w, hipStream_t s) {
+  const TopkLayout L = topk_layout(p);
+  dsa_status st;
+  if ((st = hip_check(dsa::launch_hist(scores, seq_lens, len_sub, (uint32_t*)(w + L.off_hist), p->batch, p->q_len,
+                                       p->max_seq_len, s), "histogram")) != DSA_OK) return st;
+  auto tp = topk_params(p, L, w, scores, seq_lens, topk_idx, topk_count, len_sub);
+  return hip_check(dsa::launch_select(tp, s), "select");
 }
 
 dsa_status dsa_topk(const dsa_problem* p, const float* scores, const int32_t* seq_lens,
@@ -463,23 +549,40 @@ dsa_status dsa_topk(const dsa_problem* p, const float* scores, const int32_t* se
   REQUIRE(seq_lens && aligned(seq_lens, 4), "seq_lens must be non-NULL and 4-byte aligned");
   REQUIRE(topk_idx && aligned(topk_idx, 4), "topk_idx must be non-NULL and 4-byte aligned");
   REQUIRE(!topk_count || aligned(topk_count, 4), "topk_count must be 4-byte aligned");
-  const TopkLayout L = topk_layout(p);
-  if ((int64_t)ws_bytes < L.bytes)
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_topk needs %lld workspace bytes, got %zu",
-                (long long)L.bytes, ws_bytes);
+  const int64_t need = topk_ws_bytes(p);
+  if ((int64_t)ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_topk needs %lld workspace bytes, got %zu", (long long)need,
+                ws_bytes);
   REQUIRE(ws && aligned(ws, 16), "ws must be non-NULL and 16-byte aligned");
   uint8_t* w = (uint8_t*)ws;
-  hipStream_t s = stream;
-  if ((st = hip_check(dsa::launch_hist(scores, seq_lens, (uint32_t*)(w + L.off_hist), p->batch, p->q_len,
-                                       p->max_seq_len, s), "histogram")) != DSA_OK) return st;
-  auto tp = topk_params(p, L, w, scores, seq_lens, topk_idx, topk_count);
-  if ((st = hip_check(dsa::launch_select(tp, s), "select")) != DSA_OK) return st;
+  const int n = tile_tokens(p, topk_bytes);
+  if (!n) {
+    if ((st = topk_run(p, scores, seq_lens, 0, topk_idx, topk_count, w, stream)) != DSA_OK) return st;
+    return ok();
+  }
+  const int T = p->q_len;
+  for (int b = 0; b < p->batch; ++b)
+    for (int t0 = 0; t0 < T; t0 += n) {
+      const int nn = std::min(n, T - t0);
+      const dsa_problem t = tile_problem(p, nn);
+      const int64_t q0 = (int64_t)b * T + t0;  // first query of the tile
+      if ((st = topk_run(&t, scores + q0 * p->max_seq_len, seq_lens + b, T - t0 - nn, topk_idx + q0 * p->top_k,
+                         topk_count ? topk_count + q0 : nullptr, w, stream)) != DSA_OK)
+        return st;
+    }
   return ok();
 }
 
 size_t dsa_workspace_zero_bytes(const dsa_problem* p) {
   if (validate_problem(p) != DSA_OK) return 0;
-  return (size_t)topk_layout(p).zero_bytes;  // the counters sit at offset 0 of both workspaces
+  // the counters sit at offset 0 of both workspaces, sized for the problem
+  // (or the token tile) each one lays out
+  int64_t z = 0;
+  for (int n : {tile_tokens(p, topk_bytes), tile_tokens(p, fwd_bytes)}) {
+    const dsa_problem t = n ? tile_problem(p, n) : *p;
+    z = std::max<int64_t>(z, topk_layout(&t).zero_bytes);
+  }
+  return (size_t)z;
 }
 
 dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, struct ihipStream_t* stream) {
@@ -492,9 +595,23 @@ dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, struct ihipStream_t* st
   return ok();
 }
 
+static int64_t mla_ws_bytes(const dsa_problem* p) {
+  const int n = tile_tokens(p, mla_bytes);
+  if (!n) return mla_layout(p).bytes;
+  const dsa_problem t = tile_problem(p, n);
+  return mla_layout(&t).bytes;
+}
+
 size_t dsa_sparse_mla_workspace_size(const dsa_problem* p) {
   if (validate_problem(p) != DSA_OK) return 0;
-  return (size_t)mla_layout(p).bytes;
+  return (size_t)mla_ws_bytes(p);
+}
+
+// A tile's view of the paging descriptor: its sequence's row of the table.
+static dsa_paging tile_paging(const dsa_paging* pg, int b) {
+  dsa_paging t = *pg;
+  t.block_table = pg->block_table + (int64_t)b * pg->max_pages;
+  return t;
 }
 
 static dsa_status sparse_mla_impl(const dsa_problem* p, const dsa_paging* pg, const void* q, const void* kv,
@@ -505,14 +622,38 @@ static dsa_status sparse_mla_impl(const dsa_problem* p, const dsa_paging* pg, co
   if ((st = check_mla_inputs(p, q, kv, kv_scale, seq_lens, out, lse)) != DSA_OK) return st;
   if (pg && (st = check_paging(p, pg, false, true)) != DSA_OK) return st;
   REQUIRE(topk_idx && aligned(topk_idx, 4), "topk_idx must be non-NULL and 4-byte aligned");
-  const MlaLayout L = mla_layout(p);
-  if ((int64_t)ws_bytes < L.bytes)
+  const int64_t need = mla_ws_bytes(p);
+  if ((int64_t)ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_sparse_mla_decode needs %lld workspace bytes, got %zu",
-                (long long)L.bytes, ws_bytes);
-  REQUIRE(L.bytes == 0 || (ws && aligned(ws, 16)), "ws must be non-NULL and 16-byte aligned");
-  auto mp = mla_params(p, L, (uint8_t*)ws, q, kv, kv_scale, topk_idx, seq_lens, out, lse);
-  apply_paging(mp, pg);
-  if ((st = hip_check(dsa::launch_mla(mp, mla_uses_mfma(p), stream), "sparse attention")) != DSA_OK) return st;
+                (long long)need, ws_bytes);
+  REQUIRE(need == 0 || (ws && aligned(ws, 16)), "ws must be non-NULL and 16-byte aligned");
+  auto run = [&](const dsa_problem* t, const dsa_paging* tpg, const void* tq, const void* tkv, const float* tks,
+                 const int32_t* tidx, const int32_t* tlens, void* tout, float* tlse) -> dsa_status {
+    auto mp = mla_params(t, mla_layout(t), (uint8_t*)ws, tq, tkv, tks, tidx, tlens, tout, tlse);
+    apply_paging(mp, tpg);
+    return hip_check(dsa::launch_mla(mp, mla_uses_mfma(t), stream), "sparse attention");
+  };
+  const int n = tile_tokens(p, mla_bytes);
+  if (!n) {
+    if ((st = run(p, pg, q, kv, kv_scale, topk_idx, seq_lens, out, lse)) != DSA_OK) return st;
+    return ok();
+  }
+  const int T = p->q_len;
+  for (int b = 0; b < p->batch; ++b) {
+    const dsa_paging tpg = pg ? tile_paging(pg, b) : dsa_paging{};
+    const int64_t row0 = pg ? 0 : (int64_t)b * p->max_seq_len;  // first cache row of sequence b
+    for (int t0 = 0; t0 < T; t0 += n) {
+      const int nn = std::min(n, T - t0);
+      const dsa_problem t = tile_problem(p, nn);
+      const int64_t q0 = (int64_t)b * T + t0;
+      if ((st = run(&t, pg ? &tpg : nullptr, advance(q, q0 * p->heads * p->qk_dim * elem_bytes(p->q_dtype)),
+                    advance(kv, row0 * kv_row_bytes(p)), advance(kv_scale, row0 * kv_scale_row_bytes(p)),
+                    topk_idx + q0 * p->top_k, seq_lens + b,
+                    advance(out, q0 * p->heads * p->v_dim * elem_bytes(p->out_dtype)),
+                    lse ? lse + q0 * p->heads : nullptr)) != DSA_OK)
+        return st;
+    }
+  }
   return ok();
 }
 
@@ -531,15 +672,71 @@ dsa_status dsa_sparse_mla_decode_paged(const dsa_problem* p, const dsa_paging* p
   return sparse_mla_impl(p, pg, q, kv_pages, kv_scales, topk_idx, seq_lens, out, lse, ws, ws_bytes, stream);
 }
 
+static int64_t fwd_ws_bytes(const dsa_problem* p) {
+  const int n = tile_tokens(p, fwd_bytes);
+  if (!n) return fwd_layout(p).bytes;
+  const dsa_problem t = tile_problem(p, n);
+  return fwd_layout(&t).bytes;
+}
+
 size_t dsa_forward_workspace_size(const dsa_problem* p) {
   if (validate_problem(p) != DSA_OK) return 0;
-  return (size_t)fwd_layout(p).bytes;
+  return (size_t)fwd_ws_bytes(p);
 }
 
 // kValidate checks every argument but the workspace and enqueues nothing;
 // kRunClearing zeroes the workspace's counters (a fill kernel) before the
 // path runs, for a workspace whose contents are not known.
 enum class FwdMode { kRun, kValidate, kRunClearing };
+
+// The three stages over problem p (a whole problem or one token tile) in
+// the workspace laid out for it.  With stage_events, event 0 goes before the
+// scores and event i after stage i.
+static dsa_status forward_run(const dsa_problem* p, const dsa_paging* pg, const void* q_idx, const float* head_w,
+                              const void* k_idx, const void* k_scale, const void* q, const void* kv,
+                              const float* kv_scale, const int32_t* seq_lens, int len_sub, float* scores,
+                              int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, uint8_t* w,
+                              hipStream_t s, struct ihipEvent_t* const* stage_events) {
+  dsa_status st;
+  const FwdLayout F = fwd_layout(p);
+  float* sc = scores ? scores : (float*)(w + F.off_scores);
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + F.off_idx);
+  uint32_t* hist = (uint32_t*)(w + F.off_topk + F.tk.off_hist);
+  auto rec = [&](int i) -> dsa_status {
+    if (!stage_events) return DSA_OK;
+    return hip_check(hipEventRecord((hipEvent_t)stage_events[i], s), "event record");
+  };
+
+  // the counters at the start of the workspace are zero on entry (and on return)
+  // stage 1: scores (+ fused histogram when the matrix-core kernel runs, whose
+  // dispatch then takes events 0 and 1 at the kernel's own start and end)
+  const bool mfma_score = score_uses_mfma(p);
+  auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, sc, hist, len_sub);
+  apply_paging(sp, pg);
+  if (!mfma_score) {
+    sp.hist = nullptr;
+    if ((st = rec(0)) != DSA_OK) return st;
+  }
+  hipEvent_t ev0 = mfma_score && stage_events ? (hipEvent_t)stage_events[0] : nullptr;
+  hipEvent_t ev1 = mfma_score && stage_events ? (hipEvent_t)stage_events[1] : nullptr;
+  if ((st = hip_check(dsa::launch_score(sp, mfma_score, num_cus(), s, ev0, ev1), "index score")) != DSA_OK)
+    return st;
+  if (!mfma_score) {
+    if ((st = hip_check(dsa::launch_hist(sc, seq_lens, len_sub, hist, p->batch, p->q_len, p->max_seq_len, s),
+                        "histogram")) != DSA_OK)
+      return st;
+    if ((st = rec(1)) != DSA_OK) return st;
+  }
+  // stage 2: Top-K
+  auto tp = topk_params(p, F.tk, w + F.off_topk, sc, seq_lens, idx, topk_count, len_sub);
+  if ((st = hip_check(dsa::launch_select(tp, s), "select")) != DSA_OK) return st;
+  if ((st = rec(2)) != DSA_OK) return st;
+  // stage 3: sparse MLA attention
+  auto mp = mla_params(p, F.mla, w + F.off_mla, q, kv, kv_scale, idx, seq_lens, out, lse);
+  apply_paging(mp, pg);
+  if ((st = hip_check(dsa::launch_mla(mp, mla_uses_mfma(p), s), "sparse attention")) != DSA_OK) return st;
+  return rec(3);
+}
 
 static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const void* q_idx,
                                const float* head_w, const void* k_idx, const void* k_scale, const void* q,
@@ -558,56 +755,59 @@ static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const
   if (stage_events)
     for (int i = 0; i <= DSA_FORWARD_STAGES; ++i)
       REQUIRE(stage_events[i], "stage_events[%d] is NULL", i);
-  const FwdLayout F = fwd_layout(p);
   if (mode == FwdMode::kValidate) return ok();
-  if ((int64_t)ws_bytes < F.bytes)
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_forward needs %lld workspace bytes, got %zu",
-                (long long)F.bytes, ws_bytes);
+  const int64_t need = fwd_ws_bytes(p);
+  if ((int64_t)ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_forward needs %lld workspace bytes, got %zu", (long long)need,
+                ws_bytes);
   REQUIRE(ws && aligned(ws, 256), "ws must be non-NULL and 256-byte aligned");
 
   uint8_t* w = (uint8_t*)ws;
   hipStream_t s = stream;
-  if (mode == FwdMode::kRunClearing &&
-      (st = hip_check(dsa::launch_zero_u32((uint32_t*)(w + F.off_topk + F.tk.off_hist), F.tk.zero_bytes / 4, s),
-                      "workspace counters")) != DSA_OK)
-    return st;
-  float* sc = scores ? scores : (float*)(w + F.off_scores);
-  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + F.off_idx);
-  uint32_t* hist = (uint32_t*)(w + F.off_topk + F.tk.off_hist);
+  const int n = tile_tokens(p, fwd_bytes);
+  if (mode == FwdMode::kRunClearing) {
+    const dsa_problem t = n ? tile_problem(p, n) : *p;
+    if ((st = hip_check(dsa::launch_zero_u32((uint32_t*)w, topk_layout(&t).zero_bytes / 4, s),
+                        "workspace counters")) != DSA_OK)
+      return st;
+  }
+  if (!n) {
+    if ((st = forward_run(p, pg, q_idx, head_w, k_idx, k_scale, q, kv, kv_scale, seq_lens, 0, scores, topk_idx,
+                          topk_count, out, lse, w, s, stage_events)) != DSA_OK)
+      return st;
+    return ok();
+  }
+  // token tiles: the events bracket the whole call (event 0 before the first
+  // tile, events 1 .. 3 after the last)
   auto rec = [&](int i) -> dsa_status {
     if (!stage_events) return DSA_OK;
     return hip_check(hipEventRecord((hipEvent_t)stage_events[i], s), "event record");
   };
-
-  // the counters at the start of the workspace are zero on entry (and on return)
-  // stage 1: scores (+ fused histogram when the matrix-core kernel runs, whose
-  // dispatch then takes events 0 and 1 at the kernel's own start and end)
-  const bool mfma_score = score_uses_mfma(p);
-  auto sp = score_params(p, q_idx, head_w, k_idx, k_scale, seq_lens, sc, hist);
-  apply_paging(sp, pg);
-  if (!mfma_score) {
-    sp.hist = nullptr;
-    if ((st = rec(0)) != DSA_OK) return st;
+  if ((st = rec(0)) != DSA_OK) return st;
+  const int T = p->q_len;
+  const int64_t H = p->heads;
+  for (int b = 0; b < p->batch; ++b) {
+    const dsa_paging tpg = pg ? tile_paging(pg, b) : dsa_paging{};
+    const int64_t row0 = pg ? 0 : (int64_t)b * p->max_seq_len;  // first cache row of sequence b
+    for (int t0 = 0; t0 < T; t0 += n) {
+      const int nn = std::min(n, T - t0);
+      const dsa_problem t = tile_problem(p, nn);
+      const int64_t q0 = (int64_t)b * T + t0;  // first query of the tile
+      if ((st = forward_run(&t, pg ? &tpg : nullptr,
+                            advance(q_idx, q0 * p->idx_heads * p->idx_dim * elem_bytes(p->q_idx_dtype)),
+                            head_w + q0 * p->idx_heads, advance(k_idx, row0 * key_row_bytes(p)),
+                            advance(k_scale, row0 * key_scale_row_bytes(p)),
+                            advance(q, q0 * H * p->qk_dim * elem_bytes(p->q_dtype)),
+                            advance(kv, row0 * kv_row_bytes(p)), advance(kv_scale, row0 * kv_scale_row_bytes(p)),
+                            seq_lens + b, T - t0 - nn, scores ? scores + q0 * p->max_seq_len : nullptr,
+                            topk_idx ? topk_idx + q0 * p->top_k : nullptr, topk_count ? topk_count + q0 : nullptr,
+                            advance(out, q0 * H * p->v_dim * elem_bytes(p->out_dtype)), lse ? lse + q0 * H : nullptr,
+                            w, s, nullptr)) != DSA_OK)
+        return st;
+    }
   }
-  hipEvent_t ev0 = mfma_score && stage_events ? (hipEvent_t)stage_events[0] : nullptr;
-  hipEvent_t ev1 = mfma_score && stage_events ? (hipEvent_t)stage_events[1] : nullptr;
-  if ((st = hip_check(dsa::launch_score(sp, mfma_score, num_cus(), s, ev0, ev1), "index score")) != DSA_OK)
-    return st;
-  if (!mfma_score) {
-    if ((st = hip_check(dsa::launch_hist(sc, seq_lens, hist, p->batch, p->q_len, p->max_seq_len, s),
-                        "histogram")) != DSA_OK)
-      return st;
-    if ((st = rec(1)) != DSA_OK) return st;
-  }
-  // stage 2: Top-K
-  auto tp = topk_params(p, F.tk, w + F.off_topk, sc, seq_lens, idx, topk_count);
-  if ((st = hip_check(dsa::launch_select(tp, s), "select")) != DSA_OK) return st;
-  if ((st = rec(2)) != DSA_OK) return st;
-  // stage 3: sparse MLA attention
-  auto mp = mla_params(p, F.mla, w + F.off_mla, q, kv, kv_scale, idx, seq_lens, out, lse);
-  apply_paging(mp, pg);
-  if ((st = hip_check(dsa::launch_mla(mp, mla_uses_mfma(p), s), "sparse attention")) != DSA_OK) return st;
-  if ((st = rec(3)) != DSA_OK) return st;
+  for (int i = 1; i <= DSA_FORWARD_STAGES; ++i)
+    if ((st = rec(i)) != DSA_OK) return st;
   return ok();
 }
 
@@ -630,7 +830,7 @@ dsa_status dsa_forward_noalloc(const dsa_problem* p, const void* q_idx, const fl
   dsa_status st = forward_impl(p, nullptr, q_idx, head_w, k_idx, k_scale, q, kv, kv_scale, seq_lens, scores,
                                topk_idx, topk_count, out, lse, nullptr, 0, stream, stage_events, FwdMode::kValidate);
   if (st != DSA_OK) return st;
-  const int64_t need = fwd_layout(p).bytes;
+  const int64_t need = fwd_ws_bytes(p);
   if (need > (int64_t)DSA_NOALLOC_WORKSPACE_BYTES)
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
                 "dsa_forward_noalloc: this problem needs %lld workspace bytes, more than the %zu the library "

@@ -28,7 +28,7 @@ __device__ __forceinline__ float load_elem(const void* p, int dtype, int64_t i) 
 __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
   const int bt = blockIdx.y;
   const int b = bt / p.T, t = bt % p.T;
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const int len = filled_rows(p.seq_lens[b], p.Lmax, p.len_sub);
   const int64_t vis = (int64_t)len - p.T + 1 + t;
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= vis) return;
@@ -207,12 +207,12 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
     return vis_end > 0 ? (vis_end + 63) / 64 : 0;
   };
   auto seg_units = [&](int seg) -> int64_t {
-    return seg_units_len(seg, clamp_len(p.seq_lens[seg / n_groups], p.Lmax));
+    return seg_units_len(seg, filled_rows(p.seq_lens[seg / n_groups], p.Lmax, p.len_sub));
   };
 
   // Pass 1: total units.  Segment tid's length and units are kept for the
   // first chunk of pass 2, which then starts without another memory round trip.
-  const int len0 = tid < n_seg ? clamp_len(p.seq_lens[tid / n_groups], p.Lmax) : 0;
+  const int len0 = tid < n_seg ? filled_rows(p.seq_lens[tid / n_groups], p.Lmax, p.len_sub) : 0;
   const int64_t units0 = tid < n_seg ? seg_units_len(tid, len0) : 0;
   int64_t acc = units0;
   for (int s = tid + kScoreThreads; s < n_seg; s += kScoreThreads) acc += seg_units(s);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   for (int c0 = 0; c0 < n_seg && wg_first(chunk_base) <= wg; c0 += kScoreThreads) {
     const int n_here = min(kScoreThreads, n_seg - c0);
     const int64_t mine = tid < n_here ? (c0 == 0 ? units0 : seg_units(c0 + tid)) : 0;
-    if (tid < n_here) s_len[tid] = c0 == 0 ? len0 : clamp_len(p.seq_lens[(c0 + tid) / n_groups], p.Lmax);
+    if (tid < n_here) s_len[tid] = c0 == 0 ? len0 : filled_rows(p.seq_lens[(c0 + tid) / n_groups], p.Lmax, p.len_sub);
     int64_t v = mine;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {

@@ -12,6 +12,7 @@ struct ScoreParams {
   const void* k_idx;        // [B,Lmax,Di] k_dtype
   const void* k_scale;      // fp32 [B,Lmax] (e4m3), E8M0 bytes [B,Lmax,Di/32] (mxfp8) or null
   const int32_t* seq_lens;  // [B]
+  int len_sub;              // filled rows of sequence b: seq_lens[b] (clamped) - len_sub (see filled_rows)
   float* scores;            // [B,T,Lmax]
   uint32_t* hist;           // [B*T, 4096] (zeroed) or null
   int B, T, Hi, Di;
@@ -28,6 +29,7 @@ struct ScoreParams {
 struct TopkParams {
   const float* scores;      // [B,T,Lmax]
   const int32_t* seq_lens;  // [B]
+  int len_sub;              // as in ScoreParams
   uint32_t* hist;           // [B*T, 4096] score-key histograms (complete on entry; cleared after use)
   uint2* cand;              // [B*T, Lmax] per-chunk ordered (key, position) candidates (bin >= threshold bin)
   uint32_t* bin_keys;       // [B*T, Lmax rounded up to 4] per-chunk ordered keys in the threshold bin
@@ -48,6 +50,7 @@ struct MlaParams {
   const float* kv_scale;    // [B,Lmax] (e4m3), [B,Lmax,ceil(Dqk/128)] (e4m3, 128-column tiles) or null
   const int32_t* topk_idx;  // [B,T,K]
   const int32_t* seq_lens;  // [B]
+  int len_sub;              // as in ScoreParams
   void* out;                // [B,T,H,Dv]
   float* lse;               // [B,T,H] or null
   uint16_t* part_o;         // [splits, B*T, H, Dv] bf16, each split's output normalised by its own sum (splits > 1)
@@ -77,7 +80,7 @@ hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipS
 
 // topk.hip
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
-hipError_t launch_hist(const float* scores, const int32_t* seq_lens, uint32_t* hist, int B, int T,
+hipError_t launch_hist(const float* scores, const int32_t* seq_lens, int len_sub, uint32_t* hist, int B, int T,
                        int64_t Lmax, hipStream_t stream);
 hipError_t launch_select(const TopkParams& p, hipStream_t stream);
 

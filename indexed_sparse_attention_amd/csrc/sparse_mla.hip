@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kGenThreads) void mla_generic_kernel(MlaParams p) {
 
   const int h = blockIdx.x, bt = blockIdx.y, b = bt / p.T;
   const int tid = threadIdx.x, wave = tid / kWave;
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const int len = filled_rows(p.seq_lens[b], p.Lmax, p.len_sub);
   const int64_t qoff = ((int64_t)bt * p.H + h) * p.Dqk;
   for (int i = tid; i < p.Dqk; i += kGenThreads) s_q[i] = mla_load(p.q, p.q_dtype, qoff + i);
 
@@ -449,7 +449,7 @@ void mla_mfma_kernel(MlaParams p) {
   const int b = bt / p.T;
   const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
   const int lg = l >> 4, lc = l & 15;
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const int len = filled_rows(p.seq_lens[b], p.Lmax, p.len_sub);
   const int h0 = hg * kHeadsPerWG + wave * kHeadsPerWave;  // this wave's first head
   // row index of position 0 of this sequence (paged cache: rows are
   // translated to physical rows when the index list is loaded)

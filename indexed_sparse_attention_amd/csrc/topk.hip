@@ -55,11 +55,11 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream) {
 // Standalone histogram of the top key bits over the visible scores.
 constexpr int kHistChunk = 8192;
 
-__global__ __launch_bounds__(256) void hist_kernel(const float* scores, const int32_t* seq_lens,
+__global__ __launch_bounds__(256) void hist_kernel(const float* scores, const int32_t* seq_lens, int len_sub,
                                                     uint32_t* hist, int T, int64_t Lmax) {
   __shared__ uint32_t h[kHistBins];
   const int bt = blockIdx.y, b = bt / T, t = bt % T;
-  const int64_t vis = (int64_t)clamp_len(seq_lens[b], Lmax) - T + 1 + t;
+  const int64_t vis = (int64_t)filled_rows(seq_lens[b], Lmax, len_sub) - T + 1 + t;
   const int64_t lo = (int64_t)blockIdx.x * kHistChunk;
   const int64_t hi = min(lo + kHistChunk, vis);
   if (lo >= hi) return;
@@ -74,10 +74,10 @@ __global__ __launch_bounds__(256) void hist_kernel(const float* scores, const in
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-hipError_t launch_hist(const float* scores, const int32_t* seq_lens, uint32_t* hist, int B, int T,
+hipError_t launch_hist(const float* scores, const int32_t* seq_lens, int len_sub, uint32_t* hist, int B, int T,
                        int64_t Lmax, hipStream_t stream) {
   dim3 grid((unsigned)((Lmax + kHistChunk - 1) / kHistChunk), (unsigned)(B * T));
-  hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, stream, scores, seq_lens, hist, T, Lmax);
+  hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, stream, scores, seq_lens, len_sub, hist, T, Lmax);
   return hipGetLastError();
 }
 
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(TopkParams p)
   constexpr int kRound = kSelThreads * kSelV;
 
   // every load that depends on no other: length, histogram slice, first round of scores
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const int len = filled_rows(p.seq_lens[b], p.Lmax, p.len_sub);
   BinSlice<kHistBins> hs;
   load_bin_slice<kHistBins>(p.hist + (int64_t)bt * kHistBins, hs);
   float v[kSelV];
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) 
   const uint2* mine = p.cand + (int64_t)bt * p.Lmax + c_lo;
 
   // ---- loads ----
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const int len = filled_rows(p.seq_lens[b], p.Lmax, p.len_sub);
   const uint32_t n_mine = p.chunk_cnt[(int64_t)bt * p.n_chunks + c];
   ResolveLoads rl;
   issue_resolve_loads(p, bt, rl);
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   RowShared& sh = *(RowShared*)row_lds;
   const int tid = threadIdx.x;
   const int bt = blockIdx.x, b = bt / p.T, t = bt % p.T;
-  const int len = clamp_len(p.seq_lens[b], p.Lmax);
+  const int len = filled_rows(p.seq_lens[b], p.Lmax, p.len_sub);
   const int64_t vis = max((int64_t)0, (int64_t)len - p.T + 1 + t);
   const int K = p.K;
   int32_t* out = p.topk_idx + (int64_t)bt * K;

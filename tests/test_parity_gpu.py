@@ -247,3 +247,57 @@ def test_workspace_reused_and_counters_left_zero(mode):
             G.check_attention(w, r["out"].float().cpu().numpy(), r["lse"].cpu().numpy(), ref["out"], ref["lse"])
     finally:
         del os.environ["DSA_TOPK_MODE"]
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("prefill64k", dict(batch=2, q_len=40, max_seq_len=3000, len_range=(1500, 3000), top_k=700)),
+    ("fp8_1m", dict(batch=3, q_len=2, max_seq_len=5000, len_range=(2500, 5000), top_k=600)),
+    ("mx128k", dict(batch=2, q_len=7, max_seq_len=4000, len_range=(3000, 4000), top_k=500)),
+])
+def test_token_tiles_match_oracle(name, kw):
+    # A call whose workspace would pass its budget runs tile after tile of
+    # one sequence's query tokens, each tile seeing exactly what its tokens
+    # see in the whole problem; a small budget makes these problems tile
+    # (several sequences, ragged lengths, tiles ending before the last
+    # token).  Every entry point is checked against the oracle.
+    w = _case(name, **kw)
+    ref = oracle.forward(w)
+    d = G.to_device(w)
+    whole = G.run_forward(w)
+    os.environ["DSA_TILE_BUDGET"] = str(256 * 1024)
+    try:
+        p = dsa.forward_problem(d["q_idx"], d["k_idx"], d["q"], d["kv"], d["seq_lens"], w.top_k, w.v_dim,
+                                w.softmax_scale, k_scale=d["k_scale"], kv_scale=d["kv_scale"])
+        tiled_ws = dsa.forward_workspace_size(p)
+        got = G.run_forward(w, d)
+        scores = torch.from_numpy(got["scores"]).cuda()
+        idx, cnt = dsa.dsa_topk(scores, d["seq_lens"], w.top_k)
+        out, lse = dsa.dsa_sparse_mla_decode(d["q"], d["kv"], torch.from_numpy(ref["idx"]).cuda(), d["seq_lens"],
+                                             w.v_dim, w.softmax_scale, kv_scale=d["kv_scale"],
+                                             out_dtype=G.out_torch_dtype(w))
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["DSA_TILE_BUDGET"]
+    assert tiled_ws < dsa.forward_workspace_size(p), "the budget did not make the call tile"
+    G.check_scores(w, got["scores"], ref["scores"])
+    G.check_topk(w, got["topk_idx"], got["topk_count"], ref["idx"], ref["count"])
+    G.check_attention(w, got["out"], got["lse"], ref["out"], ref["lse"])
+    G.check_topk(w, idx.cpu().numpy(), cnt.cpu().numpy(), ref["idx"], ref["count"])
+    G.check_attention(w, out.float().cpu().numpy(), lse.cpu().numpy(), ref["out"], ref["lse"])
+    for k in ("topk_idx", "topk_count"):  # (the attention's split count follows the launch's size)
+        assert np.array_equal(got[k], whole[k]), f"tiled {k} differs from the whole call"
+
+
+def test_token_tiles_on_paged_caches():
+    from tests.test_paged_gpu import paginate, run_paged
+    w = _case("prefill64k", batch=2, q_len=24, max_seq_len=3000, len_range=(1800, 3000), top_k=600)
+    ref = oracle.forward(w)
+    pgd = paginate(w, 64, seed=3)
+    os.environ["DSA_TILE_BUDGET"] = str(256 * 1024)
+    try:
+        got = run_paged(w, pgd)
+    finally:
+        del os.environ["DSA_TILE_BUDGET"]
+    G.check_scores(w, got["scores"], ref["scores"])
+    G.check_topk(w, got["topk_idx"], got["topk_count"], ref["idx"], ref["count"])
+    G.check_attention(w, got["out"], got["lse"], ref["out"], ref["lse"])
