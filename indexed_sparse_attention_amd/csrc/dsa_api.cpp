@@ -311,7 +311,7 @@ dsa_status check_mla_inputs(const dsa_problem* p, const void* q, const void* kv,
 dsa::ScoreParams score_params(const dsa_problem* p, const void* q_idx, const float* head_w,
                               const void* k_idx, const void* k_scale, const int32_t* seq_lens,
                               float* scores, uint32_t* hist, int len_sub = 0) {
-  dsa::ScoreParams s;
+  dsa::ScoreParams s{};
   s.len_sub = len_sub;
   s.q_idx = q_idx;
   s.head_w = head_w;

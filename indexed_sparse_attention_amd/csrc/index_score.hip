@@ -229,11 +229,26 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   if (U == 0) return;
   const int64_t G = gridDim.x;
   const int64_t wg = blockIdx.x;
-  // workgroups of a segment starting at unit `start` with `n` units
+  // Two ways to share a segment's units among workgroups, chosen per
+  // segment from its size alone (so every workgroup takes the same choice):
+  //  - a segment of at least 8 workgroups' shares U / G (a long sequence
+  //    with few query tokens: decode) goes to the workgroups
+  //    [wg_first, wg_end) its units start and end in, its 16-position
+  //    sub-tiles round-robin over all their waves, so at any moment they
+  //    read one window of consecutive rows (7 us faster than the exact split
+  //    at 8 sequences x 128K keys);
+  //  - a smaller one is split exactly: workgroup wg takes the units in
+  //    [u_lo, u_hi), its own U / G share of all segments' units in order.
+  //    (The round-robin ranges round to whole workgroups: with segments near
+  //    one share, some workgroup got two whole segments and the launch took
+  //    twice as long, 4096 prefill tokens over 64K keys split in 512-token
+  //    launches 1.50 ms per launch against 0.79 ms exact.)
   auto wg_first = [&](int64_t start) -> int64_t { return start * G / U; };
   auto wg_end = [&](int64_t start, int64_t n) -> int64_t {
     return max(wg_first(start) + 1, (start + n) * G / U);
   };
+  auto round_robin = [&](int64_t n) -> bool { return p.split_mode == 1 || (p.split_mode == 0 && n * G >= 8 * U); };
+  const int64_t u_lo = wg * U / G, u_hi = (wg + 1) * U / G;
 
   if (p.hist)
     for (int i = tid; i < TQ * kHistBins; i += kScoreThreads) lds_hist[i] = 0;
@@ -241,6 +256,8 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   // Pass 2: walk the segments in chunks of kScoreThreads, with an exclusive
   // scan of their unit counts, and process the segments this workgroup serves.
   int64_t chunk_base = 0;
+  // (a chunk starting at or past u_hi can still hold a round-robin segment
+  // that wg serves while wg_first(its start) <= wg, never past that)
   for (int c0 = 0; c0 < n_seg && wg_first(chunk_base) <= wg; c0 += kScoreThreads) {
     const int n_here = min(kScoreThreads, n_seg - c0);
     const int64_t mine = tid < n_here ? (c0 == 0 ? units0 : seg_units(c0 + tid)) : 0;
@@ -272,7 +289,10 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
     bool serves = false;
     if (tid < n_here && mine > 0) {
       const int64_t st = chunk_base + off + v - mine;
-      serves = st * G < (wg + 1) * U && (wg * U <= st * G || (wg + 1) * U <= (st + mine) * G);
+      if (round_robin(mine))
+        serves = st * G < (wg + 1) * U && (wg * U <= st * G || (wg + 1) * U <= (st + mine) * G);
+      else
+        serves = st < u_hi && st + mine > u_lo;
     }
     const uint64_t hits = __ballot(serves);
     if (l == 0) s_wcnt[wave] = __popcll(hits);
@@ -291,10 +311,19 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       const int64_t seg_start = chunk_base + s_excl[i];
       const int seg = c0 + i;
       const int64_t seg_n = (i + 1 < n_here ? s_excl[i + 1] : chunk_total) - s_excl[i];
-      const int64_t g0 = wg_first(seg_start), g1 = wg_end(seg_start, seg_n);
-      // this wave's units: iw, iw + n_w, iw + 2 n_w, ... of the segment
-      const int64_t n_w = (g1 - g0) * kScoreWaves;
-      const int64_t iw = (wg - g0) * kScoreWaves + wave;
+      // this wave's sub-tiles: iw, iw + n_w, iw + 2 n_w, ... below sub_end
+      int64_t n_w, iw, sub_end;
+      if (round_robin(seg_n)) {
+        const int64_t g0 = wg_first(seg_start), g1 = wg_end(seg_start, seg_n);
+        n_w = (g1 - g0) * kScoreWaves;
+        iw = (wg - g0) * kScoreWaves + wave;
+        sub_end = 4 * seg_n;
+      } else {
+        const int64_t ua = max(seg_start, u_lo) - seg_start, ub = min(seg_start + seg_n, u_hi) - seg_start;
+        n_w = kScoreWaves;
+        iw = 4 * ua + wave;
+        sub_end = 4 * ub;
+      }
 
       // ---------------- one segment: sequence b, tokens t0 .. t0+TQ-1 ----------------
       const int b = seg / n_groups;
@@ -304,11 +333,16 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       const int len = __builtin_amdgcn_readfirstlane(s_len[i]);
       const int vis_last = len - p.T + 1 + min(t0 + TQ - 1, p.T - 1);  // >= 1 here
 
-      // The segment's 16-position sub-tiles go round-robin over its n_w
-      // waves (sub-tile iw + x n_w is this wave's x-th), so at any moment the
-      // waves read one contiguous window of consecutive 4 KB (bf16) tiles.
-      // A unit is 4 of a wave's sub-tiles: x = 4u .. 4u+3.
-      const int64_t n_sub = iw < 4 * seg_n ? (4 * seg_n - iw + n_w - 1) / n_w : 0;
+      // The 16-position sub-tiles go round-robin over n_w waves (those of
+      // all the segment's workgroups, or of this one; sub-tile iw + x n_w is
+      // this wave's x-th), so at any moment the waves read one contiguous
+      // window of consecutive 4 KB (bf16) tiles.  A unit is 4 of a wave's
+      // sub-tiles: x = 4u .. 4u+3.
+      const int64_t n_sub = iw < sub_end ? (sub_end - iw + n_w - 1) / n_w : 0;
+      // A wave's last unit can run past its n_sub sub-tiles; those read no
+      // rows, and their positions (from pos_lim on) are another
+      // workgroup's under the exact split: nothing is stored or counted there.
+      const int64_t pos_lim = sub_end * 16;
       const int n_units = (int)((n_sub + 3) / 4);
       constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
       const __amdgpu_buffer_rsrc_t krows = __builtin_amdgcn_make_buffer_rsrc(
@@ -549,7 +583,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
               float sc = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16, kWave);
               if constexpr (KF == kKeyE4M3) sc *= kscale;
               sbuf[tq][ub] = sc;
-              if (p.hist && t0 + tq < p.T && pos < (int64_t)len - p.T + 1 + t0 + tq)
+              if (p.hist && t0 + tq < p.T && pos < pos_lim && pos < (int64_t)len - p.T + 1 + t0 + tq)
                 atomicAdd(&lds_hist[tq * kHistBins + (score_key(sc) >> kHistShift)], 1u);
             }
           }
@@ -558,7 +592,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 #pragma unroll
         for (int ub = 0; ub < RB; ++ub) {
           const int64_t pos = sub_pos(4 * (u0 + ub) + lg) + lc;
-          if (u0 + ub < n_units && pos < vis_last) {
+          if (u0 + ub < n_units && pos < vis_last && pos < pos_lim) {
 #pragma unroll
             for (int tq = 0; tq < TQ; ++tq)
               if (t0 + tq < p.T) p.scores[((int64_t)b * p.T + t0 + tq) * p.Lmax + pos] = sbuf[tq][ub];
@@ -633,8 +667,10 @@ static int env_int(const char* name, int dflt) {
 // per CU and DSA_SCORE_WGS the total.  (Measured at the 128K decode shape:
 // variant 0 at 2/CU streams the keys about 4 % faster than variant 1 at
 // 1/CU.)
-hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream, hipEvent_t ev_start,
-                        hipEvent_t ev_stop) {
+hipError_t launch_score(const ScoreParams& p_in, bool allow_mfma, int num_cus, hipStream_t stream,
+                        hipEvent_t ev_start, hipEvent_t ev_stop) {
+  ScoreParams p = p_in;
+  p.split_mode = env_int("DSA_SCORE_SPLIT", 0);  // (tests run both splits on small problems)
   if (allow_mfma && score_mfma_supported(p)) {
     const int variant = env_int("DSA_SCORE_VARIANT", 0);
     // two workgroups per CU (bf16 variants 1 and 2: one, with 8-deep rings or 8 waves)

@@ -24,6 +24,7 @@ struct ScoreParams {
   const int32_t* block_table;
   int64_t num_pages;
   int max_pages, page_shift;
+  int split_mode;           // 0: by segment size; 1: every segment round-robin; 2: every segment exact (tests)
 };
 
 struct TopkParams {

@@ -61,6 +61,8 @@ def check_topk_property(w, scores, idx, cnt, chunk=256):
             sel_idx = idx[b, t0:t1].long()
             valid = torch.arange(K, device=dev)[None, :] < n[:, None]
             assert torch.all(torch.where(valid, sel_idx, -1) == sel_idx), "padding must be -1"
+            # (checked before the scatter below, which needs in-range indices)
+            assert torch.all(~valid | ((sel_idx >= 0) & (sel_idx < L))), f"a selected index is out of range (b={b})"
             visible = pos[None, :] < vis[:, None]
             sel = torch.zeros_like(visible)
             sel.scatter_(1, torch.where(valid, sel_idx, 0), valid)

@@ -8,6 +8,7 @@ sets exactly), and in fact the contiguous GPU path's results bit for bit: the
 arithmetic is the same, only the addresses differ.
 """
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -102,6 +103,24 @@ def test_paged_forward_matches_oracle_and_contiguous(case):
         for t in range(w.q_len):
             vis = max(w.vis(b, t), 0)
             assert np.array_equal(got["scores"][b, t, :vis], cont["scores"][b, t, :vis])
+
+
+@pytest.mark.parametrize("case", ["prefill_chunk_p128", "fp8_drafts_p64"])
+def test_paged_exact_score_split(case):
+    # paged key reads when each workgroup takes an exact contiguous share of
+    # a segment's units (the default split of short segments)
+    kw, page_size = CASES[case]
+    kw = dict(kw)
+    w = _case(kw.pop("name"), **kw)
+    os.environ["DSA_SCORE_SPLIT"] = "2"
+    try:
+        got = run_paged(w, paginate(w, page_size, seed=12))
+    finally:
+        del os.environ["DSA_SCORE_SPLIT"]
+    ref = oracle.forward(w)
+    G.check_scores(w, got["scores"], ref["scores"])
+    G.check_topk(w, got["topk_idx"], got["topk_count"], ref["idx"], ref["count"])
+    G.check_attention(w, got["out"], got["lse"], ref["out"], ref["lse"])
 
 
 def test_paged_entry_points_separately():

@@ -83,14 +83,44 @@ def test_topk_modes_match_oracle(mode):
         del os.environ["DSA_TOPK_MODE"]
 
 
+SPLIT_CASES = {
+    "prefill_chunk": CASES["prefill_chunk"],
+    "prefill_fresh_prompt": CASES["prefill_fresh_prompt"],
+    "fp8_drafts_odd": CASES["fp8_drafts_odd"],
+    "decode_ragged": CASES["decode_ragged"],
+    "mx_two_tokens": dict(name="mx128k", batch=3, q_len=2, max_seq_len=6000, len_range=(3000, 6000), top_k=400),
+}
+
+
+@pytest.mark.parametrize("split", [1, 2])
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_score_work_splits_match_oracle(case, split):
+    # the score kernels share a segment's key units among workgroups either
+    # round-robin over all their waves (1) or as exact contiguous shares (2);
+    # by default each segment takes one by its size, so these small problems
+    # run mostly one way: force each on every case
+    kw = dict(SPLIT_CASES[case])
+    w = _case(kw.pop("name"), **kw)
+    os.environ["DSA_SCORE_SPLIT"] = str(split)
+    try:
+        _full_check(w)
+    finally:
+        del os.environ["DSA_SCORE_SPLIT"]
+
+
 @pytest.mark.parametrize("name", ["decode8k", "fp8_1m", "mx128k"])
-def test_two_tokens_with_fewer_rows_than_tokens(name):
+@pytest.mark.parametrize("split", [0, 2])
+def test_two_tokens_with_fewer_rows_than_tokens(name, split):
     # q_len 2 with len_b = 0 (no token sees anything), 1 (the first token
     # sees nothing, the second one position), 2, and a long ragged row, on
     # the two-token score kernels of bf16, per-row e4m3 and MXFP8 keys
     w = _case(name, batch=4, q_len=2, max_seq_len=3000, len_range=(2, 3000), top_k=256)
     w.seq_lens[:] = [0, 1, 2, 2999]
-    got, _ = _full_check(w)
+    os.environ["DSA_SCORE_SPLIT"] = str(split)
+    try:
+        got, _ = _full_check(w)
+    finally:
+        del os.environ["DSA_SCORE_SPLIT"]
     assert got["topk_count"].tolist() == [[0, 0], [0, 1], [1, 2], [256, 256]]
     assert np.all(got["topk_idx"][0] == -1) and np.all(got["out"][0] == 0)
     assert np.all(np.isneginf(got["lse"][0])) and np.isneginf(got["lse"][1, 0]).all()
