@@ -146,7 +146,7 @@ typedef struct dsa_problem {
   int32_t out_dtype;    /* DSA_F32 | DSA_BF16 */
 } dsa_problem;
 
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 #define DSA_FORWARD_STAGES 3 /* indexer scores, Top-K, sparse attention */
 
 int dsa_abi_version(void);
@@ -245,6 +245,14 @@ dsa_status dsa_sparse_mla_decode(const dsa_problem* p, const void* q, const void
 size_t dsa_forward_workspace_size(const dsa_problem* p);
 
 /*
+ * Query tokens per tile when dsa_forward runs problem p in token tiles (see
+ * Workspaces): tile (b, t0) covers tokens t0 .. min(t0 + n, T) - 1 of
+ * sequence b, in order b = 0 .. B-1, t0 = 0, n, 2n, ...  Returns 0 when the
+ * call runs as one pass over the whole problem, -1 for an invalid problem.
+ */
+int32_t dsa_forward_tile_tokens(const dsa_problem* p);
+
+/*
  * The whole path: indexer scores -> Top-K -> sparse MLA attention, with the
  * score histogram that drives the Top-K threshold fused into the score pass.
  * Arguments as in the three calls above, plus:
@@ -261,8 +269,9 @@ size_t dsa_forward_workspace_size(const dsa_problem* p);
  *                timing.  With the matrix-core score kernel, events 0 and 1
  *                are taken by that kernel's dispatch at its own start and end,
  *                so they time the kernel alone.  A call that runs in token
- *                tiles (see Workspaces) records event 0 before its first
- *                tile and events 1 .. 3 after its last.
+ *                tiles (see Workspaces) records the events around every
+ *                tile's stages in turn: when it returns they time the stages
+ *                of its last tile.
  */
 dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* head_w,
                        const void* k_idx, const void* k_scale, const void* q, const void* kv,
@@ -270,6 +279,29 @@ dsa_status dsa_forward(const dsa_problem* p, const void* q_idx, const float* hea
                        int32_t* topk_idx, int32_t* topk_count, void* out, float* lse, void* ws,
                        size_t ws_bytes, struct ihipStream_t* stream,
                        struct ihipEvent_t* const* stage_events);
+
+/*
+ * Workgroup timeline, for load-balance analysis ("Inference Acceleration for
+ * New Large Model Architectures" §6.3, observability).  While a buffer is
+ * set, every launch of the matrix-core score kernel, the Top-K kernels and
+ * the matrix-core attention kernels writes two stamps of the GPU's constant
+ * 100 MHz clock per workgroup, at its start and when its first thread
+ * leaves, to
+ *   buf[(kind * slots + w) * 2 + 0 / 1]
+ * with kind 0 scores, 1 Top-K chunk step, 2 Top-K emit step, 3 Top-K row
+ * mode, 4 attention, 5 attention split merge, and w the workgroup's linear
+ * index (x fastest, then y, then z).  A launch with more than `slots`
+ * workgroups writes nothing; each launch overwrites its kind's entries.
+ *   buf    device memory on the GPU the calls run on, at least
+ *          DSA_TRACE_KINDS * slots * 2 uint64 values, 8-byte aligned, owned
+ *          by the caller and kept alive while set; NULL (or slots <= 0)
+ *          turns tracing off.
+ * A process-wide setting, read at every launch from any thread.  Returns
+ * DSA_ERR_INVALID_ARG for a misaligned buffer.
+ */
+#define DSA_TRACE_KINDS 6
+
+dsa_status dsa_set_workgroup_trace(uint64_t* buf, int64_t slots);
 
 /*
  * dsa_forward for callers that cannot allocate device memory: code under HIP

@@ -92,6 +92,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_sparse_mla_workspace_size.argtypes = [PP]
     lib.dsa_sparse_mla_decode.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.dsa_forward_workspace_size.argtypes = [PP]
+    lib.dsa_forward_tile_tokens.argtypes = [PP]
+    lib.dsa_forward_tile_tokens.restype = ctypes.c_int32
+    lib.dsa_set_workgroup_trace.argtypes = [P, ctypes.c_int64]
+    lib.dsa_set_workgroup_trace.restype = ctypes.c_int
     lib.dsa_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P]
     lib.dsa_kernel_choice.argtypes = [PP, ctypes.c_char_p, ctypes.c_size_t]
     PG = ctypes.POINTER(Paging)
@@ -230,6 +234,30 @@ def make_problem(*, batch, q_len, max_seq_len, idx_heads=1, idx_dim=1, heads=1, 
 
 def forward_workspace_size(p: Problem) -> int:
     return load_library().dsa_forward_workspace_size(ctypes.byref(p))
+
+
+def forward_tile_tokens(p: Problem) -> int:
+    """Query tokens per token tile of dsa_forward on p (0: one pass over the
+    whole problem; -1: invalid problem)."""
+    return load_library().dsa_forward_tile_tokens(ctypes.byref(p))
+
+
+TRACE_KINDS = ("scores", "topk_chunk", "topk_emit", "topk_row", "attention", "attention_merge")
+
+
+def set_workgroup_trace(buf: Optional[torch.Tensor], slots: int = 0) -> None:
+    """Per-workgroup clock stamps of every later launch into `buf` (an int64
+    device tensor of len(TRACE_KINDS) * slots * 2 values, kept alive while
+    set), laid out as [kind, workgroup, start / end] in TRACE_KINDS order;
+    None turns tracing off."""
+    lib = load_library()
+    if buf is None:
+        _check(lib.dsa_set_workgroup_trace(None, 0))
+        return
+    _expect(buf, "buf", (len(TRACE_KINDS) * slots * 2,), (torch.int64,), None)
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        _bad("buf must be a contiguous device tensor")
+    _check(lib.dsa_set_workgroup_trace(_ptr(buf), slots))
 
 
 def topk_workspace_size(p: Problem) -> int:

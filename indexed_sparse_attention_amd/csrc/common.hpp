@@ -86,6 +86,20 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Stamps a workgroup's start (construction) and its first thread's exit
+// (destruction) into a wg_trace region; nothing when the region is null.
+struct WgTrace {
+  uint64_t* tr;
+  __device__ __forceinline__ void stamp(int which) const {
+    if (tr && threadIdx.x == 0) {
+      const int64_t w = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+      tr[2 * w + which] = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+  __device__ __forceinline__ explicit WgTrace(uint64_t* t) : tr(t) { stamp(0); }
+  __device__ __forceinline__ ~WgTrace() { stamp(1); }
+};
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));

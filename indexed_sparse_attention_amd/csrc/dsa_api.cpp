@@ -472,9 +472,33 @@ hipError_t set_max_dynamic_lds(const void* kernel, int bytes) {
 
 }  // namespace dsa
 
+// ------------------------------------------------------------------ workgroup trace
+namespace {
+std::mutex g_trace_mu;
+uint64_t* g_trace = nullptr;
+int64_t g_trace_slots = 0;
+}  // namespace
+
+namespace dsa {
+uint64_t* trace_region(int kind, int64_t grid) {
+  std::lock_guard<std::mutex> g(g_trace_mu);
+  if (!g_trace || grid > g_trace_slots || kind < 0 || kind >= kTraceKinds) return nullptr;
+  return g_trace + (int64_t)kind * g_trace_slots * 2;
+}
+}  // namespace dsa
+
 extern "C" {
 
 int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+dsa_status dsa_set_workgroup_trace(uint64_t* buf, int64_t slots) {
+  static_assert(DSA_TRACE_KINDS == dsa::kTraceKinds, "trace kinds of the header and the kernels differ");
+  if (buf && slots > 0) REQUIRE(aligned(buf, 8), "buf must be 8-byte aligned");
+  std::lock_guard<std::mutex> g(g_trace_mu);
+  g_trace = slots > 0 ? buf : nullptr;
+  g_trace_slots = g_trace ? slots : 0;
+  return ok();
+}
 
 const char* dsa_status_string(dsa_status s) {
   switch (s) {
@@ -684,6 +708,11 @@ size_t dsa_forward_workspace_size(const dsa_problem* p) {
   return (size_t)fwd_ws_bytes(p);
 }
 
+int32_t dsa_forward_tile_tokens(const dsa_problem* p) {
+  if (validate_problem(p) != DSA_OK) return -1;
+  return tile_tokens(p, fwd_bytes);
+}
+
 // kValidate checks every argument but the workspace and enqueues nothing;
 // kRunClearing zeroes the workspace's counters (a fill kernel) before the
 // path runs, for a workspace whose contents are not known.
@@ -777,13 +806,8 @@ static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const
       return st;
     return ok();
   }
-  // token tiles: the events bracket the whole call (event 0 before the first
-  // tile, events 1 .. 3 after the last)
-  auto rec = [&](int i) -> dsa_status {
-    if (!stage_events) return DSA_OK;
-    return hip_check(hipEventRecord((hipEvent_t)stage_events[i], s), "event record");
-  };
-  if ((st = rec(0)) != DSA_OK) return st;
+  // token tiles: every tile records the stage events around its own stages,
+  // so on return they time the last tile's
   const int T = p->q_len;
   const int64_t H = p->heads;
   for (int b = 0; b < p->batch; ++b) {
@@ -802,12 +826,10 @@ static dsa_status forward_impl(const dsa_problem* p, const dsa_paging* pg, const
                             seq_lens + b, T - t0 - nn, scores ? scores + q0 * p->max_seq_len : nullptr,
                             topk_idx ? topk_idx + q0 * p->top_k : nullptr, topk_count ? topk_count + q0 : nullptr,
                             advance(out, q0 * H * p->v_dim * elem_bytes(p->out_dtype)), lse ? lse + q0 * H : nullptr,
-                            w, s, nullptr)) != DSA_OK)
+                            w, s, stage_events)) != DSA_OK)
         return st;
     }
   }
-  for (int i = 1; i <= DSA_FORWARD_STAGES; ++i)
-    if ((st = rec(i)) != DSA_OK) return st;
   return ok();
 }
 

@@ -176,6 +176,7 @@ struct QRegs<TQ, kKeyMX> {
 
 template <int TQ, int NSLOT, int KF, int MINB, int NT, bool PAGED>
 __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
+  const WgTrace wg_trace_(p.wg_trace);
   constexpr bool FP8 = KF != kKeyBF16, MX = KF == kKeyMX;
   constexpr int kScoreThreads = NT, kScoreWaves = NT / kWave;
   // LDS: [TQ] index queries in operand order (bf16: 64 x 128 x 2 B; e4m3: 64 x 128 B),
@@ -200,11 +201,19 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   const int n_groups = (p.T + TQ - 1) / TQ;
   const int n_seg = p.B * n_groups;
 
+  // A segment's weight in the work split: its units of 64 positions plus
+  // kSegCost for what every segment costs besides its units (its queries and
+  // weights staged, the key ring filled, its histogram flushed), about 16
+  // units' time.  (Without it a fresh 8192-token prompt gave its first
+  // workgroup the first 256 token pairs, a unit or two each, and that
+  // workgroup finished at 3.1 ms where the median one did at 0.9 ms.)  The
+  // weight puts kSegCost virtual units in front of the segment's real ones.
+  constexpr int64_t kSegCost = 16;
   auto seg_units_len = [&](int seg, int len) -> int64_t {
     const int g = seg % n_groups;
     const int t_last = min(g * TQ + TQ - 1, p.T - 1);
     const int64_t vis_end = (int64_t)len - p.T + 1 + t_last;
-    return vis_end > 0 ? (vis_end + 63) / 64 : 0;
+    return vis_end > 0 ? (vis_end + 63) / 64 + kSegCost : 0;
   };
   auto seg_units = [&](int seg) -> int64_t {
     return seg_units_len(seg, filled_rows(p.seq_lens[seg / n_groups], p.Lmax, p.len_sub));
@@ -310,16 +319,20 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       const int i = __builtin_amdgcn_readfirstlane(s_list[k]);  // (uniform: it selects the key buffer)
       const int64_t seg_start = chunk_base + s_excl[i];
       const int seg = c0 + i;
-      const int64_t seg_n = (i + 1 < n_here ? s_excl[i + 1] : chunk_total) - s_excl[i];
+      const int64_t seg_w = (i + 1 < n_here ? s_excl[i + 1] : chunk_total) - s_excl[i];  // weight
+      const int64_t seg_n = seg_w - kSegCost;  // real units (>= 1: the segment is served)
       // this wave's sub-tiles: iw, iw + n_w, iw + 2 n_w, ... below sub_end
       int64_t n_w, iw, sub_end;
-      if (round_robin(seg_n)) {
-        const int64_t g0 = wg_first(seg_start), g1 = wg_end(seg_start, seg_n);
+      if (round_robin(seg_w)) {
+        const int64_t g0 = wg_first(seg_start), g1 = wg_end(seg_start, seg_w);
         n_w = (g1 - g0) * kScoreWaves;
         iw = (wg - g0) * kScoreWaves + wave;
         sub_end = 4 * seg_n;
       } else {
-        const int64_t ua = max(seg_start, u_lo) - seg_start, ub = min(seg_start + seg_n, u_hi) - seg_start;
+        // this workgroup's share of the weight, less the virtual units
+        const int64_t ua = max(max(seg_start, u_lo) - seg_start - kSegCost, (int64_t)0);
+        const int64_t ub = max(min(seg_start + seg_w, u_hi) - seg_start - kSegCost, (int64_t)0);
+        if (ub <= ua) continue;  // (uniform) only virtual units: nothing to do
         n_w = kScoreWaves;
         iw = 4 * ua + wave;
         sub_end = 4 * ub;
@@ -634,10 +647,12 @@ bool score_mfma_supported(const ScoreParams& p) {
 }
 
 template <int TQ, int NSLOT, int KF, int MINB, int NT, bool PAGED>
-static void launch_mfma_k(const ScoreParams& p, int grid, hipStream_t stream, hipEvent_t ev_start,
+static void launch_mfma_k(const ScoreParams& p_in, int grid, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop) {
   constexpr int kQBytes = KF != kKeyBF16 ? kHi * kDi : kHi * kDi * 2;
-  const size_t lds = TQ * kQBytes + (p.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
+  const size_t lds = TQ * kQBytes + (p_in.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
+  ScoreParams p = p_in;
+  p.wg_trace = trace_region(kTraceScore, grid);
   if (ev_start || ev_stop)  // events taken by the dispatch itself at the kernel's start and end
     hipExtLaunchKernelGGL((score_mfma_kernel<TQ, NSLOT, KF, MINB, NT, PAGED>), dim3(grid), dim3(NT), lds, stream,
                           ev_start, ev_stop, 0, p);
@@ -671,6 +686,7 @@ hipError_t launch_score(const ScoreParams& p_in, bool allow_mfma, int num_cus, h
                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   ScoreParams p = p_in;
   p.split_mode = env_int("DSA_SCORE_SPLIT", 0);  // (tests run both splits on small problems)
+  p.wg_trace = nullptr;
   if (allow_mfma && score_mfma_supported(p)) {
     const int variant = env_int("DSA_SCORE_VARIANT", 0);
     // two workgroups per CU (bf16 variants 1 and 2: one, with 8-deep rings or 8 waves)

@@ -25,6 +25,7 @@ struct ScoreParams {
   int64_t num_pages;
   int max_pages, page_shift;
   int split_mode;           // 0: by segment size; 1: every segment round-robin; 2: every segment exact (tests)
+  uint64_t* wg_trace;       // null, or per-workgroup clock stamps (see trace_region)
 };
 
 struct TopkParams {
@@ -43,6 +44,7 @@ struct TopkParams {
   int64_t Lmax;
   int chunk;                // positions per select workgroup
   int n_chunks;             // ceil(Lmax / chunk) <= 1024
+  uint64_t* wg_trace;       // null, or per-workgroup clock stamps (see trace_region)
 };
 
 struct MlaParams {
@@ -67,7 +69,19 @@ struct MlaParams {
   const int32_t* block_table;
   int64_t num_pages;
   int max_pages, page_shift;
+  uint64_t* wg_trace;       // null, or per-workgroup clock stamps (see trace_region)
 };
+
+// Workgroup timeline: a kernel given a non-null wg_trace writes, from its
+// first thread, the GPU's constant 100 MHz clock when workgroup w starts and
+// when that thread leaves into wg_trace[2 w] and wg_trace[2 w + 1] (w the
+// workgroup's linear index).  trace_region gives a launch of `kind` with
+// `grid` workgroups its region of the buffer set by dsa_set_workgroup_trace,
+// or null (tracing off, or the grid larger than the buffer's slots).
+enum TraceKind {
+  kTraceScore, kTraceSelectChunk, kTraceSelectEmit, kTraceSelectRow, kTraceMla, kTraceMlaCombine, kTraceKinds
+};
+uint64_t* trace_region(int kind, int64_t grid);
 
 // Raises a kernel's dynamic LDS limit to `bytes` (once per kernel and device).
 hipError_t set_max_dynamic_lds(const void* kernel, int bytes);

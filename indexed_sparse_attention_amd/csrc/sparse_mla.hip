@@ -437,6 +437,7 @@ __device__ __forceinline__ void fp8_decode(uint8_t* buf, const float (&sc)[NSC],
 template <bool FP8, int NSC = 1>
 __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_mfma_kernel(MlaParams p) {
+  const WgTrace wg_trace_(p.wg_trace);
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_smem[];
   MlaShared& sh = *reinterpret_cast<MlaShared*>(mla_smem);
   int32_t* s_idx = sh.idx;
@@ -881,6 +882,7 @@ void mla_mfma_kernel(MlaParams p) {
 constexpr int kCombineBatch = 16;
 
 __global__ __launch_bounds__(64) void mla_combine_kernel(MlaParams p) {
+  const WgTrace wg_trace_(p.wg_trace);
   const int h = blockIdx.x, bt = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t BT = (int64_t)p.B * p.T;
@@ -943,9 +945,12 @@ bool mla_mfma_supported(const MlaParams& p) {
          (p.kv_dtype == kBF16 || p.kv_dtype == kE4M3 || p.kv_dtype == kE4M3T128);
 }
 
-hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream) {
+hipError_t launch_mla(const MlaParams& p_in, bool allow_mfma, hipStream_t stream) {
+  MlaParams p = p_in;
+  p.wg_trace = nullptr;
   if (allow_mfma && mla_mfma_supported(p)) {
     dim3 grid((unsigned)p.splits, (unsigned)(p.B * p.T), (unsigned)(p.H / kHeadsPerWG));
+    p.wg_trace = trace_region(kTraceMla, (int64_t)grid.x * grid.y * grid.z);
     const size_t lds = sizeof(MlaShared);
     hipError_t e;
     if (p.kv_dtype == kBF16) {
@@ -964,10 +969,12 @@ hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream) {
     }
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
+    p.wg_trace = trace_region(kTraceMlaCombine, (int64_t)p.H * p.B * p.T);
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)p.H, (unsigned)(p.B * p.T)), dim3(kWave), 0,
                        stream, p);  // needs Dv <= 512 and splits <= 64
     return hipGetLastError();
   }
+  p.wg_trace = nullptr;
   hipLaunchKernelGGL(mla_generic_kernel, dim3((unsigned)p.H, (unsigned)(p.B * p.T)), dim3(kGenThreads),
                      0, stream, p);
   return hipGetLastError();

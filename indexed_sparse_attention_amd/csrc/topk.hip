@@ -120,6 +120,7 @@ __device__ __forceinline__ void load_scores(const float* row, int64_t s0, int64_
 // VEC4: the scores are 16-byte aligned and Lmax is a multiple of 4.
 template <bool VEC4>
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(TopkParams p) {
+  const WgTrace wg_trace_(p.wg_trace);
   __shared__ uint32_t s_wave[2 * kSelWaves];
   __shared__ uint32_t s_res[2];
   const int tid = threadIdx.x;
@@ -200,6 +201,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(TopkParams p)
 // this chunk's first kSelThreads * kEmitE candidates; a typical workgroup
 // waits for memory once.
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) {
+  const WgTrace wg_trace_(p.wg_trace);
   extern __shared__ __attribute__((aligned(16))) uint8_t emit_lds[];
   EmitShared& sh = *(EmitShared*)emit_lds;
   const int tid = threadIdx.x;
@@ -349,6 +351,7 @@ __device__ void row_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s_
 }
 
 __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
+  const WgTrace wg_trace_(p.wg_trace);
   extern __shared__ __attribute__((aligned(16))) uint8_t row_lds[];
   RowShared& sh = *(RowShared*)row_lds;
   const int tid = threadIdx.x;
@@ -500,13 +503,16 @@ bool select_row_mode(const TopkParams& p) {
   return p.Lmax <= kRowMaxLen && (int64_t)p.B * p.T >= 512;
 }
 
-hipError_t launch_select(const TopkParams& p, hipStream_t stream) {
+hipError_t launch_select(const TopkParams& p_in, hipStream_t stream) {
+  TopkParams p = p_in;
   if (select_row_mode(p)) {
+    p.wg_trace = trace_region(kTraceSelectRow, (int64_t)p.B * p.T);
     hipLaunchKernelGGL(select_row_kernel, dim3((unsigned)(p.B * p.T)), dim3(kRowThreads), sizeof(RowShared),
                        stream, p);
     return hipGetLastError();
   }
   dim3 grid((unsigned)p.n_chunks, (unsigned)(p.B * p.T));
+  p.wg_trace = trace_region(kTraceSelectChunk, (int64_t)p.n_chunks * p.B * p.T);
   if ((((uintptr_t)p.scores) & 15) == 0 && p.Lmax % 4 == 0)
     hipLaunchKernelGGL(select_chunk_kernel<true>, grid, dim3(kSelThreads), 0, stream, p);
   else
@@ -515,6 +521,7 @@ hipError_t launch_select(const TopkParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = set_max_dynamic_lds((const void*)select_emit_kernel, (int)sizeof(EmitShared));
   if (e != hipSuccess) return e;
+  p.wg_trace = trace_region(kTraceSelectEmit, (int64_t)p.n_chunks * p.B * p.T);
   hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kSelThreads), sizeof(EmitShared), stream, p);
   return hipGetLastError();
 }

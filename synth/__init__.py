@@ -14,6 +14,7 @@ scaled as listed:
   decode8k  B=32, T=1,    L=8192,       bf16, indexer 64x128, MLA 128 heads 576/512, K=2048
   decode128k B=8, T=1,    L=131072 max, lengths uniform in [98304, 131072], as decode8k
   prefill64k B=1, T=4096, L=65536 (61440 cached + 4096 new), causal, as decode8k
+  prompt8k  B=1, T=8192, L=8192: a fresh prompt (token t sees t + 1 rows), as decode8k
   fp8_1m    B=4,  T=2,    L=1048576,    e4m3 index keys and latent cache with one
             power-of-two scale per token in {2^-2..2^2}; bf16 queries
   mx128k    as decode128k, with MXFP8 index keys (e4m3 integers, one E8M0 scale
@@ -207,6 +208,10 @@ WORKLOADS = {
                        len_range=(65536, 65536), idx_heads=64, idx_dim=128, idx_int=(-4, 4),
                        w_int=(1, 8), heads=128, qk_dim=576, v_dim=512, top_k=2048,
                        idx_dtype=BF16, q_dtype=BF16, kv_dtype=BF16, out_dtype=BF16, fp8=False),
+    "prompt8k": dict(number=7, batch=1, q_len=8192, max_seq_len=8192, len_range=(8192, 8192),
+                     idx_heads=64, idx_dim=128, idx_int=(-4, 4), w_int=(1, 8), heads=128, qk_dim=576,
+                     v_dim=512, top_k=2048, idx_dtype=BF16, q_dtype=BF16, kv_dtype=BF16, out_dtype=BF16,
+                     fp8=False),
     "fp8_1m": dict(number=5, batch=4, q_len=2, max_seq_len=1048576,
                    len_range=(1048576, 1048576), idx_heads=64, idx_dim=128, idx_int=(-4, 4),
                    w_int=(1, 8), heads=128, qk_dim=576, v_dim=512, top_k=2048,

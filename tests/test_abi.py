@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = dsa.load_library()
-    assert lib.dsa_abi_version() == 5
+    assert lib.dsa_abi_version() == 6
     assert lib.dsa_status_string(0) == b"DSA_OK"
     assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
 
@@ -70,6 +70,7 @@ def test_invalid_problem_rejected_everywhere(kw):
     p = good_problem(**kw)
     P = ctypes.byref(p)
     assert lib.dsa_forward_workspace_size(P) == 0
+    assert lib.dsa_forward_tile_tokens(P) == -1
     assert lib.dsa_topk_workspace_size(P) == 0
     assert lib.dsa_sparse_mla_workspace_size(P) == 0
     f = FAKE
@@ -141,6 +142,39 @@ def test_workspace_sizes_monotone_in_problem_size():
     # Top-K needs at least the score-key histograms and one candidate slot per position
     p = good_problem()
     assert lib.dsa_topk_workspace_size(ctypes.byref(p)) >= 2 * 1 * (4096 * 4 + 4096 * 4)
+
+
+def test_token_tiles_keep_the_workspace_under_its_budget():
+    lib = dsa.load_library()
+    assert dsa.forward_tile_tokens(good_problem(batch=8, max_seq_len=131072)) == 0  # decode: one pass
+    # a 4096-token prefill chunk over 64K keys: the largest power-of-two tile
+    # whose scratch fits 1 GiB, and the workspace is that tile's
+    p = good_problem(batch=1, q_len=4096, max_seq_len=65536)
+    n = dsa.forward_tile_tokens(p)
+    assert n == 512
+    tile = good_problem(batch=1, q_len=n, max_seq_len=65536)
+    twice = good_problem(batch=1, q_len=2 * n, max_seq_len=65536)
+    ws = lib.dsa_forward_workspace_size(ctypes.byref(p))
+    assert ws == lib.dsa_forward_workspace_size(ctypes.byref(tile)) <= 1 << 30
+    assert dsa.forward_tile_tokens(tile) == 0 and dsa.forward_tile_tokens(twice) == n  # 2n tokens pass 1 GiB
+    # a smaller budget gives smaller tiles, and an odd token count a ragged last tile
+    os.environ["DSA_TILE_BUDGET"] = str(64 << 20)
+    try:
+        p3 = good_problem(batch=3, q_len=100, max_seq_len=65536)
+        n3 = dsa.forward_tile_tokens(p3)
+        assert 0 < n3 < 100 and n3 & (n3 - 1) == 0
+        assert lib.dsa_forward_workspace_size(ctypes.byref(p3)) <= 64 << 20
+    finally:
+        del os.environ["DSA_TILE_BUDGET"]
+
+
+def test_workgroup_trace_setting():
+    lib = dsa.load_library()
+    assert lib.dsa_set_workgroup_trace(FAKE + 4, 16) == 1 and b"aligned" in lib.dsa_last_error()
+    # setting and clearing touch no GPU
+    assert lib.dsa_set_workgroup_trace(FAKE, 16) == 0
+    assert lib.dsa_set_workgroup_trace(None, 0) == 0
+    assert lib.dsa_set_workgroup_trace(FAKE, 0) == 0  # no slots: off
 
 
 def test_workspace_counter_region_and_init_validation():
