@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode queries/s and achieved HBM GB/s (% of peak) at L=128K, K=2048"
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 
 
 def parse():
@@ -57,32 +58,42 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-probe run into the traffic record, then exit")
+    ap.add_argument("--wg-trace", action="store_true",
+                    help="time one eager step's workgroups (start and end of each, per kernel) with every stage "
+                         "in one launch, print the spread, then exit")
     return ap.parse_args()
 
 
 COPY_PROBE_BYTES = 1 << 30
 SCORE_KERNEL = "score_mfma_kernel"
-SCORE_SOURCES = ("index_score.hip", "common.hpp", "kernels.hpp")
+# kernels with a counter record, and the sources (plus parameter struct) each is built from
+KERNEL_SOURCES = {
+    "score_mfma_kernel": (("index_score.hip", "common.hpp"), "ScoreParams"),
+    "select_chunk_kernel": (("topk.hip", "select.hpp", "common.hpp"), "TopkParams"),
+    "select_emit_kernel": (("topk.hip", "select.hpp", "common.hpp"), "TopkParams"),
+    "mla_mfma_kernel": (("sparse_mla.hip", "common.hpp"), "MlaParams"),
+    "mla_combine_kernel": (("sparse_mla.hip", "common.hpp"), "MlaParams"),
+}
 
 
-def traffic_path(workload):
-    return os.path.join(ROOT, "profiles", f"{SCORE_KERNEL}_{workload}_traffic.txt")
+def traffic_path(workload, kernel=SCORE_KERNEL):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
 
 
-def score_source_hash():
-    """Hash of the sources the score kernel is built from (its own file, the
-    shared device helpers and its parameter struct): a traffic record taken
-    from another version of the kernel is stale."""
+def source_hash(kernel=SCORE_KERNEL):
+    """Hash of the sources a kernel is built from (its file, the shared
+    device helpers and its parameter struct): a counter record taken from
+    another version of the kernel is stale."""
     import hashlib
     import re
+    files, struct = KERNEL_SOURCES[kernel]
     h = hashlib.sha256()
-    for f in SCORE_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "indexed_sparse_attention_amd", "csrc", f), "rb") as fh:
-            text = fh.read()
-        if f == "kernels.hpp":  # only the score kernel's parameter struct
-            m = re.search(rb"struct ScoreParams \{.*?\};", text, re.S)
-            text = m.group(0) if m else text
-        h.update(text)
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "indexed_sparse_attention_amd", "csrc", "kernels.hpp"), "rb") as fh:
+        m = re.search(rb"struct " + struct.encode() + rb" \{.*?\};", fh.read(), re.S)
+    h.update(m.group(0) if m else b"")
     return h.hexdigest()[:16]
 
 
@@ -99,44 +110,49 @@ def read_counter_csv(path, counter):
 
 
 def write_traffic_record(fetch_csv, write_csv, workload):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the score kernel, each scaled
-    by the factor that makes the copy probe's counter equal its known size."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel with a record,
+    each scaled by the factor that makes the copy probe's counter equal its
+    known size; one file per kernel under profiles/."""
     import numpy as np
-    out = {}
-    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        rows = read_counter_csv(path, name)
-        copy = [v for k, v in rows if "neg" in k.lower()]
-        score = [v for k, v in rows if SCORE_KERNEL in k]
-        if not copy or not score:
-            raise SystemExit(f"{path}: no copy-probe or {SCORE_KERNEL} dispatch with {name}")
-        factor = COPY_PROBE_BYTES / (max(copy) * 1024.0)
-        out[name] = (float(np.mean(score)) * 1024.0, factor, len(score), max(copy) * 1024.0)
-    fetch, fw = out["FETCH_SIZE"][0], out["FETCH_SIZE"][1]
-    write, ww = out["WRITE_SIZE"][0], out["WRITE_SIZE"][1]
-    traffic = fetch * fw + write * ww
-    path = traffic_path(workload)
-    with open(path, "w") as f:
-        f.write(f"# HBM traffic of {SCORE_KERNEL} per launch, workload {workload}\n")
-        f.write("# from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over\n")
-        f.write(f"#   python3 bench.py --workload {workload} --no-graph --copy-probe --steps 3 --warmup 1 "
-                "--stage-steps 2 --cpu-seconds 0\n")
-        f.write(f"# each scaled by (copy probe bytes {COPY_PROBE_BYTES}) / (counter bytes of the copy probe)\n")
-        f.write(f"source_hash: {score_source_hash()}\n")
-        f.write(f"dispatches: {out['FETCH_SIZE'][2]}\n")
-        f.write(f"fetch_bytes_raw: {fetch:.0f}\n")
-        f.write(f"fetch_factor: {fw:.4f}\n")
-        f.write(f"copy_probe_fetch_bytes_raw: {out['FETCH_SIZE'][3]:.0f}\n")
-        f.write(f"write_bytes_raw: {write:.0f}\n")
-        f.write(f"write_factor: {ww:.4f}\n")
-        f.write(f"copy_probe_write_bytes_raw: {out['WRITE_SIZE'][3]:.0f}\n")
-        f.write(f"traffic_bytes: {traffic:.0f}\n")
-    print(open(path).read())
+    rows = {name: read_counter_csv(path, name) for name, path in (("FETCH_SIZE", fetch_csv),
+                                                                 ("WRITE_SIZE", write_csv))}
+    factors = {}
+    for name, r in rows.items():
+        copy = [v for k, v in r if "neg" in k.lower()]
+        if not copy:
+            raise SystemExit(f"no copy-probe dispatch with {name}")
+        factors[name] = (COPY_PROBE_BYTES / (max(copy) * 1024.0), max(copy) * 1024.0)
+    for kernel in KERNEL_SOURCES:
+        got = {name: [v for k, v in r if kernel in k] for name, r in rows.items()}
+        if not got["FETCH_SIZE"] or not got["WRITE_SIZE"]:
+            continue
+        fetch, write = (float(np.mean(got[n])) * 1024.0 for n in ("FETCH_SIZE", "WRITE_SIZE"))
+        (fw, fcopy), (ww, wcopy) = factors["FETCH_SIZE"], factors["WRITE_SIZE"]
+        path = traffic_path(workload, kernel)
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic of {kernel} per launch, workload {workload}\n")
+            f.write("# from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over\n")
+            f.write(f"#   python3 bench.py --workload {workload} --no-graph --copy-probe --steps 3 --warmup 1 "
+                    "--stage-steps 2 --cpu-seconds 0\n")
+            f.write(f"# each scaled by (copy probe bytes {COPY_PROBE_BYTES}) / (counter bytes of the copy probe)\n")
+            f.write(f"source_hash: {source_hash(kernel)}\n")
+            f.write(f"dispatches: {len(got['FETCH_SIZE'])}\n")
+            f.write(f"fetch_bytes_raw: {fetch:.0f}\n")
+            f.write(f"fetch_factor: {fw:.4f}\n")
+            f.write(f"copy_probe_fetch_bytes_raw: {fcopy:.0f}\n")
+            f.write(f"write_bytes_raw: {write:.0f}\n")
+            f.write(f"write_factor: {ww:.4f}\n")
+            f.write(f"copy_probe_write_bytes_raw: {wcopy:.0f}\n")
+            f.write(f"fetch_bytes: {fetch * fw:.0f}\n")
+            f.write(f"write_bytes: {write * ww:.0f}\n")
+            f.write(f"traffic_bytes: {fetch * fw + write * ww:.0f}\n")
+        print(open(path).read())
 
 
-def read_traffic_record(workload):
-    """Calibrated HBM bytes per score launch, or None when there is no record
-    or it was taken from other kernel sources."""
-    path = traffic_path(workload)
+def read_traffic_record(workload, kernel=SCORE_KERNEL):
+    """Calibrated HBM bytes per launch of `kernel`, or None when there is no
+    record or it was taken from other kernel sources."""
+    path = traffic_path(workload, kernel)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -145,7 +161,7 @@ def read_traffic_record(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != score_source_hash():
+    if kv.get("source_hash") != source_hash(kernel):
         return None
     return float(kv["traffic_bytes"])
 
@@ -172,8 +188,63 @@ def algorithmic_bytes(w):
     small = BT * (w.idx_heads * w.idx_dim * 2 + w.idx_heads * 4 + w.heads * w.qk_dim * qb +
                   w.heads * w.v_dim * ob + 2 * w.top_k * 4)
     score_kernel = keys + BT * (w.idx_heads * w.idx_dim * 2 + w.idx_heads * 4)
+    # the attention stage: gathered rows, queries, index lists, outputs; its
+    # matrix-core work is 2 (Dqk + Dv) flops per selected row and head
+    attention = gathered + BT * (w.heads * w.qk_dim * qb + w.heads * w.v_dim * ob + w.top_k * 4)
+    attn_flops = 2 * sel * w.heads * (w.qk_dim + w.v_dim)
     return {"total": keys + gathered + small, "keys": keys, "gathered": gathered, "small": small,
-            "score_kernel": score_kernel}
+            "score_kernel": score_kernel, "attention": attention, "attention_flops": attn_flops}
+
+
+def wg_trace_report(dsa, torch, np, step, workload, w):
+    """One eager step with per-workgroup clock stamps (the library's
+    workgroup trace, 100 MHz): for each kernel, when its workgroups started
+    and finished relative to its first start, and how far apart."""
+    slots = 1 << 17
+    kinds = dsa.TRACE_KINDS
+    buf = torch.zeros(len(kinds) * slots * 2, dtype=torch.int64, device="cuda:0")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(dsa.FORWARD_STAGES + 1)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    dsa.set_workgroup_trace(buf, slots)
+    try:
+        step(0, stage_events=evs)
+        torch.cuda.synchronize()
+    finally:
+        dsa.set_workgroup_trace(None)
+    stage_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(dsa.FORWARD_STAGES)]
+    tr = buf.view(len(kinds), slots, 2).cpu().numpy()
+    print(f"# workgroup timeline, workload {workload}: B={w.batch} T={w.q_len} Lmax={w.max_seq_len} "
+          f"K={w.top_k}, one eager step, every stage in one launch")
+    print(f"# stage events (us): scores {stage_us[0]:.1f}  topk {stage_us[1]:.1f}  attention {stage_us[2]:.1f}")
+    print("# per kernel, in us from its first workgroup's start: the last start, the finish times' "
+          "quantiles, and the busy time (end - start) per workgroup")
+    print(f"{'kernel':16s} {'wgs':>6s} {'last_start':>10s} {'end_min':>8s} {'end_p50':>8s} {'end_p90':>8s} "
+          f"{'end_max':>8s} {'spread':>8s} {'busy_p50':>8s} {'busy_max':>8s}")
+    for k, name in enumerate(kinds):
+        st, en = tr[k, :, 0], tr[k, :, 1]
+        m = (st != 0) & (en != 0)
+        if not m.any():
+            continue
+        st, en = st[m].astype(np.float64), en[m].astype(np.float64)
+        t0 = st.min()
+        s_us, e_us, busy = (st - t0) / 100.0, (en - t0) / 100.0, (en - st) / 100.0
+        q = lambda a, f: float(np.quantile(a, f))
+        print(f"{name:16s} {int(m.sum()):6d} {s_us.max():10.2f} {e_us.min():8.2f} {q(e_us, .5):8.2f} "
+              f"{q(e_us, .9):8.2f} {e_us.max():8.2f} {e_us.max() - e_us.min():8.2f} {q(busy, .5):8.2f} "
+              f"{busy.max():8.2f}")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -185,6 +256,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU (context-parallel) "
                                    "sharding is a design note, not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.wg_trace:
+        # one launch per stage, so the timeline covers the whole problem
+        os.environ["DSA_TILE_BUDGET"] = str(1 << 40)
 
     import numpy as np
     import torch
@@ -274,6 +349,10 @@ def main():
     ref_idx = outs["topk_idx"].clone()
     ref_out = outs["out"].clone()
 
+    if args.wg_trace:
+        wg_trace_report(dsa, torch, np, step, args.workload, w)
+        return
+
     graphs = None
     if args.graph and not args.no_graph:
         graphs = []
@@ -332,8 +411,19 @@ def main():
     queries = B * T
     qps = queries / (ms * 1e-3)
     e2e_gbps = ab["total"] / (ms * 1e-3) / 1e9
+    # A call in token tiles launches each stage once per tile, and its stage
+    # events time the last tile (the last tokens of the last sequence): the
+    # per-launch figures below are that tile's, its bytes and flops those of
+    # the same problem with only its tokens.
+    n_tile = dsa.forward_tile_tokens(prob)
+    launches = B * -(-T // n_tile) if n_tile > 0 else 1
+    ab_launch = ab
+    if n_tile > 0:
+        import dataclasses
+        last = T - n_tile * ((T - 1) // n_tile)
+        ab_launch = algorithmic_bytes(dataclasses.replace(w, batch=1, q_len=last, seq_lens=w.seq_lens[B - 1:]))
     score_ms = stage_ms[0]
-    score_gbps = ab["score_kernel"] / (score_ms * 1e-3) / 1e9
+    score_gbps = ab_launch["score_kernel"] / (score_ms * 1e-3) / 1e9
     traffic = read_traffic_record(args.workload)
 
     cpu = None
@@ -359,6 +449,7 @@ def main():
             if dt >= args.cpu_seconds or n_done >= args.cpu_max_queries:
                 break
         cpu = {"value": n_done / dt, "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "cpu_model": cpu_model(),
                "sample": f"{n_done} queries of this workload, one at a time in batch order (fp64 scores over "
                          f"every visible position, full-sort Top-K, {H}-head two-pass-softmax attention) "
                          f"in {dt:.1f} s",
@@ -377,11 +468,27 @@ def main():
                    "kernels": dsa.kernel_choice(prob)},
         "hbm_gbps_e2e": e2e_gbps, "hbm_frac_e2e": e2e_gbps / HBM_PEAK_GBPS, "host_us_per_step": host_us,
         "algorithmic_bytes_per_step": ab["total"],
-        "stages_us": {"scores": stage_ms[0] * 1e3, "topk": stage_ms[1] * 1e3, "attention": stage_ms[2] * 1e3},
+        "launches_per_stage": launches, "tile_tokens": n_tile,
+        "stages_us": {"scores": stage_ms[0] * 1e3, "topk": stage_ms[1] * 1e3, "attention": stage_ms[2] * 1e3,
+                      "of": "one step" if n_tile <= 0 else f"the last of {launches} token tiles"},
         "roofline": {"kernel": "score_mfma_kernel", "bound": "hbm", "achieved": score_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "bytes_per_launch": ab["score_kernel"],
+                     "traffic": traffic, "bytes_per_launch": ab_launch["score_kernel"],
                      "launch_us": score_ms * 1e3},
+        # the attention stage (sparse MLA + split merge, eager launches):
+        # against HBM on its gathered bytes and against the dense bf16
+        # matrix-core peak on its flops
+        "roofline_attention": {"kernel": "mla_mfma_kernel+mla_combine_kernel", "stage_us": stage_ms[2] * 1e3,
+                               "bytes_per_launch": ab_launch["attention"],
+                               "hbm_gbps": ab_launch["attention"] / (stage_ms[2] * 1e-3) / 1e9,
+                               "hbm_frac": ab_launch["attention"] / (stage_ms[2] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                               "flops_per_launch": ab_launch["attention_flops"],
+                               "tflops": ab_launch["attention_flops"] / (stage_ms[2] * 1e-3) / 1e12,
+                               "mfma_frac": ab_launch["attention_flops"] / (stage_ms[2] * 1e-3) / 1e12 /
+                               BF16_PEAK_TFLOPS,
+                               "traffic": (lambda a, b: a + b if a is not None and b is not None else None)(
+                                   read_traffic_record(args.workload, "mla_mfma_kernel"),
+                                   read_traffic_record(args.workload, "mla_combine_kernel"))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
