@@ -321,21 +321,26 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       const int seg = c0 + i;
       const int64_t seg_w = (i + 1 < n_here ? s_excl[i + 1] : chunk_total) - s_excl[i];  // weight
       const int64_t seg_n = seg_w - kSegCost;  // real units (>= 1: the segment is served)
-      // this wave's sub-tiles: iw, iw + n_w, iw + 2 n_w, ... below sub_end
-      int64_t n_w, iw, sub_end;
-      if (round_robin(seg_w)) {
+      // The segment's work is its seg_n units of 64 consecutive positions
+      // (4 sub-tiles of 16).  This wave takes units id_0 + k stride (k = 0,
+      // 1, ...) below u_end: round-robin over the `stride` waves of all the
+      // segment's workgroups, or of this one's share under the exact split.
+      // Round-robin keeps the waves reading one window of consecutive rows.
+      const bool rr = round_robin(seg_w);
+      int id_0, stride, u_end;
+      if (rr) {
         const int64_t g0 = wg_first(seg_start), g1 = wg_end(seg_start, seg_w);
-        n_w = (g1 - g0) * kScoreWaves;
-        iw = (wg - g0) * kScoreWaves + wave;
-        sub_end = 4 * seg_n;
+        stride = (int)((g1 - g0) * kScoreWaves);
+        id_0 = (int)((wg - g0) * kScoreWaves + wave);
+        u_end = (int)seg_n;
       } else {
         // this workgroup's share of the weight, less the virtual units
         const int64_t ua = max(max(seg_start, u_lo) - seg_start - kSegCost, (int64_t)0);
         const int64_t ub = max(min(seg_start + seg_w, u_hi) - seg_start - kSegCost, (int64_t)0);
         if (ub <= ua) continue;  // (uniform) only virtual units: nothing to do
-        n_w = kScoreWaves;
-        iw = 4 * ua + wave;
-        sub_end = 4 * ub;
+        stride = kScoreWaves;
+        id_0 = (int)ua + wave;
+        u_end = (int)ub;
       }
 
       // ---------------- one segment: sequence b, tokens t0 .. t0+TQ-1 ----------------
@@ -346,17 +351,17 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       const int len = __builtin_amdgcn_readfirstlane(s_len[i]);
       const int vis_last = len - p.T + 1 + min(t0 + TQ - 1, p.T - 1);  // >= 1 here
 
-      // The 16-position sub-tiles go round-robin over n_w waves (those of
-      // all the segment's workgroups, or of this one; sub-tile iw + x n_w is
-      // this wave's x-th), so at any moment the waves read one contiguous
-      // window of consecutive 4 KB (bf16) tiles.  A unit is 4 of a wave's
-      // sub-tiles: x = 4u .. 4u+3.
-      const int64_t n_sub = iw < sub_end ? (sub_end - iw + n_w - 1) / n_w : 0;
-      // A wave's last unit can run past its n_sub sub-tiles; those read no
-      // rows, and their positions (from pos_lim on) are another
-      // workgroup's under the exact split: nothing is stored or counted there.
-      const int64_t pos_lim = sub_end * 16;
-      const int n_units = (int)((n_sub + 3) / 4);
+      // (A counter handing units out to whichever wave is ready was tried
+      // for round-robin segments: device-scope atomics on one address
+      // serialise in memory across the XCDs, about 90 ns each, and 128K-key
+      // decode went from 41 to 200 us.)
+      constexpr int D = NSLOT / 4;  // units in the ring ahead of the current one
+      // (wave-uniform: kept in scalar registers)
+      id_0 = __builtin_amdgcn_readfirstlane(id_0);
+      stride = __builtin_amdgcn_readfirstlane(stride);
+      u_end = __builtin_amdgcn_readfirstlane(u_end);
+      const int n_units = id_0 < u_end ? (u_end - id_0 + stride - 1) / stride : 0;  // this wave's
+      auto unit_id = [&](int k) -> int { return id_0 + k * stride; };  // (< 2^25: positions fit int64 x 64)
       constexpr int kRowBytes = FP8 ? kDi : kDi * 2;
       const __amdgpu_buffer_rsrc_t krows = __builtin_amdgcn_make_buffer_rsrc(
           (void*)((const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * kRowBytes), (short)0, len * kRowBytes, kBufferFlags);
@@ -365,7 +370,6 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                                                  (short)0, len * kGroups, kBufferFlags)
              : krows;
       const int last_row = len - 1;
-      auto sub_pos = [&](int64_t x) -> int64_t { return (iw + x * n_w) * 16; };  // first position of sub-tile x
 
       // Paged caches: a 16-row sub-tile never straddles a page (pages hold a
       // multiple of 64 rows), so each sub-tile's rows are read through a
@@ -378,9 +382,10 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       // so the entries sit in scalar registers)
       typedef const __attribute__((address_space(4))) int32_t* const_i32p;
       const const_i32p btab = PAGED ? (const_i32p)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
-      auto page_entry = [&](int x) -> int32_t {  // block-table entry of sub-tile x (clamped into the wave's)
-        const int64_t xs = min((int64_t)x, max(n_sub - 1, (int64_t)0));
-        return btab[__builtin_amdgcn_readfirstlane((int)min(sub_pos(xs) >> p.page_shift, (int64_t)p.max_pages - 1))];
+      // block-table entry of sub-tile st of the wave's unit k (clamped into the wave's units)
+      auto page_entry = [&](int k, int st) -> int32_t {
+        const int64_t pos = 64 * unit_id(min(k, max(n_units - 1, 0))) + 16 * st;
+        return btab[__builtin_amdgcn_readfirstlane((int)min(pos >> p.page_shift, (int64_t)p.max_pages - 1))];
       };
       auto phys_page = [&](int32_t entry) -> int64_t { return min(max((int64_t)entry, (int64_t)0), p.num_pages - 1); };
       auto key_rsrc = [&](int32_t entry) -> __amdgpu_buffer_rsrc_t {
@@ -401,10 +406,11 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                                                    (short)0, (int)(page_rows * kGroups), kBufferFlags);
         }
       };
-      auto st_off = [&](int x) -> uint32_t {  // offset of the key row this lane loads for sub-tile x
-        const int64_t pos = sub_pos(x) + lc;
+      // offset of the key row this lane loads for sub-tile st of the wave's unit k
+      auto st_off = [&](int k, int st) -> uint32_t {
+        const int64_t pos = 64 * unit_id(k) + 16 * st + lc;
         const int64_t r = PAGED ? (pos & (page_rows - 1)) : pos;
-        return (x < n_sub && pos < len) ? (uint32_t)(r * kRowBytes) : kNoRow;
+        return (k < n_units && pos < len) ? (uint32_t)(r * kRowBytes) : kNoRow;
       };
       int32_t pg_cur[NSLOT], pg_next[NSLOT];  // (paged) entries of the slots' sub-tiles and of those NSLOT ahead
 
@@ -421,13 +427,13 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
       auto fill_ring = [&]() {
         if constexpr (PAGED) {
 #pragma unroll
-          for (int j = 0; j < NSLOT; ++j) pg_cur[j] = page_entry(j);
+          for (int j = 0; j < NSLOT; ++j) pg_cur[j] = page_entry(j >> 2, j & 3);
 #pragma unroll
-          for (int j = 0; j < NSLOT; ++j) pg_next[j] = page_entry(j + NSLOT);
+          for (int j = 0; j < NSLOT; ++j) pg_next[j] = page_entry(D + (j >> 2), j & 3);
         }
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j)
-          load_key_tile<KF>(slot[j], key_rsrc(pg_cur[j]), scale_rsrc(pg_cur[j]), st_off(j), lg);
+          load_key_tile<KF>(slot[j], key_rsrc(pg_cur[j]), scale_rsrc(pg_cur[j]), st_off(j >> 2, j & 3), lg);
       };
 
       // head weights (used from the first unit on), then the index queries
@@ -538,14 +544,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           const bool live = u0 + ub < n_units;
           // this unit's position for lane l, and (e4m3 keys) its row scale, loaded
           // before the ring refills so waiting for it does not drain them
-          // after the reduce-scatter lane l holds position lc of its sub-tile 4u + lg
-          const int64_t pos = sub_pos(4 * (u0 + ub) + lg) + lc;
+          // after the reduce-scatter lane l holds position lc of its sub-tile lg
+          const int64_t pos = 64 * unit_id(u0 + ub) + 16 * lg + lc;
           float kscale = 1.0f;
           const float* k_scale = (const float*)p.k_scale;
           if constexpr (KF == kKeyE4M3 && !PAGED) {
             kscale = k_scale[(int64_t)b * p.Lmax + (pos < len ? pos : last_row)];
           } else if constexpr (KF == kKeyE4M3) {
-            // this lane's sub-tile 4u + lg sits in slot (4 ub + lg) % NSLOT (u0 is a multiple of NSLOT)
+            // this lane's sub-tile lg of the unit sits in slot (4 ub + lg) % NSLOT (u0 is a multiple of NSLOT)
             const int s0 = (4 * ub) % NSLOT;
             const int32_t e = lg == 0 ? pg_cur[s0] : lg == 1 ? pg_cur[s0 + 1] : lg == 2 ? pg_cur[s0 + 2] : pg_cur[s0 + 3];
             kscale = k_scale[phys_page(e) * page_rows + (pos < len ? (pos & (page_rows - 1)) : 0)];
@@ -553,7 +559,6 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           float part[TQ][4];
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
-            const int x = (u0 + ub) * 4 + st;
             const int j = (ub * 4 + st) % NSLOT;
             if (live) {
 #pragma unroll
@@ -579,11 +584,11 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                 part[tq][st] = sacc;
               }
             }
-            // refill this slot with the sub-tile NSLOT ahead (nothing is read
-            // past the wave's sub-tiles or the sequence's end)
+            // refill this slot with the same sub-tile of unit k + D (nothing
+            // is read past the wave's units or the sequence's end)
             if constexpr (PAGED) pg_cur[j] = pg_next[j];
-            load_key_tile<KF>(slot[j], key_rsrc(pg_cur[j]), scale_rsrc(pg_cur[j]), st_off(x + NSLOT), lg);
-            if constexpr (PAGED) pg_next[j] = page_entry(x + 2 * NSLOT);
+            load_key_tile<KF>(slot[j], key_rsrc(pg_cur[j]), scale_rsrc(pg_cur[j]), st_off(u0 + ub + D, st), lg);
+            if constexpr (PAGED) pg_next[j] = page_entry(u0 + ub + 2 * D, st);
           }
           if (live) {
             // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
@@ -596,7 +601,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
               float sc = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16, kWave);
               if constexpr (KF == kKeyE4M3) sc *= kscale;
               sbuf[tq][ub] = sc;
-              if (p.hist && t0 + tq < p.T && pos < pos_lim && pos < (int64_t)len - p.T + 1 + t0 + tq)
+              if (p.hist && t0 + tq < p.T && pos < (int64_t)len - p.T + 1 + t0 + tq)
                 atomicAdd(&lds_hist[tq * kHistBins + (score_key(sc) >> kHistShift)], 1u);
             }
           }
@@ -604,15 +609,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         // store the batch
 #pragma unroll
         for (int ub = 0; ub < RB; ++ub) {
-          const int64_t pos = sub_pos(4 * (u0 + ub) + lg) + lc;
-          if (u0 + ub < n_units && pos < vis_last && pos < pos_lim) {
+          const int64_t pos = 64 * unit_id(u0 + ub) + 16 * lg + lc;
+          if (u0 + ub < n_units && pos < vis_last) {
 #pragma unroll
             for (int tq = 0; tq < TQ; ++tq)
               if (t0 + tq < p.T) p.scores[((int64_t)b * p.T + t0 + tq) * p.Lmax + pos] = sbuf[tq][ub];
           }
         }
       }
-
       __syncthreads();  // all waves done with lds_q (and their histogram updates)
       if (p.hist) {
         for (int tq = 0; tq < TQ; ++tq) {
