@@ -26,7 +26,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdsa.so")
+# (DSA_LIBRARY: another build of the same sources, e.g. a sanitised one)
+LIB_PATH = os.environ.get("DSA_LIBRARY") or os.path.join(_HERE, "libdsa.so")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_MXFP8_E4M3, DSA_FP8_E4M3_T128 = 0, 1, 2, 3, 4
 FORWARD_STAGES = 3

@@ -31,7 +31,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# (DSA_ORACLE_LIBRARY: another build of oracle.c, e.g. a sanitised one)
+_LIB_PATH = os.environ.get("DSA_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 

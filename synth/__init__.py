@@ -35,7 +35,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# (DSA_SYNTH_LIBRARY: another build of gen.c, e.g. a sanitised one)
+_LIB_PATH = os.environ.get("DSA_SYNTH_LIBRARY") or os.path.join(_HERE, "libsynth.so")
 _lib = None
 
 F32, BF16, E4M3, MXE4M3, E4M3T128 = 0, 1, 2, 3, 4
