@@ -770,6 +770,13 @@ void mla_mfma_kernel(MlaParams p) {
   };
 
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // vmask complete (copies may be in flight)
+  // Tiles after the split's last valid entry are skipped: a query that sees
+  // fewer than K positions has an index list ending in -1s (the first
+  // tokens of a fresh prompt), and its split would otherwise run them all.
+  int n_live = 0;
+  for (int t = 0; t < n_tiles; ++t)
+    if (sh.vmask[t] != 0) n_live = t + 1;
+  n_live = __builtin_amdgcn_readfirstlane(n_live);
   // One compact loop over the tiles (the body stays in the instruction
   // cache).  Tile t sits in buffer t % 2.  The rows this lane copies for
   // tile t are entries 64 t + 16 wave + l/8 (+8); they are read one tile
@@ -781,9 +788,9 @@ void mla_mfma_kernel(MlaParams p) {
     // every wave is done with tile t-1, whose buffer is reused), compute tile
     // t while issuing the copy of tile t+1 step by step (a token copy after
     // the last tile).
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int t = 0; t < n_live; ++t) {
       tile_barrier();
-      const TileCopy<false> next(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l, t + 1 < n_tiles);
+      const TileCopy<false> next(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l, t + 1 < n_live);
       pos[0] = s_idx[(t + 2) * kTile + my_row];
       pos[1] = s_idx[(t + 2) * kTile + my_row + 8];
       compute(sh.rows[cur], t * kTile, [&](int k) { next.issue(k); });
@@ -799,7 +806,7 @@ void mla_mfma_kernel(MlaParams p) {
     const int srow = 16 * wave + (l >> 2);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     fp8_decode(sh.rows[0], kscale, wave, l);
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int t = 0; t < n_live; ++t) {
       __syncthreads();
       tile_dma<true>(sh.rows[cur ^ 1], p, pos, seq_row0, wave, l);
       load_kscale(seq_row0 + max(s_idx[(t + 1) * kTile + srow], 0));
