@@ -150,9 +150,8 @@ MlaLayout mla_layout(const dsa_problem* p) {
     const int64_t max_s = std::min<int64_t>(64, (p->top_k + tile - 1) / tile);
     if (env_int("DSA_MLA_SPLITS", 0) > 0) s = env_int("DSA_MLA_SPLITS", 0);
     s = std::max<int64_t>(1, std::min(s, max_s));
-    // each split stages its whole index list in LDS
-    const int64_t cap = dsa::mla_max_rows_per_split();
-    s = std::max<int64_t>(s, (p->top_k + cap - 1) / cap);
+    // (a workgroup stages its index list in LDS chunk after chunk, so only
+    // parallelism sets the splits: many queries need none, and no merge)
     L.rows_per_split = (int)align_up((p->top_k + s - 1) / s, tile);
     L.splits = (p->top_k + L.rows_per_split - 1) / L.rows_per_split;
   }

@@ -106,7 +106,7 @@ hipError_t noalloc_workspace(void** ptr, size_t* bytes);
 // sparse_mla.hip
 bool mla_mfma_supported(const MlaParams& p);
 int mla_row_tile();
-int mla_max_rows_per_split();  // index entries one MFMA-kernel workgroup stages in LDS
+int mla_max_rows_per_split();  // index entries one MFMA-kernel workgroup stages in LDS at a time
 hipError_t launch_mla(const MlaParams& p, bool allow_mfma, hipStream_t stream);
 
 }  // namespace dsa

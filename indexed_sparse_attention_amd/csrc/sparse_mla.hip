@@ -457,8 +457,15 @@ void mla_mfma_kernel(MlaParams p) {
   const bool paged = p.block_table != nullptr;
   const int64_t seq_row0 = paged ? 0 : (int64_t)b * p.Lmax;
   const int32_t* sel = p.topk_idx + (int64_t)bt * p.K;
-  const int j_begin = split * p.rows_per_split;
-  const int n_rows = max(0, min(min(p.K, j_begin + p.rows_per_split) - j_begin, kIdxCap));
+  // The split's entries j_split .. +split_rows go through LDS in chunks of
+  // at most kIdxCap (whole tiles), one after another, with the softmax
+  // state carried across: a split needs no more rows than the host's
+  // parallelism asks for, whatever the LDS holds.
+  const int j_split = split * p.rows_per_split;
+  const int split_rows = max(0, min(p.K, j_split + p.rows_per_split) - j_split);
+  const int n_chunks = max(1, (split_rows + kIdxCap - 1) / kIdxCap);
+  const int chunk_rows = (((split_rows + n_chunks - 1) / n_chunks) + kTile - 1) / kTile * kTile;  // <= kIdxCap
+  int j_begin = j_split, n_rows = 0;  // the current chunk's entries
   const int my_row = 16 * wave + (l >> 3);  // this lane's row of 8-row group 0 (group 1: +8)
   // index entry j of the split -> position (-1: none); the load is
   // unconditional and clamped into the list, so that several of them can be
@@ -468,51 +475,68 @@ void mla_mfma_kernel(MlaParams p) {
     return (j < n_rows && v >= 0 && v < len) ? v : -1;
   };
 
-  // Prologue: every load of the split's index list is issued at once (the
-  // host sizes splits to <= kIdxCap rows); once they land the list is stored
-  // to LDS and the first tile's copy starts (its rows come straight from
-  // registers), with the query loads behind it.  The LDS stores go first:
-  // stored after the copy was issued, they would wait for it to land.
-  constexpr int kPer = kIdxCap / kMlaThreads;
-  int32_t iv[kPer];  // entries tid + 256 k
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) iv[k] = resolve(tid + k * kMlaThreads);
-  if (paged) {
-    // position -> physical row: page table[b][pos / page] (clamped into the
-    // cache), row pos % page within it; every entry's load is issued first
-    const int64_t prow = (int64_t)1 << p.page_shift;
-    const int32_t* btab = p.block_table + (int64_t)b * p.max_pages;
-    int32_t pe[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) pe[k] = btab[min((int64_t)(max(iv[k], 0) >> p.page_shift), (int64_t)p.max_pages - 1)];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int64_t pp = min(max((int64_t)pe[k], (int64_t)0), p.num_pages - 1);
-      iv[k] = iv[k] >= 0 ? (int32_t)(pp * prow + (iv[k] & (prow - 1))) : -1;
-    }
-  }
-  // the list in LDS, padded with -1 through the last tile plus the 2 tiles
-  // whose positions are read ahead
-  const int n_tiles = (n_rows + kTile - 1) / kTile;
-  const int n_pad = (n_tiles + 2) * kTile;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) s_idx[tid + k * kMlaThreads] = iv[k];  // -1 past the list
-  for (int i = kIdxCap + tid; i < n_pad; i += kMlaThreads) s_idx[i] = -1;
   float kscale[NSC] = {};  // e4m3: scales of row 16 wave + l/4 of the tile being copied
   auto load_kscale = [&](int64_t row) {
 #pragma unroll
     for (int i = 0; i < NSC; ++i) kscale[i] = p.kv_scale[row * NSC + i];
   };
-  if (paged) {  // the first tile's rows come back from LDS
+  // Prologue of a chunk: every load of its index list is issued at once;
+  // once they land the list is stored to LDS and the first tile's copy
+  // starts (its rows come straight from registers).  The LDS stores go
+  // first: stored after the copy was issued, they would wait for it to land.
+  // Returns the chunk's tile count.
+  constexpr int kPer = kIdxCap / kMlaThreads;
+  auto load_chunk = [&](int c) -> int {
+    j_begin = j_split + c * chunk_rows;
+    n_rows = max(0, min(chunk_rows, j_split + split_rows - j_begin));
+    int32_t iv[kPer];  // entries tid + 256 k
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) iv[k] = resolve(tid + k * kMlaThreads);
+    if (paged) {
+      // position -> physical row: page table[b][pos / page] (clamped into the
+      // cache), row pos % page within it; every entry's load is issued first
+      const int64_t prow = (int64_t)1 << p.page_shift;
+      const int32_t* btab = p.block_table + (int64_t)b * p.max_pages;
+      int32_t pe[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        pe[k] = btab[min((int64_t)(max(iv[k], 0) >> p.page_shift), (int64_t)p.max_pages - 1)];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int64_t pp = min(max((int64_t)pe[k], (int64_t)0), p.num_pages - 1);
+        iv[k] = iv[k] >= 0 ? (int32_t)(pp * prow + (iv[k] & (prow - 1))) : -1;
+      }
+    }
+    // the list in LDS, padded with -1 through the last tile plus the 2 tiles
+    // whose positions are read ahead
+    const int n_tiles = (n_rows + kTile - 1) / kTile;
+    const int n_pad = (n_tiles + 2) * kTile;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) s_idx[tid + k * kMlaThreads] = iv[k];  // -1 past the list
+    for (int i = kIdxCap + tid; i < n_pad; i += kMlaThreads) s_idx[i] = -1;
+    if (paged) {  // the first tile's rows come back from LDS
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const int32_t pos0[2] = {s_idx[my_row], s_idx[my_row + 8]};
+      tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
+      if constexpr (FP8) load_kscale(max(s_idx[16 * wave + (l >> 2)], 0));
+    } else {
+      const int32_t pos0[2] = {resolve(my_row), resolve(my_row + 8)};
+      tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
+      if constexpr (FP8) load_kscale(seq_row0 + max(resolve(16 * wave + (l >> 2)), 0));
+    }
+    return n_tiles;
+  };
+  // the list is complete in LDS (a bare barrier lets the first tile's copy
+  // stay in flight: __syncthreads() would wait for it); then each tile's
+  // mask of valid rows
+  auto chunk_masks = [&](int n_tiles) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int32_t pos0[2] = {s_idx[my_row], s_idx[my_row + 8]};
-    tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
-    if constexpr (FP8) load_kscale(max(s_idx[16 * wave + (l >> 2)], 0));
-  } else {
-    const int32_t pos0[2] = {resolve(my_row), resolve(my_row + 8)};
-    tile_dma<FP8>(sh.rows[0], p, pos0, seq_row0, wave, l);
-    if constexpr (FP8) load_kscale(seq_row0 + max(resolve(16 * wave + (l >> 2)), 0));
-  }
+    for (int t = wave; t < n_tiles + 2; t += kMlaWaves) {
+      const uint64_t bal = __ballot(s_idx[t * kTile + l] >= 0);
+      if (l == 0) sh.vmask[t] = bal;
+    }
+  };
+  int n_tiles = load_chunk(0);
 
   // query heads h0 + lc, dims 32 ks + 8 lg .. +8  (operand B of QK^T)
   bf16x8 qreg[kKSteps];
@@ -523,13 +547,6 @@ void mla_mfma_kernel(MlaParams p) {
   }
 
   const float zscale = p.scale * 1.4426950408889634f;  // logits in base-2 units
-  // the list is complete in LDS; a bare barrier lets the first tile's copy
-  // stay in flight (__syncthreads() would wait for it)
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int t = wave; t < n_pad / kTile; t += kMlaWaves) {
-    const uint64_t bal = __ballot(s_idx[t * kTile + l] >= 0);
-    if (l == 0) sh.vmask[t] = bal;
-  }
 
   // LDS byte offsets of this lane's operand reads within a tile
   uint32_t a_off[kBlocks][2];  // QK^T operand A: [16-row block][k-step parity], plus 1 KB per 2 k-steps
@@ -769,8 +786,19 @@ void mla_mfma_kernel(MlaParams p) {
     }
   };
 
+  int cur = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+  if (c > 0) {
+    // the last chunk's copies have landed and every wave is done with its
+    // list and tiles before the next list and first tile overwrite them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    n_tiles = load_chunk(c);
+    cur = 0;
+  }
+  chunk_masks(n_tiles);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // vmask complete (copies may be in flight)
-  // Tiles after the split's last valid entry are skipped: a query that sees
+  // Tiles after the chunk's last valid entry are skipped: a query that sees
   // fewer than K positions has an index list ending in -1s (the first
   // tokens of a fresh prompt), and its split would otherwise run them all.
   int n_live = 0;
@@ -782,7 +810,6 @@ void mla_mfma_kernel(MlaParams p) {
   // tile t are entries 64 t + 16 wave + l/8 (+8); they are read one tile
   // ahead, so the copy is issued without an LDS round trip.
   int32_t pos[2] = {s_idx[kTile + my_row], s_idx[kTile + my_row + 8]};
-  int cur = 0;
   if constexpr (!FP8) {
     // Step t: wait for this wave's copy of tile t, barrier (tile t complete;
     // every wave is done with tile t-1, whose buffer is reused), compute tile
@@ -818,6 +845,7 @@ void mla_mfma_kernel(MlaParams p) {
       cur ^= 1;
     }
   }
+  }  // chunks
 
   // ---- write-out ----
   // The owner wave of each head publishes 1 / sum (after every wave's last

@@ -108,6 +108,28 @@ def test_score_work_splits_match_oracle(case, split):
         del os.environ["DSA_SCORE_SPLIT"]
 
 
+@pytest.mark.parametrize("name,kw,splits", [
+    # one split of 2048 rows: two chunks of 1024 through LDS (bf16, e4m3, tile-scaled e4m3)
+    ("decode128k", dict(batch=3, max_seq_len=20000, len_range=(12000, 20000)), 1),
+    ("fp8_1m", dict(batch=2, max_seq_len=16384, len_range=(9000, 16384), top_k=2048), 1),
+    ("mx128k", dict(batch=2, max_seq_len=9000, len_range=(5000, 9000), top_k=2048), 1),
+    # 1600 rows: chunks of 832 and 768, the second ending mid-tile
+    ("decode128k", dict(batch=2, max_seq_len=9000, len_range=(5000, 9000), top_k=1600), 1),
+    # many queries: one split per query by default, no merge
+    ("prefill64k", dict(q_len=128, max_seq_len=2304, len_range=(2304, 2304), top_k=2048), 0),
+])
+def test_attention_index_list_in_chunks(name, kw, splits):
+    # a workgroup whose split holds more entries than its LDS list takes
+    # them in chunks, one after another, with its softmax state carried over
+    w = _case(name, **kw)
+    if splits:
+        os.environ["DSA_MLA_SPLITS"] = str(splits)
+    try:
+        _full_check(w)
+    finally:
+        os.environ.pop("DSA_MLA_SPLITS", None)
+
+
 @pytest.mark.parametrize("name", ["decode8k", "fp8_1m", "mx128k"])
 @pytest.mark.parametrize("split", [0, 2])
 def test_two_tokens_with_fewer_rows_than_tokens(name, split):
