@@ -174,6 +174,13 @@ struct QRegs<TQ, kKeyMX> {
   int sc[TQ][4];   // [token][head tile]: E8M0 scale of this lane's head row and group
 };
 
+// ReLU on the bit pattern: a float with its sign bit set is a negative
+// integer, so max(bits, 0) is x for x > 0 and +0 otherwise (-0 included), in
+// one integer max.  fmaxf(x, 0) costs two float maxes on a matrix-core result
+// (the first quiets a possible signalling NaN), and the epilogue's VALU time
+// rivals the MFMA time in the two-token kernel.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int TQ, int NSLOT, int KF, int MINB, int NT, bool PAGED>
 __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   const WgTrace wg_trace_(p.wg_trace);
@@ -535,6 +542,26 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           }
         }
       }
+      // One workgroup per CU gives a wave 256 arithmetic registers and 256
+      // accumulation registers.  The queries (64 registers a token) are pinned
+      // in the accumulation registers, which the matrix core reads its A
+      // operand from directly: left to itself the compiler ran out of
+      // arithmetic registers, parked them there anyway and copied each back
+      // before every MFMA (1434 copies per batch of two-token prefill), and
+      // kept every MFMA result in one accumulator tile, serialising them.
+      if constexpr (MINB == 1 && NT == 256) {
+#pragma unroll
+        for (int tq = 0; tq < TQ; ++tq)
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) {
+            if constexpr (!FP8) {
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(q.a[tq][ht][ks]));
+            } else {
+              asm volatile("" : "+a"(q.a[tq][ht]));
+            }
+          }
+      }
 
       const bool upper = l >= 32, odd = (lg & 1) != 0;
       for (int u0 = 0; u0 < n_units; u0 += RB) {
@@ -561,9 +588,12 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           for (int st = 0; st < 4; ++st) {
             const int j = (ub * 4 + st) % NSLOT;
             if (live) {
+              // every head tile's MFMA chain first, each into its own
+              // accumulator (the chains overlap in the matrix core), then
+              // the ReLU-weighted head sums
+              f32x4 acc[TQ][4];
 #pragma unroll
               for (int tq = 0; tq < TQ; ++tq) {
-                float sacc = 0.0f;
 #pragma unroll
                 for (int ht = 0; ht < 4; ++ht) {
                   f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -578,9 +608,16 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                     a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[tq][ht], slot[j].v, a, 0, 0, 0,
                                                                          q.sc[tq][ht], 0, slot[j].sc);
                   }
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) sacc = fmaf(w[tq][ht][e], fmaxf(a[e], 0.0f), sacc);
+                  acc[tq][ht] = a;
                 }
+              }
+#pragma unroll
+              for (int tq = 0; tq < TQ; ++tq) {
+                float sacc = 0.0f;
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) sacc = fmaf(w[tq][ht][e], relu_bits(acc[tq][ht][e]), sacc);
                 part[tq][st] = sacc;
               }
             }
