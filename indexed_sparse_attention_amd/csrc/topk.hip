@@ -276,25 +276,37 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) 
 }
 
 // --------------------------------------------------------------------------
-// Row mode: one 1024-thread workgroup per query streams that query's scores
-// once (16 consecutive positions per thread per round, two rounds in flight),
-// compacts the candidates (key bin >= threshold bin) in position order
-// straight into LDS, then refines the threshold and emits there.  No global
-// candidate list, no cross-workgroup synchronisation.  Used when a query's
-// visible range is at most kRowMaxLen positions.
+// Row mode: one 1024-thread workgroup per query.  Each of its 16 waves
+// streams one contiguous range of the query's scores (16 consecutive
+// positions per lane per round, two rounds in flight) and appends its
+// candidates (key bin >= threshold bin) in position order to a list of its
+// own: kWaveCap entries in LDS, then a spill range in the global candidate
+// list that only this wave uses (the slots of its own positions).  No
+// barrier while streaming, and no other wave ever reads a wave's spill.  The
+// refinement histograms and the emit then run over the 16 lists, which in
+// wave order are the candidates in position order: one scan over the waves'
+// counts gives each wave its output offsets.  No cross-workgroup
+// synchronisation.  Used when a query's visible range is at most kRowMaxLen
+// positions.  (A first version compacted each round of the whole workgroup
+// with a block-wide scan, two barriers per 16K positions: 41 us for 8
+// queries of 128K positions.)
 // --------------------------------------------------------------------------
 constexpr int kRowThreads = 1024;
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kRowV = 16;
 constexpr int kRowCap = 6000;  // candidates kept in LDS (struct < 64 KB); the rest spill to the global list
+constexpr int kWaveCap = kRowCap / kRowWaves;  // each wave's share of them
+static_assert(kWaveCap * kRowWaves == kRowCap, "LDS list split evenly over the waves");
 
 struct RowShared {
   uint32_t wave[kRowWaves];
   uint32_t res[2];
+  uint32_t gt[kRowWaves], eq[kRowWaves];  // per wave: candidates above / equal to the K-th key
   uint32_t sub[kHistBins];
   uint32_t key[kRowCap];
   uint32_t pos[kRowCap];
 };
+
 
 __device__ __forceinline__ uint32_t row_incl_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
   const int wave = threadIdx.x / kWave, l = lane_id();
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   const WgTrace wg_trace_(p.wg_trace);
   extern __shared__ __attribute__((aligned(16))) uint8_t row_lds[];
   RowShared& sh = *(RowShared*)row_lds;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
   const int bt = blockIdx.x, b = bt / p.T, t = bt % p.T;
   const int len = filled_rows(p.seq_lens[b], p.Lmax, p.len_sub);
   const int64_t vis = max((int64_t)0, (int64_t)len - p.T + 1 + t);
@@ -374,14 +386,23 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   row_threshold_bin<kHistBins>(p.hist + (int64_t)bt * kHistBins, (uint32_t)K, sh.wave, sh.res, &bin, &above);
   clear_query_hist(p, bt, kRowThreads);
 
-  // 2. one pass over the scores: candidates in position order into LDS
+  // 2. each wave streams its range [lo, hi) of the scores into its own list,
+  // in rounds of 1024 positions.  Ranges are multiples of 16 positions (a
+  // lane's share of a round, so vector loads stay 16-byte aligned) and as
+  // short as 16 equal ranges allow: a wave never holds more candidates than
+  // positions, so a query that sees little more than K positions fits its
+  // lists in LDS.
+  constexpr int kRound = kWave * kRowV;
+  const int64_t span = (vis + kRowWaves * kRowV - 1) / (kRowWaves * kRowV) * kRowV;
+  const int64_t lo = min((int64_t)wave * span, vis), hi = min(lo + span, vis);
   const float* row = p.scores + (int64_t)bt * p.Lmax;
-  uint2* spill = p.cand + (int64_t)bt * p.Lmax;  // candidates beyond kRowCap, in order
+  uint32_t* lkey = sh.key + wave * kWaveCap;
+  uint32_t* lpos = sh.pos + wave * kWaveCap;
+  uint2* spill = p.cand + (int64_t)bt * p.Lmax + lo;  // entries kWaveCap.. of this wave's list
   const bool vec_ok = (((uintptr_t)row) & 15) == 0;
-  constexpr int kRound = kRowThreads * kRowV;
   auto load_round = [&](int64_t base, float (&v)[kRowV]) {
-    const int64_t s0 = base + (int64_t)tid * kRowV;
-    if (vec_ok && s0 + kRowV <= vis) {
+    const int64_t s0 = base + (int64_t)l * kRowV;
+    if (vec_ok && s0 + kRowV <= hi) {
 #pragma unroll
       for (int j = 0; j < kRowV; j += 4) {
         const f32x4 x = *(const f32x4*)(row + s0 + j);
@@ -392,57 +413,55 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < kRowV; ++j) v[j] = (s0 + j < vis) ? row[s0 + j] : 0.0f;
+      for (int j = 0; j < kRowV; ++j) v[j] = (s0 + j < hi) ? row[s0 + j] : 0.0f;
     }
   };
-  uint32_t N = 0;
-  float cur[kRowV], nxt[kRowV];
-  load_round(0, cur);
-  for (int64_t base = 0; base < vis; base += kRound) {
-    if (base + kRound < vis) load_round(base + kRound, nxt);
-    const int64_t s0 = base + (int64_t)tid * kRowV;
+  uint32_t n = 0;  // this wave's list length (wave-uniform)
+  float cur[kRowV], nxt[kRowV];  // the round being compacted and the next one, in flight
+  if (lo < hi) load_round(lo, cur);
+  for (int64_t base = lo; base < hi; base += kRound) {
+    if (base + kRound < hi) load_round(base + kRound, nxt);
+    const int64_t s0 = base + (int64_t)l * kRowV;
     uint32_t key[kRowV];
     bool f[kRowV];
     uint32_t cnt = 0;
 #pragma unroll
     for (int j = 0; j < kRowV; ++j) {
       key[j] = score_key(cur[j]);
-      f[j] = (s0 + j < vis) && ((key[j] >> kHistShift) >= bin);
+      f[j] = (s0 + j < hi) && ((key[j] >> kHistShift) >= bin);
       cnt += f[j] ? 1u : 0u;
     }
-    uint32_t total;
-    uint32_t o = N + row_incl_scan(cnt, sh.wave, &total) - cnt;
+    const uint32_t incl = wave_incl_scan(cnt);
+    uint32_t o = n + incl - cnt;
 #pragma unroll
     for (int j = 0; j < kRowV; ++j) {
       if (f[j]) {
-        if (o < (uint32_t)kRowCap) {
-          sh.key[o] = key[j];
-          sh.pos[o] = (uint32_t)(s0 + j);
+        if (o < (uint32_t)kWaveCap) {
+          lkey[o] = key[j];
+          lpos[o] = (uint32_t)(s0 + j);
         } else {
-          spill[o - kRowCap] = make_uint2(key[j], (uint32_t)(s0 + j));
+          spill[o - kWaveCap] = make_uint2(key[j], (uint32_t)(s0 + j));
         }
         ++o;
       }
     }
-    N += total;
+    n += __shfl(incl, kWave - 1, kWave);
 #pragma unroll
     for (int j = 0; j < kRowV; ++j) cur[j] = nxt[j];
   }
-  if (N > (uint32_t)kRowCap) {  // spilled candidates are read back by other waves
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-  auto key_at = [&](uint32_t n) -> uint32_t { return n < (uint32_t)kRowCap ? sh.key[n] : spill[n - kRowCap].x; };
-  auto pos_at = [&](uint32_t n) -> uint32_t { return n < (uint32_t)kRowCap ? sh.pos[n] : spill[n - kRowCap].y; };
+  n = __builtin_amdgcn_readfirstlane(n);
+  // this wave's spilled entries are read back by this wave only: its own
+  // stores complete before its loads
+  if (n > (uint32_t)kWaveCap) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  auto key_at = [&](uint32_t i) -> uint32_t { return i < (uint32_t)kWaveCap ? lkey[i] : spill[i - kWaveCap].x; };
+  auto pos_at = [&](uint32_t i) -> uint32_t { return i < (uint32_t)kWaveCap ? lpos[i] : spill[i - kWaveCap].y; };
 
   const uint32_t need = (uint32_t)K - above;
   // 3. refine: next 12 key bits among keys in `bin`, then the last 8
   for (int i = tid; i < kHistBins; i += kRowThreads) sh.sub[i] = 0;
   __syncthreads();
-  for (uint32_t n = tid; n < N; n += kRowThreads) {
-    const uint32_t k = key_at(n);
+  for (uint32_t i = l; i < n; i += kWave) {
+    const uint32_t k = key_at(i);
     if ((k >> kHistShift) == bin) atomicAdd(&sh.sub[(k >> 8) & 0xFFFu], 1u);
   }
   __syncthreads();
@@ -452,8 +471,8 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   const uint32_t prefix24 = (bin << 12) | bin2;
   for (int i = tid; i < 256; i += kRowThreads) sh.sub[i] = 0;
   __syncthreads();
-  for (uint32_t n = tid; n < N; n += kRowThreads) {
-    const uint32_t k = key_at(n);
+  for (uint32_t i = l; i < n; i += kWave) {
+    const uint32_t k = key_at(i);
     if ((k >> 8) == prefix24) atomicAdd(&sh.sub[k & 0xFFu], 1u);
   }
   __syncthreads();
@@ -462,35 +481,55 @@ __global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
   const uint32_t tau = (prefix24 << 8) | bin3;
   const uint32_t take_ties = need2 - above3;
 
-  // 4. emit in position order (E consecutive candidates per thread)
-  constexpr int E = 4;
+  // 4. emit in position order: each wave's counts above / at tau, a scan
+  // over the waves, then each wave writes its own entries (E consecutive
+  // entries per lane) at their ranks
+  uint32_t gt_w = 0, eq_w = 0;
+  for (uint32_t i = l; i < n; i += kWave) {
+    const uint32_t k = key_at(i);
+    gt_w += k > tau ? 1u : 0u;
+    eq_w += k == tau ? 1u : 0u;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    gt_w += __shfl_xor(gt_w, o, kWave);
+    eq_w += __shfl_xor(eq_w, o, kWave);
+  }
+  if (l == 0) {
+    sh.gt[wave] = gt_w;
+    sh.eq[wave] = eq_w;
+  }
+  __syncthreads();
   uint32_t gt_seen = 0, ties_seen = 0;
-  for (uint32_t n0 = 0; n0 < N; n0 += kRowThreads * E) {
-    const uint32_t nb = n0 + (uint32_t)tid * E;
+  for (int w = 0; w < wave; ++w) {
+    gt_seen += sh.gt[w];
+    ties_seen += sh.eq[w];
+  }
+  constexpr int E = 4;
+  for (uint32_t i0 = 0; i0 < n; i0 += kWave * E) {
+    const uint32_t ib = i0 + (uint32_t)l * E;
     uint32_t k[E];
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      k[e] = (nb + e < N) ? key_at(nb + e) : 0u;
-      gt += (nb + e < N && k[e] > tau) ? 1u : 0u;
-      eq += (nb + e < N && k[e] == tau) ? 1u : 0u;
+      k[e] = (ib + e < n) ? key_at(ib + e) : 0u;
+      gt += (ib + e < n && k[e] > tau) ? 1u : 0u;
+      eq += (ib + e < n && k[e] == tau) ? 1u : 0u;
     }
-    uint32_t eq_tot, gt_tot;
-    uint32_t rank = ties_seen + row_incl_scan(eq, sh.wave, &eq_tot) - eq;
-    const uint32_t gt_before = gt_seen + row_incl_scan(gt, sh.wave, &gt_tot) - gt;
-    uint32_t o = gt_before + min(rank, take_ties);
+    const uint32_t eq_incl = wave_incl_scan(eq), gt_incl = wave_incl_scan(gt);
+    uint32_t rank = ties_seen + eq_incl - eq;
+    uint32_t o = gt_seen + (gt_incl - gt) + min(rank, take_ties);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (nb + e >= N) break;
+      if (ib + e >= n) break;
       bool sel = k[e] > tau;
       if (k[e] == tau) sel = rank++ < take_ties;
       if (sel) {
-        if (o < (uint32_t)K) out[o] = (int32_t)pos_at(nb + e);
+        if (o < (uint32_t)K) out[o] = (int32_t)pos_at(ib + e);
         ++o;
       }
     }
-    gt_seen += gt_tot;
-    ties_seen += eq_tot;
+    gt_seen += __shfl(gt_incl, kWave - 1, kWave);
+    ties_seen += __shfl(eq_incl, kWave - 1, kWave);
   }
   if (tid == 0 && p.topk_count) p.topk_count[bt] = K;
 }
@@ -500,7 +539,11 @@ bool select_row_mode(const TopkParams& p) {
   const char* e = getenv("DSA_TOPK_MODE");
   if (e && strcmp(e, "row") == 0) return true;
   if (e && strcmp(e, "chunk") == 0) return false;
-  return p.Lmax <= kRowMaxLen && (int64_t)p.B * p.T >= 512;
+  // one workgroup per query when the queries fill the GPU, or when they are
+  // short enough that one workgroup streams a row faster than the two-kernel
+  // chunked path finishes (32 queries of 8K: 15.9 against 18.0 us; 8 of
+  // 128K: 30.9 against 18.0 us)
+  return p.Lmax <= kRowMaxLen && ((int64_t)p.B * p.T >= 512 || p.Lmax <= 16384);
 }
 
 hipError_t launch_select(const TopkParams& p_in, hipStream_t stream) {

@@ -54,5 +54,5 @@ def test_trace_stamps_every_workgroup_once(name, kw, kinds):
 
 def test_trace_skips_launches_past_its_slots():
     w = synth.make("decode128k", batch=2, max_seq_len=9000, len_range=(5000, 9000))
-    _, tr = _traced(w, 4)  # every launch here has more than 4 workgroups
+    _, tr = _traced(w, 1)  # every launch here has more than one workgroup
     assert not tr.any()
