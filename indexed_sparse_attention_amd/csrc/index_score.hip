@@ -717,12 +717,13 @@ static int env_int(const char* name, int dflt) {
 // Launch shape: DSA_SCORE_VARIANT selects the bf16 key-prefetch depth,
 // tokens per segment and occupancy (0, the default: one token, rings of 4
 // sub-tiles, two workgroups per CU, so two waves per SIMD interleave their
-// loads and MFMAs; two tokens and one workgroup per CU when there are
-// several query tokens.  1: rings of 8 sub-tiles at one per CU; 2: 8 waves;
-// 3 / 4: two / four tokens), DSA_SCORE_WGS_PER_CU overrides the workgroups
-// per CU and DSA_SCORE_WGS the total.  (Measured at the 128K decode shape:
-// variant 0 at 2/CU streams the keys about 4 % faster than variant 1 at
-// 1/CU.)
+// loads and MFMAs, or for short rows rings of 8 at one workgroup per CU;
+// two tokens and one workgroup per CU when there are several query tokens.
+// 1: rings of 8 sub-tiles at one per CU; 2: 8 waves; 3 / 4: two / four
+// tokens; 5: rings of 4 at two per CU whatever the rows), and
+// DSA_SCORE_WGS_PER_CU overrides the workgroups per CU and DSA_SCORE_WGS
+// the total.  (Measured at the 128K decode shape: variant 0 at 2/CU streams
+// the keys about 5 % faster than variant 1 at 1/CU.)
 hipError_t launch_score(const ScoreParams& p_in, bool allow_mfma, int num_cus, hipStream_t stream,
                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   ScoreParams p = p_in;
@@ -740,14 +741,25 @@ hipError_t launch_score(const ScoreParams& p_in, bool allow_mfma, int num_cus, h
         case 2: launch_mfma<1, 4, kKeyBF16, 1, 512>(p, grid, stream, ev_start, ev_stop); break;
         case 3: launch_mfma<2, 4, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
         case 4: launch_mfma<4, 4, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
+        case 5: launch_mfma<1, 4, kKeyBF16, 2>(p, 2 * num_cus, stream, ev_start, ev_stop); break;
         default:
           // several query tokens: two per segment, so each key tile feeds twice
           // the MFMAs (12 % faster at 4096 tokens over 64K keys; four tokens
           // need one workgroup per CU and were slower)
-          if (p.T >= 2)
+          if (p.T >= 2) {
             launch_mfma<2, 4, kKeyBF16, 1>(p, num_cus, stream, ev_start, ev_stop);
-          else
-            launch_mfma<1, 4, kKeyBF16, 2>(p, grid, stream, ev_start, ev_stop);
+          } else {
+            // one token per sequence: two workgroups per CU, unless each
+            // would stream fewer than 16 units (the rows are short and the
+            // start-up dominates): then one per CU with 8-deep rings (32
+            // sequences of 8K: 22.4 against 25.3 us; 8 of 128K: 47.1
+            // against 49.7 us the other way round)
+            const int64_t est_units = (int64_t)p.B * (p.Lmax / 64 + 16);
+            if (est_units < (int64_t)16 * grid)
+              launch_mfma<1, 8, kKeyBF16, 1>(p, num_cus, stream, ev_start, ev_stop);
+            else
+              launch_mfma<1, 4, kKeyBF16, 2>(p, grid, stream, ev_start, ev_stop);
+          }
           break;
       }
     } else if (p.k_dtype == kE4M3) {

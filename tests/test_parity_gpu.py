@@ -149,6 +149,19 @@ def test_two_tokens_with_fewer_rows_than_tokens(name, split):
     assert got["topk_idx"][1, 1, 0] == 0 and np.all(got["topk_idx"][1, 1, 1:] == -1)
 
 
+@pytest.mark.parametrize("variant", [1, 5])
+def test_one_token_score_kernels(variant):
+    # one query token per sequence: the deep-ring kernel at one workgroup
+    # per CU (the default for short rows) and the kernel at two per CU (the
+    # default for long rows), each forced on a ragged decode batch
+    w = _case("decode128k", batch=3, max_seq_len=20000, len_range=(12000, 20000))
+    os.environ["DSA_SCORE_VARIANT"] = str(variant)
+    try:
+        _full_check(w)
+    finally:
+        del os.environ["DSA_SCORE_VARIANT"]
+
+
 def test_entry_points_separately():
     w = _case("decode128k", batch=2, max_seq_len=9000, len_range=(5000, 9000), top_k=1024)
     d = G.to_device(w)
