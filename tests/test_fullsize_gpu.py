@@ -1,10 +1,11 @@
 """Every workload at its full size, in the launch configuration the benchmark
 uses (dsa_forward with the default kernel choice), checked three ways:
 
-  * against the CPU oracle: every query of the decode workloads, and 65
-    tokens spread over the 4096-token prefill chunk (first, last, every
-    64th): scores bit for bit over the visible range, Top-K sets and counts
-    exactly, attention within the stated tolerance;
+  * against the CPU oracle: every query of the decode workloads, and the
+    first, last and every 64th token of the 4096-token prefill chunk and of
+    the 8192-token fresh prompt (65 and 129 tokens): scores bit for bit over
+    the visible range, Top-K sets and counts exactly, attention within the
+    stated tolerance;
   * the Top-K defining property for every query against the GPU's own
     scores: count = min(K, vis), only visible positions, every unselected
     score below the K-th or tied with it at a higher position; positions
@@ -64,8 +65,12 @@ def check_topk_property(w, scores, idx, cnt, chunk=256):
             # (checked before the scatter below, which needs in-range indices)
             assert torch.all(~valid | ((sel_idx >= 0) & (sel_idx < L))), f"a selected index is out of range (b={b})"
             visible = pos[None, :] < vis[:, None]
-            sel = torch.zeros_like(visible)
-            sel.scatter_(1, torch.where(valid, sel_idx, 0), valid)
+            # padding entries scatter into a spare last column: written to a
+            # real column, their False could land after a True there (the
+            # order of duplicate scatter writes is undefined)
+            sel = torch.zeros((t1 - t0, L + 1), dtype=torch.bool, device=dev)
+            sel.scatter_(1, torch.where(valid, sel_idx, L), torch.ones_like(valid))
+            sel = sel[:, :L]
             assert torch.all(~sel | visible), f"an invisible position is selected (b={b})"
             neg = torch.tensor(float("-inf"), device=dev)
             tau = torch.where(sel, S, torch.tensor(float("inf"), device=dev)).amin(dim=1)
@@ -78,7 +83,7 @@ def check_topk_property(w, scores, idx, cnt, chunk=256):
             assert torch.all(~has | (first_rest_tie > last_sel_tie)), f"a tie at the K-th score went to a higher position (b={b})"
 
 
-@pytest.mark.parametrize("name", ["decode8k", "decode128k", "prefill64k", "fp8_1m", "mx128k"])
+@pytest.mark.parametrize("name", ["decode8k", "decode128k", "prefill64k", "fp8_1m", "mx128k", "prompt8k"])
 def test_full_size_workload(name):
     w = synth.make(name)
     print(f"\n[full] {name} B={w.batch} T={w.q_len} Lmax={w.max_seq_len} K={w.top_k}", flush=True)
