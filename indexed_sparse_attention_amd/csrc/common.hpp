@@ -86,6 +86,23 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Stores that write through the L2 to memory (device-scope coherent: the
+// `sc1` policy), for results a later kernel reads.  The eight XCDs' L2s are
+// not coherent with one another, so the release at a kernel's end writes
+// every line its ordinary stores left dirty back to memory before the next
+// kernel may start: megabytes of results then leave after the last
+// workgroup has finished.  Stored through, they leave while the kernel still
+// runs.
+__device__ __forceinline__ void store_through(void* p, i32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_through(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_through(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Stamps a workgroup's start (construction) and its first thread's exit
 // (destruction) into a wg_trace region; nothing when the region is null.
 struct WgTrace {

@@ -858,11 +858,12 @@ void mla_mfma_kernel(MlaParams p) {
     const int h = h0 + lc;
     if (p.splits == 1) {
       if (p.lse && lg == 0)
-        p.lse[(int64_t)bt * p.H + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+        store_through(&p.lse[(int64_t)bt * p.H + h],
+                      l_run > 0.0f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY);
     } else if (lg == 0) {
       const int64_t slot = ((int64_t)split * p.B * p.T + bt) * p.H + h;
-      p.part_ml[slot * 2] = m_run;
-      p.part_ml[slot * 2 + 1] = l_run;
+      store_through(&p.part_ml[slot * 2], m_run);
+      store_through(&p.part_ml[slot * 2 + 1], l_run);
     }
   }
   if (p.splits == 1 && p.out_dtype == kF32) {
@@ -873,8 +874,9 @@ void mla_mfma_kernel(MlaParams p) {
       const int64_t ooff = ((int64_t)bt * p.H + h) * kDv + 128 * wave + 4 * lg;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        *(f32x4*)((float*)p.out + ooff + 16 * db) =
-            f32x4{o[hb][db][0] * inv, o[hb][db][1] * inv, o[hb][db][2] * inv, o[hb][db][3] * inv};
+        store_through((float*)p.out + ooff + 16 * db,
+                      __builtin_bit_cast(i32x4, f32x4{o[hb][db][0] * inv, o[hb][db][1] * inv,
+                                                      o[hb][db][2] * inv, o[hb][db][3] * inv}));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy into LDS outlives the workgroup
     return;
@@ -884,7 +886,8 @@ void mla_mfma_kernel(MlaParams p) {
   // LDS (in the last tile's buffer, free after the barrier above) and written
   // back as whole rows, one 1 KB row per wave instruction.  Written straight from the accumulator
   // layout, every store instruction would cover sixteen 32-byte pieces of
-  // sixteen rows.
+  // sixteen rows.  (Results leave through the L2: the partials are the
+  // merge's input, tens of MB at long contexts.)
   uint8_t* stage = sh.rows[cur ^ 1];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
@@ -903,7 +906,7 @@ void mla_mfma_kernel(MlaParams p) {
 #pragma unroll
   for (int r = 0; r < kHeadsPerWG / kMlaWaves; ++r) {
     const int hl = kMlaWaves * r + wave;
-    *(i32x4*)(dst + (int64_t)hl * kDv + 8 * l) = *(const i32x4*)(stage + hl * kStageRow + 16 * l);
+    store_through(dst + (int64_t)hl * kDv + 8 * l, *(const i32x4*)(stage + hl * kStageRow + 16 * l));
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy into LDS outlives the workgroup
 }
