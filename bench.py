@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--wg-trace", action="store_true",
                     help="time one eager step's workgroups (start and end of each, per kernel) with every stage "
                          "in one launch, print the spread, then exit")
+    ap.add_argument("--wg-trace-dump", default=None, metavar="FILE.npy",
+                    help="with --wg-trace: also save the raw stamps, int64 [kind][workgroup][start, end] "
+                         "in 100 MHz clock ticks (0: not stamped)")
     return ap.parse_args()
 
 
@@ -196,10 +199,13 @@ def algorithmic_bytes(w):
             "score_kernel": score_kernel, "attention": attention, "attention_flops": attn_flops}
 
 
-def wg_trace_report(dsa, torch, np, step, workload, w):
-    """One eager step with per-workgroup clock stamps (the library's
-    workgroup trace, 100 MHz): for each kernel, when its workgroups started
-    and finished relative to its first start, and how far apart."""
+def wg_trace_report(dsa, torch, np, step, workload, w, dump=None):
+    """Per-workgroup clock stamps (the library's workgroup trace, 100 MHz)
+    of one eager step: for each kernel, when its workgroups started and
+    finished relative to its first start, how far apart, and the gap between
+    the previous kernel's last finish and its first start.  The stage events
+    come from a separate eager step: recorded between the stages they would
+    widen the gaps."""
     slots = 1 << 17
     kinds = dsa.TRACE_KINDS
     buf = torch.zeros(len(kinds) * slots * 2, dtype=torch.int64, device="cuda:0")
@@ -207,21 +213,28 @@ def wg_trace_report(dsa, torch, np, step, workload, w):
     for e in evs:
         e.record()
     torch.cuda.synchronize()
+    step(0, stage_events=evs)
+    torch.cuda.synchronize()
+    stage_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(dsa.FORWARD_STAGES)]
     dsa.set_workgroup_trace(buf, slots)
     try:
-        step(0, stage_events=evs)
+        step(0)
         torch.cuda.synchronize()
     finally:
         dsa.set_workgroup_trace(None)
-    stage_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(dsa.FORWARD_STAGES)]
     tr = buf.view(len(kinds), slots, 2).cpu().numpy()
+    if dump:
+        np.save(dump, tr)
     print(f"# workgroup timeline, workload {workload}: B={w.batch} T={w.q_len} Lmax={w.max_seq_len} "
           f"K={w.top_k}, one eager step, every stage in one launch")
-    print(f"# stage events (us): scores {stage_us[0]:.1f}  topk {stage_us[1]:.1f}  attention {stage_us[2]:.1f}")
+    print(f"# stage events of another eager step (us): scores {stage_us[0]:.1f}  topk {stage_us[1]:.1f}  "
+          f"attention {stage_us[2]:.1f}")
     print("# per kernel, in us from its first workgroup's start: the last start, the finish times' "
-          "quantiles, and the busy time (end - start) per workgroup")
+          "quantiles, the busy time (end - start) per workgroup, and the gap from the previous "
+          "kernel's last finish to this one's first start")
     print(f"{'kernel':16s} {'wgs':>6s} {'last_start':>10s} {'end_min':>8s} {'end_p50':>8s} {'end_p90':>8s} "
-          f"{'end_max':>8s} {'spread':>8s} {'busy_p50':>8s} {'busy_max':>8s}")
+          f"{'end_max':>8s} {'spread':>8s} {'busy_p50':>8s} {'busy_max':>8s} {'gap':>6s}")
+    prev_end = None
     for k, name in enumerate(kinds):
         st, en = tr[k, :, 0], tr[k, :, 1]
         m = (st != 0) & (en != 0)
@@ -230,10 +243,12 @@ def wg_trace_report(dsa, torch, np, step, workload, w):
         st, en = st[m].astype(np.float64), en[m].astype(np.float64)
         t0 = st.min()
         s_us, e_us, busy = (st - t0) / 100.0, (en - t0) / 100.0, (en - st) / 100.0
+        gap = "" if prev_end is None else f"{(t0 - prev_end) / 100.0:6.2f}"
+        prev_end = en.max()
         q = lambda a, f: float(np.quantile(a, f))
         print(f"{name:16s} {int(m.sum()):6d} {s_us.max():10.2f} {e_us.min():8.2f} {q(e_us, .5):8.2f} "
               f"{q(e_us, .9):8.2f} {e_us.max():8.2f} {e_us.max() - e_us.min():8.2f} {q(busy, .5):8.2f} "
-              f"{busy.max():8.2f}")
+              f"{busy.max():8.2f} {gap:>6s}")
 
 
 def cpu_model():
@@ -350,7 +365,7 @@ def main():
     ref_out = outs["out"].clone()
 
     if args.wg_trace:
-        wg_trace_report(dsa, torch, np, step, args.workload, w)
+        wg_trace_report(dsa, torch, np, step, args.workload, w, args.wg_trace_dump)
         return
 
     graphs = None
