@@ -381,9 +381,13 @@ dsa_status dsa_forward_paged(const dsa_problem* p, const dsa_paging* pg, const v
 
 /*
  * Diagnostics.  dsa_kernel_choice() names the kernels dsa_forward would launch
- * for p ("mfma" or "generic" per step) into buf (NUL-terminated, truncated to
- * len).  While the environment variable DSA_FORCE_GENERIC is set to a value
- * other than "0", every call uses the portable SIMT kernels for every step.
+ * for p into buf (NUL-terminated, truncated to len): "mfma" or "generic" per
+ * step, the score launch's shape and workgroup count, the Top-K mode, the
+ * attention's row splits, and the token tile (0: one pass).  A call in token
+ * tiles is described by its tile's launches.  Returns 0, or -1 for an invalid
+ * problem or buffer.  While the environment variable DSA_FORCE_GENERIC is set
+ * to a value other than "0", every call uses the portable SIMT kernels for
+ * every step.
  */
 int dsa_kernel_choice(const dsa_problem* p, char* buf, size_t len);
 

@@ -281,8 +281,8 @@ def sparse_mla_workspace_size(p: Problem) -> int:
 
 
 def kernel_choice(p: Problem) -> str:
-    buf = ctypes.create_string_buffer(256)
-    load_library().dsa_kernel_choice(ctypes.byref(p), buf, 256)
+    buf = ctypes.create_string_buffer(512)
+    load_library().dsa_kernel_choice(ctypes.byref(p), buf, 512)
     return buf.value.decode()
 
 

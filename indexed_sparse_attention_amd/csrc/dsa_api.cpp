@@ -881,10 +881,22 @@ int dsa_kernel_choice(const dsa_problem* p, char* buf, size_t len) {
     snprintf(buf, len, "invalid");
     return -1;
   }
-  const MlaLayout L = mla_layout(p);
-  snprintf(buf, len, "score=%s topk=radix-select mla=%s splits=%d rows_per_split=%d select_chunk=%d",
-           score_uses_mfma(p) ? "mfma" : "generic", mla_uses_mfma(p) ? "mfma" : "generic", L.splits,
-           L.rows_per_split, topk_layout(p).chunk);
+  // a call in token tiles launches each stage per tile: name the tile's launches
+  const int n = tile_tokens(p, fwd_bytes);
+  const dsa_problem t = n ? tile_problem(p, n) : *p;
+  char score[160] = "generic";
+  if (score_uses_mfma(&t))
+    dsa::score_launch_desc(score_params(&t, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), num_cus(),
+                           score, sizeof score);
+  dsa::TopkParams tk{};
+  tk.B = t.batch;
+  tk.T = t.q_len;
+  tk.K = t.top_k;
+  tk.Lmax = t.max_seq_len;
+  const MlaLayout L = mla_layout(&t);
+  snprintf(buf, len, "score=%s topk=%s mla=%s splits=%d rows_per_split=%d select_chunk=%d tile_tokens=%d", score,
+           dsa::select_row_mode(tk) ? "radix-select, one workgroup per query" : "radix-select, chunks + emit",
+           mla_uses_mfma(&t) ? "mfma" : "generic", L.splits, L.rows_per_split, topk_layout(&t).chunk, n);
   return 0;
 }
 

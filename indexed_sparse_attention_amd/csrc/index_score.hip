@@ -724,56 +724,77 @@ static int env_int(const char* name, int dflt) {
 // DSA_SCORE_WGS_PER_CU overrides the workgroups per CU and DSA_SCORE_WGS
 // the total.  (Measured at the 128K decode shape: variant 0 at 2/CU streams
 // the keys about 5 % faster than variant 1 at 1/CU.)
+// The matrix-core kernel and grid launch_score takes for p (shared with the
+// diagnostics that name the launch).
+enum ScoreKernel { kSkBf16R8, kSkBf16W8, kSkBf16T2, kSkBf16T4, kSkBf16R4, kSkE4m3T1, kSkE4m3T2, kSkMxT1, kSkMxT2 };
+struct ScoreLaunch {
+  ScoreKernel kernel;
+  int grid;
+};
+
+static ScoreLaunch score_launch_plan(const ScoreParams& p, int num_cus) {
+  const int variant = env_int("DSA_SCORE_VARIANT", 0);
+  // two workgroups per CU (bf16 variants 1 and 2: one, with 8-deep rings or 8 waves)
+  const int per_cu = (p.k_dtype != kBF16 || variant == 0) ? 2 : 1;
+  int grid = max(1, env_int("DSA_SCORE_WGS_PER_CU", per_cu)) * num_cus;
+  if (env_int("DSA_SCORE_WGS", 0) > 0) grid = env_int("DSA_SCORE_WGS", 0);
+  if (p.k_dtype == kBF16) {
+    switch (variant) {
+      case 1: return {kSkBf16R8, grid};
+      case 2: return {kSkBf16W8, grid};
+      case 3: return {kSkBf16T2, grid};
+      case 4: return {kSkBf16T4, grid};
+      case 5: return {kSkBf16R4, 2 * num_cus};
+      default:
+        // several query tokens: two per segment, so each key tile feeds twice
+        // the MFMAs (12 % faster at 4096 tokens over 64K keys; four tokens
+        // need one workgroup per CU and were slower)
+        if (p.T >= 2) return {kSkBf16T2, num_cus};
+        // one token per sequence: two workgroups per CU, unless each would
+        // stream fewer than 16 units (the rows are short and the start-up
+        // dominates): then one per CU with 8-deep rings (32 sequences of 8K:
+        // 22.4 against 25.3 us; 8 of 128K: 47.1 against 49.7 us the other
+        // way round)
+        if ((int64_t)p.B * (p.Lmax / 64 + 16) < (int64_t)16 * grid) return {kSkBf16R8, num_cus};
+        return {kSkBf16R4, grid};
+    }
+  }
+  if (p.k_dtype == kE4M3) return {p.T == 1 ? kSkE4m3T1 : kSkE4m3T2, grid};
+  // (two tokens with their group scales need more than half the registers:
+  // one workgroup per CU)
+  return p.T == 1 ? ScoreLaunch{kSkMxT1, grid} : ScoreLaunch{kSkMxT2, num_cus};
+}
+
+int score_launch_desc(const ScoreParams& p, int num_cus, char* buf, size_t len) {
+  if (!score_mfma_supported(p)) return snprintf(buf, len, "generic");
+  // keys, query tokens per segment, key ring depth (16-row sub-tiles), waves per workgroup
+  static const char* const names[] = {
+      "bf16 keys, 1 token, ring 8, 4 waves",  "bf16 keys, 1 token, ring 4, 8 waves",
+      "bf16 keys, 2 tokens, ring 4, 4 waves", "bf16 keys, 4 tokens, ring 4, 4 waves",
+      "bf16 keys, 1 token, ring 4, 4 waves",  "e4m3 keys, 1 token, ring 8, 4 waves",
+      "e4m3 keys, 2 tokens, ring 4, 4 waves", "mxfp8 keys, 1 token, ring 8, 4 waves",
+      "mxfp8 keys, 2 tokens, ring 4, 4 waves"};
+  const ScoreLaunch l = score_launch_plan(p, num_cus);
+  return snprintf(buf, len, "mfma(%s; %d workgroups)", names[l.kernel], l.grid);
+}
+
 hipError_t launch_score(const ScoreParams& p_in, bool allow_mfma, int num_cus, hipStream_t stream,
                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   ScoreParams p = p_in;
   p.split_mode = env_int("DSA_SCORE_SPLIT", 0);  // (tests run both splits on small problems)
   p.wg_trace = nullptr;
   if (allow_mfma && score_mfma_supported(p)) {
-    const int variant = env_int("DSA_SCORE_VARIANT", 0);
-    // two workgroups per CU (bf16 variants 1 and 2: one, with 8-deep rings or 8 waves)
-    const int per_cu = (p.k_dtype != kBF16 || variant == 0) ? 2 : 1;
-    int grid = max(1, env_int("DSA_SCORE_WGS_PER_CU", per_cu)) * num_cus;
-    if (env_int("DSA_SCORE_WGS", 0) > 0) grid = env_int("DSA_SCORE_WGS", 0);
-    if (p.k_dtype == kBF16) {
-      switch (variant) {
-        case 1: launch_mfma<1, 8, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
-        case 2: launch_mfma<1, 4, kKeyBF16, 1, 512>(p, grid, stream, ev_start, ev_stop); break;
-        case 3: launch_mfma<2, 4, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
-        case 4: launch_mfma<4, 4, kKeyBF16, 1>(p, grid, stream, ev_start, ev_stop); break;
-        case 5: launch_mfma<1, 4, kKeyBF16, 2>(p, 2 * num_cus, stream, ev_start, ev_stop); break;
-        default:
-          // several query tokens: two per segment, so each key tile feeds twice
-          // the MFMAs (12 % faster at 4096 tokens over 64K keys; four tokens
-          // need one workgroup per CU and were slower)
-          if (p.T >= 2) {
-            launch_mfma<2, 4, kKeyBF16, 1>(p, num_cus, stream, ev_start, ev_stop);
-          } else {
-            // one token per sequence: two workgroups per CU, unless each
-            // would stream fewer than 16 units (the rows are short and the
-            // start-up dominates): then one per CU with 8-deep rings (32
-            // sequences of 8K: 22.4 against 25.3 us; 8 of 128K: 47.1
-            // against 49.7 us the other way round)
-            const int64_t est_units = (int64_t)p.B * (p.Lmax / 64 + 16);
-            if (est_units < (int64_t)16 * grid)
-              launch_mfma<1, 8, kKeyBF16, 1>(p, num_cus, stream, ev_start, ev_stop);
-            else
-              launch_mfma<1, 4, kKeyBF16, 2>(p, grid, stream, ev_start, ev_stop);
-          }
-          break;
-      }
-    } else if (p.k_dtype == kE4M3) {
-      if (p.T == 1)
-        launch_mfma<1, 8, kKeyE4M3>(p, grid, stream, ev_start, ev_stop);
-      else
-        launch_mfma<2, 4, kKeyE4M3>(p, grid, stream, ev_start, ev_stop);
-    } else {
-      // (two tokens with their group scales need more than half the
-      // registers: one workgroup per CU)
-      if (p.T == 1)
-        launch_mfma<1, 8, kKeyMX>(p, grid, stream, ev_start, ev_stop);
-      else
-        launch_mfma<2, 4, kKeyMX, 1>(p, num_cus, stream, ev_start, ev_stop);
+    const ScoreLaunch l = score_launch_plan(p, num_cus);
+    switch (l.kernel) {
+      case kSkBf16R8: launch_mfma<1, 8, kKeyBF16, 1>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkBf16W8: launch_mfma<1, 4, kKeyBF16, 1, 512>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkBf16T2: launch_mfma<2, 4, kKeyBF16, 1>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkBf16T4: launch_mfma<4, 4, kKeyBF16, 1>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkBf16R4: launch_mfma<1, 4, kKeyBF16, 2>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkE4m3T1: launch_mfma<1, 8, kKeyE4M3>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkE4m3T2: launch_mfma<2, 4, kKeyE4M3>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkMxT1: launch_mfma<1, 8, kKeyMX>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkMxT2: launch_mfma<2, 4, kKeyMX, 1>(p, l.grid, stream, ev_start, ev_stop); break;
     }
   } else {
     dim3 grid((unsigned)((p.Lmax + 255) / 256), (unsigned)(p.B * p.T));

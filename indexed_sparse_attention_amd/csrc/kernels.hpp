@@ -92,12 +92,16 @@ bool score_mfma_supported(const ScoreParams& p);
 // recorded by the dispatch itself at the kernel's start and end.
 hipError_t launch_score(const ScoreParams& p, bool allow_mfma, int num_cus, hipStream_t stream,
                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// Names the matrix-core launch launch_score would make for p (snprintf's result).
+int score_launch_desc(const ScoreParams& p, int num_cus, char* buf, size_t len);
 
 // topk.hip
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
 hipError_t launch_hist(const float* scores, const int32_t* seq_lens, int len_sub, uint32_t* hist, int B, int T,
                        int64_t Lmax, hipStream_t stream);
 hipError_t launch_select(const TopkParams& p, hipStream_t stream);
+// Whether launch_select runs one workgroup per query (reads B, T and Lmax only).
+bool select_row_mode(const TopkParams& p);
 
 // noalloc_ws.hip: the device address (on the current device) and size of
 // the library-owned workspace of dsa_forward_noalloc.
