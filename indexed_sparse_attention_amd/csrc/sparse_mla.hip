@@ -186,9 +186,14 @@ __device__ __forceinline__ int tile_row(int mt, int i) {
   return 16 * mt + 2 * (i & 3) + ((i >> 2) & 1) + 8 * (i >> 3);
 }
 
-// Byte offset of 16-byte chunk c (0..71) of tile row r (0..63).
+// Byte offset of 16-byte chunk c (0..71) of tile row r (0..63): chunk c of
+// a segment sits in slot (c ^ r ^ r/4) % 8 of the row's 128 bytes.  Of the
+// XOR swizzles tried on the LDS bank-conflict counter, this one leaves both
+// the score operand reads (16 rows x 4 chunks per instruction) and the
+// transposed value reads conflict-free; with (c ^ r ^ r/8) % 8 the score
+// reads took two passes each.
 __device__ __forceinline__ int chunk_off(int r, int c) {
-  return ((r >> 3) * 9 + (c >> 3)) * 1024 + 16 * (8 * (r & 7) + ((c ^ r ^ (r >> 3)) & 7));
+  return ((r >> 3) * 9 + (c >> 3)) * 1024 + 16 * (8 * (r & 7) + ((c ^ r ^ (r >> 2)) & 7));
 }
 
 // Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane groups
@@ -345,7 +350,8 @@ __device__ __forceinline__ void tile_dma(uint8_t* dst, const MlaParams& p, const
   for (int g = 0; g < 2; ++g) {
     const int rg = 2 * wave + g;  // 8-row group
     const int64_t row = seq_row0 + max(pos[g], 0);
-    const int cx = ((l & 7) ^ (l >> 3) ^ rg) & 7;  // chunk slot of this lane within each 8-chunk group
+    // the chunk whose slot is l % 8 in row 8 rg + l / 8 (the inverse of chunk_off's swizzle)
+    const int cx = ((l & 7) ^ (l >> 3) ^ (2 * rg + (l >> 5))) & 7;
     const uint8_t* src = FP8 ? (const uint8_t*)p.kv + row * kDqk + (cx >> 1) * 16
                              : (const uint8_t*)p.kv + row * (2 * kDqk) + cx * 16;
     uint8_t* seg = dst + rg * 9 * 1024;
@@ -372,7 +378,7 @@ struct TileCopy {
     for (int g = 0; g < 2; ++g) {
       const int rg = 2 * wave + g;
       const int64_t row = seq_row0 + (live ? max(pos[g], 0) : 0);
-      const int cx = live ? ((l & 7) ^ (l >> 3) ^ rg) & 7 : 0;
+      const int cx = live ? ((l & 7) ^ (l >> 3) ^ (2 * rg + (l >> 5))) & 7 : 0;
       src[g] = FP8 ? (const uint8_t*)p.kv + row * kDqk + (cx >> 1) * 16
                    : (const uint8_t*)p.kv + row * (2 * kDqk) + cx * 16;
       seg[g] = dst + rg * 9 * 1024;
