@@ -199,7 +199,7 @@ def algorithmic_bytes(w):
             "score_kernel": score_kernel, "attention": attention, "attention_flops": attn_flops}
 
 
-def wg_trace_report(dsa, torch, np, step, workload, w, dump=None):
+def wg_trace_report(dsa, torch, np, step, workload, w, dump=None, rotate=1):
     """Per-workgroup clock stamps (the library's workgroup trace, 100 MHz)
     of one eager step: for each kernel, when its workgroups started and
     finished relative to its first start, how far apart, and the gap between
@@ -249,6 +249,31 @@ def wg_trace_report(dsa, torch, np, step, workload, w, dump=None):
         print(f"{name:16s} {int(m.sum()):6d} {s_us.max():10.2f} {e_us.min():8.2f} {q(e_us, .5):8.2f} "
               f"{q(e_us, .9):8.2f} {e_us.max():8.2f} {e_us.max() - e_us.min():8.2f} {q(busy, .5):8.2f} "
               f"{busy.max():8.2f} {gap:>6s}")
+
+    # Three steps launched back to back (rotating inputs), each into its own
+    # trace buffer: the span of a step's workgroups and the gap from one
+    # step's last workgroup to the next one's first.
+    n = 3
+    bufs = [torch.zeros(len(kinds) * slots * 2, dtype=torch.int64, device="cuda:0") for _ in range(n)]
+    torch.cuda.synchronize()
+    try:
+        for i in range(n):
+            dsa.set_workgroup_trace(bufs[i], slots)
+            step(i % rotate)
+        torch.cuda.synchronize()
+    finally:
+        dsa.set_workgroup_trace(None)
+    spans = []
+    for b in bufs:
+        t = b.view(len(kinds), slots, 2).cpu().numpy()
+        st, en = t[:, :, 0], t[:, :, 1]
+        m = (st != 0) & (en != 0)
+        spans.append((float(st[m].min()), float(en[m].max())))
+    span_us = [(e - s0) / 100.0 for s0, e in spans]
+    gaps_us = [(spans[i + 1][0] - spans[i][1]) / 100.0 for i in range(n - 1)]
+    print(f"# {n} steps back to back: first to last workgroup of each step "
+          f"{' '.join(f'{x:.1f}' for x in span_us)} us; from a step's last workgroup to the next "
+          f"step's first {' '.join(f'{x:.2f}' for x in gaps_us)} us")
 
 
 def cpu_model():
@@ -365,7 +390,7 @@ def main():
     ref_out = outs["out"].clone()
 
     if args.wg_trace:
-        wg_trace_report(dsa, torch, np, step, args.workload, w, args.wg_trace_dump)
+        wg_trace_report(dsa, torch, np, step, args.workload, w, args.wg_trace_dump, R)
         return
 
     graphs = None
