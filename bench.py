@@ -63,7 +63,8 @@ def parse():
                          "in one launch, print the spread, then exit")
     ap.add_argument("--wg-trace-dump", default=None, metavar="FILE.npy",
                     help="with --wg-trace: also save the raw stamps, int64 [kind][workgroup][start, end] "
-                         "in 100 MHz clock ticks (0: not stamped)")
+                         "in 100 MHz clock ticks (0: not stamped), and those of the back-to-back steps "
+                         "as FILE_step<i>.npy")
     return ap.parse_args()
 
 
@@ -264,8 +265,10 @@ def wg_trace_report(dsa, torch, np, step, workload, w, dump=None, rotate=1):
     finally:
         dsa.set_workgroup_trace(None)
     spans = []
-    for b in bufs:
+    for i, b in enumerate(bufs):
         t = b.view(len(kinds), slots, 2).cpu().numpy()
+        if dump:
+            np.save(dump.replace(".npy", "") + f"_step{i}.npy", t)
         st, en = t[:, :, 0], t[:, :, 1]
         m = (st != 0) & (en != 0)
         spans.append((float(st[m].min()), float(en[m].max())))
