@@ -218,6 +218,21 @@ def test_kernel_choice_reports_paths():
         del os.environ["DSA_FORCE_GENERIC"]
 
 
+def test_kernel_choice_names_the_launches():
+    """The description follows the launch rules: the score kernel's shape and
+    workgroup count, the Top-K mode and the token tile."""
+    def prob(B, T, L):
+        return dsa.make_problem(batch=B, q_len=T, max_seq_len=L, idx_heads=64, idx_dim=128, heads=128,
+                                qk_dim=576, v_dim=512, top_k=2048, q_idx_dtype=1, idx_key_dtype=1, q_dtype=1,
+                                kv_dtype=1, out_dtype=1)
+    long_decode = dsa.kernel_choice(prob(8, 1, 131072))  # 8 sequences of 128K keys
+    assert "1 token, ring 4" in long_decode and "chunks + emit" in long_decode and "tile_tokens=0" in long_decode
+    short_decode = dsa.kernel_choice(prob(32, 1, 8192))  # short rows: 8-deep rings, one workgroup per query
+    assert "1 token, ring 8" in short_decode and "one workgroup per query" in short_decode
+    prefill = dsa.kernel_choice(prob(1, 4096, 65536))  # two tokens per segment, token tiles of 512
+    assert "2 tokens" in prefill and "tile_tokens=512" in prefill and "splits=1 " in prefill
+
+
 def _paging(table=FAKE, page_size=64, max_pages=64, num_pages=1024):
     return dsa.Paging(table, page_size, max_pages, num_pages)
 
