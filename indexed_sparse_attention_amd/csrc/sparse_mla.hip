@@ -892,8 +892,9 @@ void mla_mfma_kernel(MlaParams p) {
   // LDS (in the last tile's buffer, free after the barrier above) and written
   // back as whole rows, one 1 KB row per wave instruction.  Written straight from the accumulator
   // layout, every store instruction would cover sixteen 32-byte pieces of
-  // sixteen rows.  (Results leave through the L2: the partials are the
-  // merge's input, tens of MB at long contexts.)
+  // sixteen rows.  (All results are stored through the L2 to memory: the
+  // partials are the merge's input, tens of MB at long contexts, which as
+  // dirty L2 lines would be written back only after the last workgroup.)
   uint8_t* stage = sh.rows[cur ^ 1];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
