@@ -16,7 +16,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-variable",
     "-Wno-unused-function",
@@ -25,11 +24,29 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  The indexer's matrix-core kernels apply ReLU and the head
+# weights to every MFMA result; with the results in accumulation registers each
+# element costs one more copy instruction (v_accvgpr_read) before the VALU can
+# use it, so that file takes the MFMA forms that write arithmetic registers.
+# (The attention kernel keeps its 128 output accumulators in accumulation
+# registers on purpose, so the option is not global.)
+EXTRA = {"index_score.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+OBJ_DIR = os.path.join(HERE, "_build")
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libdsa.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every HIP source and link libdsa.so (always recompiles)."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = []
+    for s in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

@@ -116,6 +116,14 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreParams p) {
 // scales going into the scaled e4m3 MFMA.
 // ---------------------------------------------------------------------------
 constexpr int kHi = 64, kDi = 128;
+constexpr int kSharedTokens = 8;    // tokens per segment of the shared-key variant
+constexpr int kSharedThreads = 512;  // its workgroup: 8 waves, two per SIMD, one token each
+// Its LDS key ring (16-row sub-tiles of 4 KB): what the 8 tokens' packed
+// histograms (64 KB) and the static arrays leave of 160 KB.
+__host__ __device__ constexpr int ks_ring_slots(int threads) { return threads == 512 ? 20 : 21; }
+// Units a shared-key workgroup takes before flushing its 16-bit counters
+// (1020 x 64 positions per token stay below 2^16); a multiple of its store batch.
+constexpr int kPassUnits = 1020;
 constexpr int kKeyBF16 = 0, kKeyE4M3 = 1, kKeyMX = 2;
 constexpr int kGroups = kDi / 32;  // MX groups per row
 
@@ -186,19 +194,32 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   const WgTrace wg_trace_(p.wg_trace);
   constexpr bool FP8 = KF != kKeyBF16, MX = KF == kKeyMX;
   constexpr int kScoreThreads = NT, kScoreWaves = NT / kWave;
+  // Eight tokens per segment (bf16 keys, contiguous cache, many query
+  // tokens): the workgroup's four waves take two tokens each and share every
+  // key sub-tile through an LDS ring (see the segment body).
+  constexpr bool KS = TQ == kSharedTokens;
+  static_assert(!KS || (KF == kKeyBF16 && !PAGED && MINB == 1), "shared-key variant: bf16, contiguous");
+  constexpr int TW = KS ? TQ / kScoreWaves : 1;  // (shared-key variant) tokens per wave
+  constexpr int kRing = KS ? ks_ring_slots(NT) : 1;
+  // LDS histogram words per token: the shared-key variant packs two 16-bit
+  // counters per word (bins 2i, 2i + 1), which leaves room for its key ring;
+  // it flushes them at least every kPassUnits units, before one can overflow
+  constexpr int kHistWords = KS ? kHistBins / 2 : kHistBins;
   // LDS: [TQ] index queries in operand order (bf16: 64 x 128 x 2 B; e4m3: 64 x 128 B),
-  // then [TQ][kHistBins] histogram counters when p.hist.
+  // then [TQ][kHistBins] histogram counters when p.hist.  Shared-key variant:
+  // [TQ][kHistBins / 2] packed histogram counters, then the key ring.
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ uint8_t s_qsc[MX ? TQ * kHi * kGroups : 4];  // (MXFP8) query group scales [TQ][head][group]
   constexpr int kQBytes = FP8 ? kHi * kDi : kHi * kDi * 2;
   uint8_t* lds_q = (uint8_t*)lds;
-  uint32_t* lds_hist = lds + TQ * kQBytes / 4;
+  uint32_t* lds_hist = lds + (KS ? 0 : TQ * kQBytes / 4);
   __shared__ int64_t s_total;
   __shared__ int64_t s_wsum[kScoreWaves];
   __shared__ int64_t s_excl[kScoreThreads];
   __shared__ int s_len[kScoreThreads];  // clamped length of each segment's sequence in the current chunk
   __shared__ int s_list[kScoreThreads];  // the segments of the current chunk this workgroup serves, in order
   __shared__ int s_wcnt[kScoreWaves];
+  __shared__ int64_t s_hist_row;  // global histogram row of the current segment's first token
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -263,11 +284,13 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   auto wg_end = [&](int64_t start, int64_t n) -> int64_t {
     return max(wg_first(start) + 1, (start + n) * G / U);
   };
-  auto round_robin = [&](int64_t n) -> bool { return p.split_mode == 1 || (p.split_mode == 0 && n * G >= 8 * U); };
+  auto round_robin = [&](int64_t n) -> bool {
+    return !KS && (p.split_mode == 1 || (p.split_mode == 0 && n * G >= 8 * U));
+  };
   const int64_t u_lo = wg * U / G, u_hi = (wg + 1) * U / G;
 
   if (p.hist)
-    for (int i = tid; i < TQ * kHistBins; i += kScoreThreads) lds_hist[i] = 0;
+    for (int i = tid; i < TQ * kHistWords; i += kScoreThreads) lds_hist[i] = 0;
 
   // Pass 2: walk the segments in chunks of kScoreThreads, with an exclusive
   // scan of their unit counts, and process the segments this workgroup serves.
@@ -377,6 +400,210 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                                                  (short)0, len * kGroups, kBufferFlags)
              : krows;
       const int last_row = len - 1;
+      // the segment's histogram counters into the global histograms (after a
+      // barrier); leaves them zero
+      // (the histogram row is read back from LDS, after a barrier: a flush
+      // inside the key loop must not keep eight row addresses in registers)
+      if (tid == 0) s_hist_row = (int64_t)b * p.T + t0;
+      auto flush_hist = [&]() {
+        if (!p.hist) return;
+        const int64_t row0 = s_hist_row;
+        for (int tq = 0; tq < TQ; ++tq) {
+          if (t0 + tq >= p.T) break;
+          uint32_t* gh = p.hist + (row0 + tq) * kHistBins;
+          for (int i = tid; i < kHistWords; i += kScoreThreads) {
+            const uint32_t c = lds_hist[tq * kHistWords + i];
+            if (c) {
+              if constexpr (KS) {  // bins 2i (low half) and 2i + 1
+                if (c & 0xFFFFu) atomicAdd(&gh[2 * i], c & 0xFFFFu);
+                if (c >> 16) atomicAdd(&gh[2 * i + 1], c >> 16);
+              } else {
+                atomicAdd(&gh[i], c);
+              }
+              lds_hist[tq * kHistWords + i] = 0;
+            }
+          }
+        }
+      };
+
+      if constexpr (KS) {
+        // ---- keys shared through LDS ----
+        // All the workgroup's waves walk its units [u_a, u_end) of the
+        // segment together.  Each 16-row key sub-tile is copied into a ring of
+        // kRing LDS slots once, by DMA (no registers: waves 0..3 copy 4 rows,
+        // 1 KB, each), and every wave multiplies it with its own TW tokens'
+        // queries, so one key read feeds 8 tokens where the register ring
+        // feeds 2.  Per unit (sub-tiles n .. n + 3): every copying wave waits
+        // for its own copies of them, then a barrier (they are complete; every
+        // wave is done with the previous unit), then the copies of the unit
+        // kRing - 4 sub-tiles ahead go into the previous unit's slots.
+        // (One barrier and one LDS wait per unit: one per sub-tile made the
+        // 512-token prefill tile's scores 517 us, one per two 486, per four 482.)
+        constexpr int kSpb = 4;  // sub-tiles per barrier
+        const int u_a = __builtin_amdgcn_readfirstlane(id_0 - wave);
+        const int n_wg_units = u_end - u_a;  // >= 1
+        const int n_sub = 4 * n_wg_units;
+        uint8_t* ring = (uint8_t*)(lds_hist + TQ * kHistWords);
+        const int tw = t0 + TW * wave;  // this wave's tokens tw .. tw + TW - 1
+        // Lane l copies row 4 wave + l/16 of the sub-tile, chunk (l%16) ^ row
+        // into chunk slot l%16 (rows 256 B apart; the XOR spreads the 16 rows
+        // a 16-lane read of one chunk touches over distinct banks).
+        const int drow = 4 * (wave & 3) + (l >> 4);  // (waves 4..7 copy nothing)
+        const uint8_t* kbase =
+            (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * (kDi * 2) + (((l & 15) ^ drow) << 4);
+        auto dma = [&](int n, int slot) {  // (n past the range re-copies a valid row: nobody reads it)
+          const int nn = min(n, n_sub - 1);
+          const int64_t row = min(64 * (int64_t)(u_a + (nn >> 2)) + 16 * (nn & 3) + drow, (int64_t)last_row);
+          if (wave < 4)
+            __builtin_amdgcn_global_load_lds((const void*)(kbase + row * (kDi * 2)),
+                                             (__attribute__((address_space(3))) void*)(ring + slot * 4096 + wave * 1024),
+                                             16, 0, 0);
+        };
+        // operand A: this wave's TW tokens' queries, straight from memory
+        // (head 16 ht + lc, dims 32 ks + 8 lg .. +8), and their head weights
+        bf16x8 qa[TW][4][4];
+        float w2[TW][4][4];
+#pragma unroll
+        for (int tq = 0; tq < TW; ++tq) {
+          const int t = min(tw + tq, p.T - 1);
+          const bf16x8* qrow = (const bf16x8*)((const uint16_t*)p.q_idx + ((int64_t)b * p.T + t) * kHi * kDi);
+          const float* wrow = p.head_w + ((int64_t)b * p.T + t) * kHi;
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qa[tq][ht][ks] = qrow[(ht * 16 + lc) * (kDi / 8) + ks * 4 + lg];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w2[tq][ht][e] = wrow[ht * 16 + 4 * lg + e];
+          }
+        }
+        // (pinned in accumulation registers, which the MFMA reads directly;
+        // the ring's first copies go out after them, since the compiler's
+        // wait for the queries would otherwise wait for the copies too)
+#pragma unroll
+        for (int tq = 0; tq < TW; ++tq)
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qa[tq][ht][ks]));
+#pragma unroll
+        for (int n = 0; n < kRing - kSpb; ++n) dma(n, n);
+        // this lane's operand-B read of chunk 4 ks + lg of row lc, within a slot
+        uint32_t boff[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) boff[ks] = (uint32_t)(lc * 256 + (((4 * ks + lg) ^ lc) << 4));
+        const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+        const uint32_t hist_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)lds_hist;
+        const bool upper = l >= 32, odd = (lg & 1) != 0;
+        int slot = 0;  // slot of sub-tile n (n % kRing)
+        constexpr int RBK = 4;  // units per store batch
+        static_assert(kPassUnits % RBK == 0, "flushes fall between store batches");
+        for (int u0 = 0; u0 < n_wg_units; u0 += RBK) {
+          if (u0 > 0 && u0 % kPassUnits == 0) {  // (uniform; rare) flush the packed counters before they can overflow
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+            flush_hist();
+            __syncthreads();
+          }
+          float sbuf[TW][RBK];
+#pragma unroll
+          for (int ub = 0; ub < RBK; ++ub) {
+            if (u0 + ub < n_wg_units) {  // (uniform over the workgroup)
+              float part[TW][4];
+#pragma unroll
+              for (int sp = 0; sp < 4; sp += kSpb) {
+                // sub-tiles n .. n + kSpb - 1: this wave's copies of them have
+                // landed (kRing - 2 kSpb newer ones may be in flight: copies
+                // complete in order), barrier, then the copies of the kSpb
+                // sub-tiles kRing - kSpb ahead go into the slots of n - kSpb .. n - 1
+                const int n = 4 * (u0 + ub) + sp;
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kRing - 2 * kSpb) : "memory");
+                int sl[kSpb];  // slots of n .. n + kSpb - 1
+#pragma unroll
+                for (int h = 0; h < kSpb; ++h) {
+                  sl[h] = slot + h >= kRing ? slot + h - kRing : slot + h;
+                  dma(n + kRing - kSpb + h, sl[h] >= kSpb ? sl[h] - kSpb : sl[h] + kRing - kSpb);
+                }
+                slot = slot + kSpb >= kRing ? slot + kSpb - kRing : slot + kSpb;
+                // operand B of the kSpb sub-tiles, read in one block (its wait included)
+                bf16x8 kb[kSpb][4];
+#pragma unroll
+                for (int h = 0; h < kSpb; h += 2) {
+                  const uint32_t sb0 = ring_base + (uint32_t)sl[h] * 4096u, sb1 = ring_base + (uint32_t)sl[h + 1] * 4096u;
+                  asm volatile(
+                      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
+                      "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+                      "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+                      : "=&v"(kb[h][0]), "=&v"(kb[h][1]), "=&v"(kb[h][2]), "=&v"(kb[h][3]), "=&v"(kb[h + 1][0]),
+                        "=&v"(kb[h + 1][1]), "=&v"(kb[h + 1][2]), "=&v"(kb[h + 1][3])
+                      : "v"(sb0 + boff[0]), "v"(sb0 + boff[1]), "v"(sb0 + boff[2]), "v"(sb0 + boff[3]),
+                        "v"(sb1 + boff[0]), "v"(sb1 + boff[1]), "v"(sb1 + boff[2]), "v"(sb1 + boff[3])
+                      : "memory");
+                }
+#pragma unroll
+                for (int h = 0; h < kSpb; ++h) {
+                  f32x4 acc[TW][4];
+#pragma unroll
+                  for (int tq = 0; tq < TW; ++tq)
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht) {
+                      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                      for (int ks = 0; ks < 4; ++ks)
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[tq][ht][ks], kb[h][ks], a, 0, 0, 0);
+                      acc[tq][ht] = a;
+                    }
+#pragma unroll
+                  for (int tq = 0; tq < TW; ++tq) {
+                    float sacc = 0.0f;
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+                      for (int e = 0; e < 4; ++e) sacc = fmaf(w2[tq][ht][e], relu_bits(acc[tq][ht][e]), sacc);
+                    part[tq][sp + h] = sacc;
+                  }
+                }
+              }
+              // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
+              const int64_t pos = 64 * (int64_t)(u_a + u0 + ub) + 16 * lg + lc;
+#pragma unroll
+              for (int tq = 0; tq < TW; ++tq) {
+                const float r0 = (upper ? part[tq][2] : part[tq][0]) +
+                                 __shfl_xor(upper ? part[tq][0] : part[tq][2], 32, kWave);
+                const float r1 = (upper ? part[tq][3] : part[tq][1]) +
+                                 __shfl_xor(upper ? part[tq][1] : part[tq][3], 32, kWave);
+                const float sc = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16, kWave);
+                sbuf[tq][ub] = sc;
+                // (the histogram add is written as asm: an LDS access the
+                // compiler sees while a ring copy is in flight makes it wait
+                // for every copy, since both lie in the same LDS array)
+                if (p.hist && tw + tq < p.T && pos < (int64_t)len - p.T + 1 + tw + tq)
+                {
+                  const uint32_t bin = score_key(sc) >> kHistShift;
+                  asm volatile("ds_add_u32 %0, %1" ::"v"(hist_base + 4u * ((uint32_t)(TW * wave + tq) * kHistWords +
+                                                                           (bin >> 1))),
+                               "v"(1u << (16 * (bin & 1)))
+                               : "memory");
+                }
+              }
+            }
+          }
+          // store the batch, then let the stores complete: on this target
+          // loads and stores share one completion counter, and the ring's
+          // partial waits assume that only its copies are outstanding
+#pragma unroll
+          for (int ub = 0; ub < RBK; ++ub) {
+            const int64_t pos = 64 * (int64_t)(u_a + u0 + ub) + 16 * lg + lc;
+            if (u0 + ub < n_wg_units && pos < vis_last) {
+#pragma unroll
+              for (int tq = 0; tq < TW; ++tq)
+                if (tw + tq < p.T) p.scores[((int64_t)b * p.T + tw + tq) * p.Lmax + pos] = sbuf[tq][ub];
+            }
+          }
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        // (the copies past the range have landed; the histogram adds are done)
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)" ::: "memory");
+      } else {
 
       // Paged caches: a 16-row sub-tile never straddles a page (pages hold a
       // multiple of 64 rows), so each sub-tile's rows are read through a
@@ -654,19 +881,10 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           }
         }
       }
-      __syncthreads();  // all waves done with lds_q (and their histogram updates)
+      }  // register ring
+      __syncthreads();  // all waves done with lds_q or the key ring (and their histogram updates)
       if (p.hist) {
-        for (int tq = 0; tq < TQ; ++tq) {
-          if (t0 + tq >= p.T) break;
-          uint32_t* gh = p.hist + ((int64_t)b * p.T + t0 + tq) * kHistBins;
-          for (int i = tid; i < kHistBins; i += kScoreThreads) {
-            const uint32_t c = lds_hist[tq * kHistBins + i];
-            if (c) {
-              atomicAdd(&gh[i], c);
-              lds_hist[tq * kHistBins + i] = 0;
-            }
-          }
-        }
+        flush_hist();
         __syncthreads();
       }
     }
@@ -691,7 +909,10 @@ template <int TQ, int NSLOT, int KF, int MINB, int NT, bool PAGED>
 static void launch_mfma_k(const ScoreParams& p_in, int grid, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop) {
   constexpr int kQBytes = KF != kKeyBF16 ? kHi * kDi : kHi * kDi * 2;
-  const size_t lds = TQ * kQBytes + (p_in.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
+  size_t lds = TQ * kQBytes + (p_in.hist ? TQ * kHistBins * sizeof(uint32_t) : 0);
+  if constexpr (TQ == kSharedTokens) {  // histograms, then the key ring
+    lds = TQ * kHistBins * sizeof(uint16_t) + ks_ring_slots(NT) * 4096;
+  }
   ScoreParams p = p_in;
   p.wg_trace = trace_region(kTraceScore, grid);
   if (ev_start || ev_stop)  // events taken by the dispatch itself at the kernel's start and end
@@ -726,7 +947,9 @@ static int env_int(const char* name, int dflt) {
 // the keys about 5 % faster than variant 1 at 1/CU.)
 // The matrix-core kernel and grid launch_score takes for p (shared with the
 // diagnostics that name the launch).
-enum ScoreKernel { kSkBf16R8, kSkBf16W8, kSkBf16T2, kSkBf16T4, kSkBf16R4, kSkE4m3T1, kSkE4m3T2, kSkMxT1, kSkMxT2 };
+enum ScoreKernel {
+  kSkBf16R8, kSkBf16W8, kSkBf16T2, kSkBf16T4, kSkBf16R4, kSkE4m3T1, kSkE4m3T2, kSkMxT1, kSkMxT2, kSkBf16S8
+};
 struct ScoreLaunch {
   ScoreKernel kernel;
   int grid;
@@ -746,6 +969,10 @@ static ScoreLaunch score_launch_plan(const ScoreParams& p, int num_cus) {
       case 4: return {kSkBf16T4, grid};
       case 5: return {kSkBf16R4, 2 * num_cus};
       default:
+        // eight or more query tokens (contiguous cache): eight per segment,
+        // each key sub-tile shared by the workgroup's four waves through LDS
+        if (p.T >= kSharedTokens && !p.block_table)
+          return {kSkBf16S8, env_int("DSA_SCORE_WGS", 0) > 0 ? grid : num_cus};
         // several query tokens: two per segment, so each key tile feeds twice
         // the MFMAs (12 % faster at 4096 tokens over 64K keys; four tokens
         // need one workgroup per CU and were slower)
@@ -773,7 +1000,7 @@ int score_launch_desc(const ScoreParams& p, int num_cus, char* buf, size_t len) 
       "bf16 keys, 2 tokens, ring 4, 4 waves", "bf16 keys, 4 tokens, ring 4, 4 waves",
       "bf16 keys, 1 token, ring 4, 4 waves",  "e4m3 keys, 1 token, ring 8, 4 waves",
       "e4m3 keys, 2 tokens, ring 4, 4 waves", "mxfp8 keys, 1 token, ring 8, 4 waves",
-      "mxfp8 keys, 2 tokens, ring 4, 4 waves"};
+      "mxfp8 keys, 2 tokens, ring 4, 4 waves", "bf16 keys, 8 tokens, shared LDS ring 20, 8 waves"};
   const ScoreLaunch l = score_launch_plan(p, num_cus);
   return snprintf(buf, len, "mfma(%s; %d workgroups)", names[l.kernel], l.grid);
 }
@@ -795,6 +1022,14 @@ hipError_t launch_score(const ScoreParams& p_in, bool allow_mfma, int num_cus, h
       case kSkE4m3T2: launch_mfma<2, 4, kKeyE4M3>(p, l.grid, stream, ev_start, ev_stop); break;
       case kSkMxT1: launch_mfma<1, 8, kKeyMX>(p, l.grid, stream, ev_start, ev_stop); break;
       case kSkMxT2: launch_mfma<2, 4, kKeyMX, 1>(p, l.grid, stream, ev_start, ev_stop); break;
+      case kSkBf16S8: {
+        constexpr size_t lds = kSharedTokens * kHistBins * sizeof(uint16_t) + ks_ring_slots(kSharedThreads) * 4096;
+        const hipError_t e = set_max_dynamic_lds(
+            (const void*)score_mfma_kernel<kSharedTokens, 4, kKeyBF16, 1, kSharedThreads, false>, (int)lds);
+        if (e != hipSuccess) return e;
+        launch_mfma_k<kSharedTokens, 4, kKeyBF16, 1, kSharedThreads, false>(p, l.grid, stream, ev_start, ev_stop);
+        break;
+      }
     }
   } else {
     dim3 grid((unsigned)((p.Lmax + 255) / 256), (unsigned)(p.B * p.T));

@@ -229,8 +229,10 @@ def test_kernel_choice_names_the_launches():
     assert "1 token, ring 4" in long_decode and "chunks + emit" in long_decode and "tile_tokens=0" in long_decode
     short_decode = dsa.kernel_choice(prob(32, 1, 8192))  # short rows: 8-deep rings, one workgroup per query
     assert "1 token, ring 8" in short_decode and "one workgroup per query" in short_decode
-    prefill = dsa.kernel_choice(prob(1, 4096, 65536))  # two tokens per segment, token tiles of 512
-    assert "2 tokens" in prefill and "tile_tokens=512" in prefill and "splits=1 " in prefill
+    prefill = dsa.kernel_choice(prob(1, 4096, 65536))  # eight tokens per segment, token tiles of 512
+    assert "8 tokens, shared LDS ring" in prefill and "tile_tokens=512" in prefill and "splits=1 " in prefill
+    drafts = dsa.kernel_choice(prob(4, 2, 65536))  # two draft tokens: two per segment
+    assert "2 tokens, ring 4" in drafts
 
 
 def _paging(table=FAKE, page_size=64, max_pages=64, num_pages=1024):

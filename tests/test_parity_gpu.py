@@ -61,6 +61,13 @@ CASES = {
                               batch=2, top_k=700),
     "fp8_drafts_odd": dict(name="fp8_1m", batch=2, q_len=3, max_seq_len=9000, len_range=(5000, 9000),
                            top_k=600),
+    # eight or more tokens: the shared-key score kernel (eight tokens per
+    # segment) with a token count that leaves a partial last group (13 = 8 + 5:
+    # three tokens of it do not exist), ragged sequences of several lengths
+    # that are not whole units of 64 positions, and one sequence shorter than
+    # a unit
+    "prefill_shared_keys_ragged": dict(name="prefill64k", batch=4, q_len=13, max_seq_len=7000,
+                                       len_range=(13, 7000), top_k=600),
 }
 
 
@@ -147,6 +154,31 @@ def test_two_tokens_with_fewer_rows_than_tokens(name, split):
     assert np.all(got["topk_idx"][0] == -1) and np.all(got["out"][0] == 0)
     assert np.all(np.isneginf(got["lse"][0])) and np.isneginf(got["lse"][1, 0]).all()
     assert got["topk_idx"][1, 1, 0] == 0 and np.all(got["topk_idx"][1, 1, 1:] == -1)
+
+
+def test_shared_key_score_kernel_short_rows():
+    # eight tokens per segment on rows shorter than the token count (len 5 <
+    # T = 13: tokens 0..7 see nothing), an empty row, a row of exactly T, one
+    # shorter than a unit of 64 positions and a long ragged one
+    w = _case("prefill64k", batch=5, q_len=13, max_seq_len=7000, len_range=(13, 7000), top_k=300)
+    w.seq_lens[:] = [0, 5, 13, 40, 6999]
+    got, _ = _full_check(w)
+    counts = got["topk_count"]
+    assert np.all(counts[0] == 0) and np.all(counts[1, :8] == 0)
+    assert counts[1, 8:].tolist() == [1, 2, 3, 4, 5] and counts[2].tolist() == list(range(1, 14))
+    assert np.all(counts[4] == 300)
+
+
+def test_shared_key_score_kernel_flushes_its_counters():
+    # one workgroup takes all 1110 units of an 8-token segment over 70000
+    # positions: its 16-bit histogram counters are flushed after 1020 units,
+    # before any can overflow, and the histogram (hence the Top-K) stays exact
+    w = _case("prefill64k", batch=1, q_len=8, max_seq_len=70000, len_range=(70000, 70000), top_k=700)
+    os.environ["DSA_SCORE_WGS"] = "1"
+    try:
+        _full_check(w)
+    finally:
+        del os.environ["DSA_SCORE_WGS"]
 
 
 @pytest.mark.parametrize("variant", [1, 5])
