@@ -451,13 +451,25 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         const int drow = 4 * (wave & 3) + (l >> 4);  // (waves 4..7 copy nothing)
         const uint8_t* kbase =
             (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * (kDi * 2) + (((l & 15) ^ drow) << 4);
+        // The copy is written as asm, so the compiler does not see an LDS
+        // write in flight: seeing one, it would make every LDS access in the
+        // loop wait for all copies (the ring and the histograms share one
+        // array).  The ring's own waits and barriers order the copies with the
+        // reads.  (M0, which the instruction takes its LDS address from, is
+        // restored in the block.)
+        const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
         auto dma = [&](int n, int slot) {  // (n past the range re-copies a valid row: nobody reads it)
           const int nn = min(n, n_sub - 1);
           const int64_t row = min(64 * (int64_t)(u_a + (nn >> 2)) + 16 * (nn & 3) + drow, (int64_t)last_row);
-          if (wave < 4)
-            __builtin_amdgcn_global_load_lds((const void*)(kbase + row * (kDi * 2)),
-                                             (__attribute__((address_space(3))) void*)(ring + slot * 4096 + wave * 1024),
-                                             16, 0, 0);
+          if (wave < 4) {
+            uint32_t m0_saved;
+            asm volatile(
+                "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                : "=&s"(m0_saved)
+                : "s"(__builtin_amdgcn_readfirstlane(ring_base + (uint32_t)(slot * 4096 + wave * 1024))),
+                  "v"(kbase + row * (kDi * 2))
+                : "memory");
+          }
         };
         // operand A: this wave's TW tokens' queries, straight from memory
         // (head 16 ht + lc, dims 32 ks + 8 lg .. +8), and their head weights
@@ -491,8 +503,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         uint32_t boff[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) boff[ks] = (uint32_t)(lc * 256 + (((4 * ks + lg) ^ lc) << 4));
-        const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
-        const uint32_t hist_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)lds_hist;
+
         const bool upper = l >= 32, odd = (lg & 1) != 0;
         int slot = 0;  // slot of sub-tile n (n % kRing)
         constexpr int RBK = 4;  // units per store batch
@@ -524,21 +535,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                   dma(n + kRing - kSpb + h, sl[h] >= kSpb ? sl[h] - kSpb : sl[h] + kRing - kSpb);
                 }
                 slot = slot + kSpb >= kRing ? slot + kSpb - kRing : slot + kSpb;
-                // operand B of the kSpb sub-tiles, read in one block (its wait included)
+                // operand B of the kSpb sub-tiles (plain LDS loads: the
+                // compiler issues them together and waits for each just
+                // before its first MFMA)
                 bf16x8 kb[kSpb][4];
 #pragma unroll
-                for (int h = 0; h < kSpb; h += 2) {
-                  const uint32_t sb0 = ring_base + (uint32_t)sl[h] * 4096u, sb1 = ring_base + (uint32_t)sl[h + 1] * 4096u;
-                  asm volatile(
-                      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
-                      "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
-                      "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
-                      : "=&v"(kb[h][0]), "=&v"(kb[h][1]), "=&v"(kb[h][2]), "=&v"(kb[h][3]), "=&v"(kb[h + 1][0]),
-                        "=&v"(kb[h + 1][1]), "=&v"(kb[h + 1][2]), "=&v"(kb[h + 1][3])
-                      : "v"(sb0 + boff[0]), "v"(sb0 + boff[1]), "v"(sb0 + boff[2]), "v"(sb0 + boff[3]),
-                        "v"(sb1 + boff[0]), "v"(sb1 + boff[1]), "v"(sb1 + boff[2]), "v"(sb1 + boff[3])
-                      : "memory");
-                }
+                for (int h = 0; h < kSpb; ++h)
+#pragma unroll
+                  for (int ks = 0; ks < 4; ++ks) kb[h][ks] = *(const bf16x8*)(ring + sl[h] * 4096 + boff[ks]);
 #pragma unroll
                 for (int h = 0; h < kSpb; ++h) {
                   f32x4 acc[TW][4];
@@ -573,16 +577,9 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                                  __shfl_xor(upper ? part[tq][1] : part[tq][3], 32, kWave);
                 const float sc = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16, kWave);
                 sbuf[tq][ub] = sc;
-                // (the histogram add is written as asm: an LDS access the
-                // compiler sees while a ring copy is in flight makes it wait
-                // for every copy, since both lie in the same LDS array)
-                if (p.hist && tw + tq < p.T && pos < (int64_t)len - p.T + 1 + tw + tq)
-                {
+                if (p.hist && tw + tq < p.T && pos < (int64_t)len - p.T + 1 + tw + tq) {
                   const uint32_t bin = score_key(sc) >> kHistShift;
-                  asm volatile("ds_add_u32 %0, %1" ::"v"(hist_base + 4u * ((uint32_t)(TW * wave + tq) * kHistWords +
-                                                                           (bin >> 1))),
-                               "v"(1u << (16 * (bin & 1)))
-                               : "memory");
+                  atomicAdd(&lds_hist[(TW * wave + tq) * kHistWords + (bin >> 1)], 1u << (16 * (bin & 1)));
                 }
               }
             }
