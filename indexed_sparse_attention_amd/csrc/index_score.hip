@@ -543,6 +543,21 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                 for (int h = 0; h < kSpb; ++h)
 #pragma unroll
                   for (int ks = 0; ks < 4; ++ks) kb[h][ks] = *(const bf16x8*)(ring + sl[h] * 4096 + boff[ks]);
+                // Software-pipelined: sub-tile h's MFMAs are issued next to
+                // the ReLU-weighted sums of sub-tile h - 1, which do not
+                // depend on them, so the matrix core and the VALU overlap.
+                f32x4 accp[TW][4];
+                auto head_sums = [&](const f32x4 (&a)[TW][4], int st) {
+#pragma unroll
+                  for (int tq = 0; tq < TW; ++tq) {
+                    float sacc = 0.0f;
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+                      for (int e = 0; e < 4; ++e) sacc = fmaf(w2[tq][ht][e], relu_bits(a[tq][ht][e]), sacc);
+                    part[tq][st] = sacc;
+                  }
+                };
 #pragma unroll
                 for (int h = 0; h < kSpb; ++h) {
                   f32x4 acc[TW][4];
@@ -556,16 +571,21 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[tq][ht][ks], kb[h][ks], a, 0, 0, 0);
                       acc[tq][ht] = a;
                     }
+                  if (h > 0) {
+                    head_sums(accp, sp + h - 1);
+                    // (the schedule: each MFMA followed by two VALU instructions)
 #pragma unroll
-                  for (int tq = 0; tq < TW; ++tq) {
-                    float sacc = 0.0f;
-#pragma unroll
-                    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-                      for (int e = 0; e < 4; ++e) sacc = fmaf(w2[tq][ht][e], relu_bits(acc[tq][ht][e]), sacc);
-                    part[tq][sp + h] = sacc;
+                    for (int i = 0; i < 16 * TW; ++i) {
+                      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+                    }
                   }
+#pragma unroll
+                  for (int tq = 0; tq < TW; ++tq)
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht) accp[tq][ht] = acc[tq][ht];
                 }
+                head_sums(accp, sp + kSpb - 1);
               }
               // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
               const int64_t pos = 64 * (int64_t)(u_a + u0 + ub) + 16 * lg + lc;
