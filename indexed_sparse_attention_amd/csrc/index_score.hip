@@ -120,7 +120,7 @@ constexpr int kSharedTokens = 8;    // tokens per segment of the shared-key vari
 constexpr int kSharedThreads = 512;  // its workgroup: 8 waves, two per SIMD, one token each
 // Its LDS key ring (16-row sub-tiles of 4 KB): what the 8 tokens' packed
 // histograms (64 KB) and the static arrays leave of 160 KB.
-__host__ __device__ constexpr int ks_ring_slots(int threads) { return threads == 512 ? 20 : 21; }
+__host__ __device__ constexpr int ks_ring_slots(int threads) { return threads == 512 ? 20 : 0; }
 // Units a shared-key workgroup takes before flushing its 16-bit counters
 // (1020 x 64 positions per token stay below 2^16); a multiple of its store batch.
 constexpr int kPassUnits = 1020;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
   // tokens): the workgroup's four waves take two tokens each and share every
   // key sub-tile through an LDS ring (see the segment body).
   constexpr bool KS = TQ == kSharedTokens;
-  static_assert(!KS || (KF == kKeyBF16 && !PAGED && MINB == 1), "shared-key variant: bf16, contiguous");
+  static_assert(!KS || (KF == kKeyBF16 && !PAGED && MINB == 1 && NT == 512), "shared-key variant: bf16, contiguous, 8 waves");
   constexpr int TW = KS ? TQ / kScoreWaves : 1;  // (shared-key variant) tokens per wave
   constexpr int kRing = KS ? ks_ring_slots(NT) : 1;
   // LDS histogram words per token: the shared-key variant packs two 16-bit
@@ -428,27 +428,26 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 
       if constexpr (KS) {
         // ---- keys shared through LDS ----
-        // All the workgroup's waves walk its units [u_a, u_end) of the
-        // segment together.  Each 16-row key sub-tile is copied into a ring of
-        // kRing LDS slots once, by DMA (no registers: waves 0..3 copy 4 rows,
-        // 1 KB, each), and every wave multiplies it with its own TW tokens'
-        // queries, so one key read feeds 8 tokens where the register ring
-        // feeds 2.  Per unit (sub-tiles n .. n + 3): every copying wave waits
-        // for its own copies of them, then a barrier (they are complete; every
-        // wave is done with the previous unit), then the copies of the unit
-        // kRing - 4 sub-tiles ahead go into the previous unit's slots.
-        // (One barrier and one LDS wait per unit: one per sub-tile made the
-        // 512-token prefill tile's scores 517 us, one per two 486, per four 482.)
-        constexpr int kSpb = 4;  // sub-tiles per barrier
+        // All eight waves walk the workgroup's units [u_a, u_end) of the
+        // segment together.  Each unit's keys (64 rows, 16 KB) are copied into
+        // a ring of kRingU unit slots in LDS once, by DMA (no registers), and
+        // every wave multiplies them with its own token's queries, so one key
+        // read feeds 8 tokens where the register ring feeds 2.  Per unit: each
+        // wave waits for its own copies of it, then a barrier (the unit is
+        // complete; every wave is done with the previous one), then the copies
+        // of the unit kRingU - 1 ahead go into the previous unit's slot.  (One
+        // barrier per unit: one per 16-row sub-tile made the 512-token prefill
+        // tile's scores 517 us, one per two 486, one per unit 482.)
+        constexpr int kRingU = kRing / 4;  // the ring in units (4 sub-tiles, 16 KB)
         const int u_a = __builtin_amdgcn_readfirstlane(id_0 - wave);
         const int n_wg_units = u_end - u_a;  // >= 1
         const int n_sub = 4 * n_wg_units;
         uint8_t* ring = (uint8_t*)(lds_hist + TQ * kHistWords);
         const int tw = t0 + TW * wave;  // this wave's tokens tw .. tw + TW - 1
-        // Lane l copies row 4 wave + l/16 of the sub-tile, chunk (l%16) ^ row
-        // into chunk slot l%16 (rows 256 B apart; the XOR spreads the 16 rows
-        // a 16-lane read of one chunk touches over distinct banks).
-        const int drow = 4 * (wave & 3) + (l >> 4);  // (waves 4..7 copy nothing)
+        // Lane l copies row 4 (wave % 4) + l/16 of a sub-tile, chunk (l%16) ^
+        // row into chunk slot l%16 (rows 256 B apart; the XOR spreads the 16
+        // rows a 16-lane read of one chunk touches over distinct banks).
+        const int drow = 4 * (wave & 3) + (l >> 4);
         const uint8_t* kbase =
             (const uint8_t*)p.k_idx + (int64_t)b * p.Lmax * (kDi * 2) + (((l & 15) ^ drow) << 4);
         // The copy is written as asm, so the compiler does not see an LDS
@@ -458,15 +457,22 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         // reads.  (M0, which the instruction takes its LDS address from, is
         // restored in the block.)
         const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
-        auto dma = [&](int n, int slot) {  // (n past the range re-copies a valid row: nobody reads it)
-          const int nn = min(n, n_sub - 1);
-          const int64_t row = min(64 * (int64_t)(u_a + (nn >> 2)) + 16 * (nn & 3) + drow, (int64_t)last_row);
-          if (wave < 4) {
+        // Unit k's copies into unit slot us (sub-tile slots 4 us .. 4 us + 3):
+        // wave w copies rows 4 (w % 4) + l/16 of its sub-tiles w/4 and w/4 + 2,
+        // so every wave issues two of the unit's sixteen 1 KB copies.  (k past
+        // the range re-copies the last unit: nobody reads it.)
+        const int dsub = wave >> 2;
+        auto dma_unit = [&](int k, int us) {
+          const int64_t r0 = 64 * (int64_t)(u_a + min(k, n_wg_units - 1)) + drow;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int h = dsub + 2 * j;
+            const int64_t row = min(r0 + 16 * h, (int64_t)last_row);
             uint32_t m0_saved;
             asm volatile(
                 "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
                 : "=&s"(m0_saved)
-                : "s"(__builtin_amdgcn_readfirstlane(ring_base + (uint32_t)(slot * 4096 + wave * 1024))),
+                : "s"(__builtin_amdgcn_readfirstlane(ring_base + (uint32_t)((us * 4 + h) * 4096 + (wave & 3) * 1024))),
                   "v"(kbase + row * (kDi * 2))
                 : "memory");
           }
@@ -498,14 +504,14 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qa[tq][ht][ks]));
 #pragma unroll
-        for (int n = 0; n < kRing - kSpb; ++n) dma(n, n);
+        for (int k = 0; k < kRingU - 1; ++k) dma_unit(k, k);
         // this lane's operand-B read of chunk 4 ks + lg of row lc, within a slot
         uint32_t boff[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) boff[ks] = (uint32_t)(lc * 256 + (((4 * ks + lg) ^ lc) << 4));
 
         const bool upper = l >= 32, odd = (lg & 1) != 0;
-        int slot = 0;  // slot of sub-tile n (n % kRing)
+        int uslot = 0;  // unit slot of the current unit (its index % kRingU)
         constexpr int RBK = 4;  // units per store batch
         static_assert(kPassUnits % RBK == 0, "flushes fall between store batches");
         for (int u0 = 0; u0 < n_wg_units; u0 += RBK) {
@@ -520,29 +526,23 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
           for (int ub = 0; ub < RBK; ++ub) {
             if (u0 + ub < n_wg_units) {  // (uniform over the workgroup)
               float part[TW][4];
-#pragma unroll
-              for (int sp = 0; sp < 4; sp += kSpb) {
-                // sub-tiles n .. n + kSpb - 1: this wave's copies of them have
-                // landed (kRing - 2 kSpb newer ones may be in flight: copies
-                // complete in order), barrier, then the copies of the kSpb
-                // sub-tiles kRing - kSpb ahead go into the slots of n - kSpb .. n - 1
-                const int n = 4 * (u0 + ub) + sp;
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kRing - 2 * kSpb) : "memory");
-                int sl[kSpb];  // slots of n .. n + kSpb - 1
-#pragma unroll
-                for (int h = 0; h < kSpb; ++h) {
-                  sl[h] = slot + h >= kRing ? slot + h - kRing : slot + h;
-                  dma(n + kRing - kSpb + h, sl[h] >= kSpb ? sl[h] - kSpb : sl[h] + kRing - kSpb);
-                }
-                slot = slot + kSpb >= kRing ? slot + kSpb - kRing : slot + kSpb;
-                // operand B of the kSpb sub-tiles (plain LDS loads: the
+              {
+                // unit k = u0 + ub: this wave's copies of it have landed (those
+                // of the kRingU - 2 units after it may be in flight: copies
+                // complete in order), barrier (every wave's copies of unit k
+                // are complete; every wave is done with unit k - 1), then the
+                // copies of unit k + kRingU - 1 go into unit k - 1's slot
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * (kRingU - 2)) : "memory");
+                dma_unit(u0 + ub + kRingU - 1, uslot == 0 ? kRingU - 1 : uslot - 1);
+                // operand B of the unit's four sub-tiles (plain LDS loads: the
                 // compiler issues them together and waits for each just
                 // before its first MFMA)
-                bf16x8 kb[kSpb][4];
+                bf16x8 kb[4][4];
 #pragma unroll
-                for (int h = 0; h < kSpb; ++h)
+                for (int h = 0; h < 4; ++h)
 #pragma unroll
-                  for (int ks = 0; ks < 4; ++ks) kb[h][ks] = *(const bf16x8*)(ring + sl[h] * 4096 + boff[ks]);
+                  for (int ks = 0; ks < 4; ++ks) kb[h][ks] = *(const bf16x8*)(ring + (uslot * 4 + h) * 4096 + boff[ks]);
+                uslot = uslot + 1 == kRingU ? 0 : uslot + 1;
                 // Software-pipelined: sub-tile h's MFMAs are issued next to
                 // the ReLU-weighted sums of sub-tile h - 1, which do not
                 // depend on them, so the matrix core and the VALU overlap.
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                   }
                 };
 #pragma unroll
-                for (int h = 0; h < kSpb; ++h) {
+                for (int h = 0; h < 4; ++h) {
                   f32x4 acc[TW][4];
 #pragma unroll
                   for (int tq = 0; tq < TW; ++tq)
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
                       acc[tq][ht] = a;
                     }
                   if (h > 0) {
-                    head_sums(accp, sp + h - 1);
+                    head_sums(accp, h - 1);
                     // (the schedule: each MFMA followed by two VALU instructions)
 #pragma unroll
                     for (int i = 0; i < 16 * TW; ++i) {
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 #pragma unroll
                     for (int ht = 0; ht < 4; ++ht) accp[tq][ht] = acc[tq][ht];
                 }
-                head_sums(accp, sp + kSpb - 1);
+                head_sums(accp, 3);
               }
               // reduce-scatter over the 4 lane groups: lane l gets column lc of sub-tile lg
               const int64_t pos = 64 * (int64_t)(u_a + u0 + ub) + 16 * lg + lc;
