@@ -122,8 +122,8 @@ constexpr int kSharedThreads = 512;  // its workgroup: 8 waves, two per SIMD, on
 // histograms (64 KB) and the static arrays leave of 160 KB.
 __host__ __device__ constexpr int ks_ring_slots(int threads) { return threads == 512 ? 20 : 0; }
 // Units a shared-key workgroup takes before flushing its 16-bit counters
-// (1020 x 64 positions per token stay below 2^16); a multiple of its store batch.
-constexpr int kPassUnits = 1020;
+// (1008 x 64 positions per token stay below 2^16); a multiple of its store batch.
+constexpr int kPassUnits = 1008;
 constexpr int kKeyBF16 = 0, kKeyE4M3 = 1, kKeyMX = 2;
 constexpr int kGroups = kDi / 32;  // MX groups per row
 
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 
         const bool upper = l >= 32, odd = (lg & 1) != 0;
         int uslot = 0;  // unit slot of the current unit (its index % kRingU)
-        constexpr int RBK = 4;  // units per store batch
+        constexpr int RBK = 16;  // units per store batch
         static_assert(kPassUnits % RBK == 0, "flushes fall between store batches");
         for (int u0 = 0; u0 < n_wg_units; u0 += RBK) {
           if (u0 > 0 && u0 % kPassUnits == 0) {  // (uniform; rare) flush the packed counters before they can overflow

@@ -171,7 +171,7 @@ def test_shared_key_score_kernel_short_rows():
 
 def test_shared_key_score_kernel_flushes_its_counters():
     # one workgroup takes all 1110 units of an 8-token segment over 70000
-    # positions: its 16-bit histogram counters are flushed after 1020 units,
+    # positions: its 16-bit histogram counters are flushed after 1008 units,
     # before any can overflow, and the histogram (hence the Top-K) stays exact
     w = _case("prefill64k", batch=1, q_len=8, max_seq_len=70000, len_range=(70000, 70000), top_k=700)
     os.environ["DSA_SCORE_WGS"] = "1"
