@@ -108,6 +108,7 @@ TopkLayout topk_layout(const dsa_problem* p) {
   // only add redundant work (at 1M positions x 8 queries, 2048 chunks of 4096
   // took twice as long as 512 of 16384)
   int64_t chunk = std::max<int64_t>(4096, (Lmax * BT + 511) / 512);
+  if (env_int("DSA_SELECT_CHUNK", 0) > 0) chunk = env_int("DSA_SELECT_CHUNK", 0);  // (tuning)
   chunk = std::max<int64_t>(chunk, (Lmax + 1023) / 1024);  // at most 1024 chunks per query
   chunk = align_up(chunk, 1024);
   if (chunk > align_up(Lmax, 1024)) chunk = align_up(Lmax, 1024);
