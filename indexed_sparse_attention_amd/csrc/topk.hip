@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(TopkParams p) 
 // --------------------------------------------------------------------------
 constexpr int kRowThreads = 1024;
 constexpr int kRowWaves = kRowThreads / kWave;
-constexpr int kRowV = 16;
+constexpr int kRowV = 4;
 constexpr int kRowCap = 6000;  // candidates kept in LDS (struct < 64 KB); the rest spill to the global list
 constexpr int kWaveCap = kRowCap / kRowWaves;  // each wave's share of them
 static_assert(kWaveCap * kRowWaves == kRowCap, "LDS list split evenly over the waves");
@@ -362,7 +362,7 @@ __device__ void row_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* s_
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kRowThreads) void select_row_kernel(TopkParams p) {
+__global__ __launch_bounds__(kRowThreads, 8) void select_row_kernel(TopkParams p) {
   const WgTrace wg_trace_(p.wg_trace);
   extern __shared__ __attribute__((aligned(16))) uint8_t row_lds[];
   RowShared& sh = *(RowShared*)row_lds;
