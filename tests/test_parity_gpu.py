@@ -194,8 +194,13 @@ def test_one_token_score_kernels(variant):
         del os.environ["DSA_SCORE_VARIANT"]
 
 
-def test_entry_points_separately():
-    w = _case("decode128k", batch=2, max_seq_len=9000, len_range=(5000, 9000), top_k=1024)
+@pytest.mark.parametrize("name,kw", [
+    ("decode128k", dict(batch=2, max_seq_len=9000, len_range=(5000, 9000), top_k=1024)),
+    # many tokens: the shared-key score kernel without a histogram to fill
+    ("prefill64k", dict(batch=2, q_len=13, max_seq_len=3000, len_range=(1500, 3000), top_k=500)),
+])
+def test_entry_points_separately(name, kw):
+    w = _case(name, **kw)
     d = G.to_device(w)
     ref = oracle.forward(w)
     scores = dsa.dsa_index_score(d["q_idx"], d["head_w"], d["k_idx"], d["seq_lens"])
