@@ -432,12 +432,13 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         // segment together.  Each unit's keys (64 rows, 16 KB) are copied into
         // a ring of kRingU unit slots in LDS once, by DMA (no registers), and
         // every wave multiplies them with its own token's queries, so one key
-        // read feeds 8 tokens where the register ring feeds 2.  Per unit: each
-        // wave waits for its own copies of it, then a barrier (the unit is
-        // complete; every wave is done with the previous one), then the copies
-        // of the unit kRingU - 1 ahead go into the previous unit's slot.  (One
-        // barrier per unit: one per 16-row sub-tile made the 512-token prefill
-        // tile's scores 517 us, one per two 486, one per unit 482.)
+        // read feeds 8 tokens where the register ring feeds 2.  Per pair of
+        // units k, k + 1: each wave waits for its own copies of them, then a
+        // barrier (both are complete; every wave is done with the previous
+        // pair), then the copies of units k + kRingU - 2 and k + kRingU - 1 go
+        // into the previous pair's slots.  (Barriers per 16-row sub-tile made
+        // the 512-token prefill tile's scores 517 us, per two sub-tiles 486,
+        // per unit 482 and, with the later changes, per unit 418, per pair 404.)
         constexpr int kRingU = kRing / 4;  // the ring in units (4 sub-tiles, 16 KB)
         const int u_a = __builtin_amdgcn_readfirstlane(id_0 - wave);
         const int n_wg_units = u_end - u_a;  // >= 1
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qa[tq][ht][ks]));
 #pragma unroll
-        for (int k = 0; k < kRingU - 1; ++k) dma_unit(k, k);
+        for (int k = 0; k < kRingU - 2; ++k) dma_unit(k, k);
         // this lane's operand-B read of chunk 4 ks + lg of row lc, within a slot
         uint32_t boff[4];
 #pragma unroll
@@ -513,6 +514,7 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
         const bool upper = l >= 32, odd = (lg & 1) != 0;
         int uslot = 0;  // unit slot of the current unit (its index % kRingU)
         constexpr int RBK = 16;  // units per store batch
+        static_assert(kRingU == 5 && RBK % 2 == 0, "a pair of units in use, one landed, two being copied");
         static_assert(kPassUnits % RBK == 0, "flushes fall between store batches");
         for (int u0 = 0; u0 < n_wg_units; u0 += RBK) {
           if (u0 > 0 && u0 % kPassUnits == 0) {  // (uniform; rare) flush the packed counters before they can overflow
@@ -527,13 +529,15 @@ __global__ __launch_bounds__(NT, MINB) void score_mfma_kernel(ScoreParams p) {
             if (u0 + ub < n_wg_units) {  // (uniform over the workgroup)
               float part[TW][4];
               {
-                // unit k = u0 + ub: this wave's copies of it have landed (those
-                // of the kRingU - 2 units after it may be in flight: copies
-                // complete in order), barrier (every wave's copies of unit k
-                // are complete; every wave is done with unit k - 1), then the
-                // copies of unit k + kRingU - 1 go into unit k - 1's slot
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * (kRingU - 2)) : "memory");
-                dma_unit(u0 + ub + kRingU - 1, uslot == 0 ? kRingU - 1 : uslot - 1);
+                // unit k = u0 + ub; at an even k, this wave's copies of units
+                // k and k + 1 have landed (those of k + 2 may be in flight:
+                // copies complete in order), barrier, then units k + 3 and
+                // k + 4 go into the slots of k - 2 and k - 1
+                if (ub % 2 == 0) {  // (u0 is even: units pair up as k, k + 1)
+                  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * (kRingU - 4)) : "memory");
+                  dma_unit(u0 + ub + kRingU - 2, uslot + kRingU - 2 >= kRingU ? uslot - 2 : uslot + kRingU - 2);
+                  dma_unit(u0 + ub + kRingU - 1, uslot + kRingU - 1 >= kRingU ? uslot - 1 : uslot + kRingU - 1);
+                }
                 // operand B of the unit's four sub-tiles (plain LDS loads: the
                 // compiler issues them together and waits for each just
                 // before its first MFMA)
