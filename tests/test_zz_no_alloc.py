@@ -68,6 +68,13 @@ def test_noalloc_fp8_two_tokens():
     _run_both(w)
 
 
+def test_noalloc_many_tokens():
+    # sixteen query tokens: the shared-key score kernel and the row-mode Top-K
+    w = synth.make("prefill64k", batch=2, q_len=16, max_seq_len=4000, len_range=(2500, 4000), top_k=700)
+    print(f"\n[noalloc prefill] B={w.batch} T={w.q_len} Lmax={w.max_seq_len}", flush=True)
+    _run_both(w)
+
+
 def test_noalloc_rejects_a_problem_larger_than_its_workspace():
     w = synth.make("decode8k", batch=2, max_seq_len=4096, top_k=256)
     d = G.to_device(w)
