@@ -296,8 +296,8 @@ def main():
         write_traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU (context-parallel) "
-                                   "sharding is a design note, not implemented", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this library runs on one GPU only; sharding over several GPUs "
+                                   "(by sequence, or context-parallel along L) is not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     if args.wg_trace:
